@@ -1,0 +1,222 @@
+"""ctypes wrapper over the CPU oracle (libstep5_oracle.so).
+
+TEST INFRASTRUCTURE ONLY: used by tests, the smoke check and the benchmark's
+CPU-baseline leg. The GPU library never imports it.
+
+All arrays are numpy, C-contiguous: bf16 as uint16 bit patterns, e4m3 as
+uint8 codes.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("STEP5_ORACLE_LIB") or os.path.join(HERE, "libstep5_oracle.so")
+
+IDX_DIM = 64
+REGION = 8
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            from oracle import build as _b  # noqa: WPS433
+            _b.build()
+        L = C.CDLL(LIB_PATH)
+        P, I64, I32, F, D = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_double
+        L.o_exp.restype = F
+        L.o_exp.argtypes = [F]
+        L.o_sum64.restype = F
+        L.o_sum64.argtypes = [P]
+        L.o_f32_to_bf16.restype = C.c_uint16
+        L.o_f32_to_bf16.argtypes = [F]
+        L.o_bf16_to_e4m3.restype = C.c_uint8
+        L.o_bf16_to_e4m3.argtypes = [C.c_uint16]
+        L.o_e4m3_to_f64.restype = D
+        L.o_e4m3_to_f64.argtypes = [C.c_uint8]
+        L.o_f32_to_bf16_n.argtypes = [P, P, I64]
+        L.o_bf16_to_e4m3_n.argtypes = [P, P, I64]
+        L.o_exp_n.argtypes = [P, P, I64, C.c_int]
+        L.o_k_prep_n.argtypes = [P, I64, P, P, F, P, P, P]
+        L.o_q_prep_head.argtypes = [P, P, F, P, P]
+        L.o_q_prep.restype = C.c_int
+        L.o_q_prep.argtypes = [P, I64, I32, I64, P, F, P, I64, P, P, C.c_int]
+        L.o_summarize.restype = C.c_int
+        L.o_summarize.argtypes = [P, P, I64, I64, I64, I32, I64, I64, P, P, F, P, I64, P, I64, I64,
+                                  P, C.c_int]
+        L.o_score.restype = C.c_int
+        L.o_score.argtypes = [P, I32, I32, P, I64, P, P, I64, P, I64, I64, I64, P, C.c_int]
+        L.o_select.restype = C.c_int
+        L.o_select.argtypes = [P, P, I64, I32, I64, I32, P, P, C.c_int]
+        L.o_attend.restype = C.c_int
+        L.o_attend.argtypes = [P, I64, I32, I32, I32, P, P, I64, I64, I64, P, I32, P, P, I64, D,
+                               P, P, C.c_int]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def default_threads() -> int:
+    return int(os.environ.get("STEP5_ORACLE_THREADS", os.cpu_count() or 1))
+
+
+# ---- formats and helpers ---------------------------------------------------
+
+def f32_to_bf16(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib().o_f32_to_bf16_n(_p(x), _p(y), x.size)
+    return y
+
+
+def bf16_to_f32(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    return (h.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_to_e4m3(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    y = np.empty(h.shape, np.uint8)
+    lib().o_bf16_to_e4m3_n(_p(h), _p(y), h.size)
+    return y
+
+
+def e4m3_to_f64(c) -> np.ndarray:
+    table = np.array([lib().o_e4m3_to_f64(i) for i in range(256)], dtype=np.float64)
+    return table[np.asarray(c, dtype=np.uint8)]
+
+
+def exp(x, nthreads=None) -> np.ndarray:
+    x = _c(x, np.float32)
+    y = np.empty(x.shape, np.float32)
+    lib().o_exp_n(_p(x), _p(y), x.size, nthreads or default_threads())
+    return y
+
+
+def sum64(x) -> float:
+    x = _c(x, np.float32)
+    assert x.size == 64
+    return float(lib().o_sum64(_p(x)))
+
+
+def k_prep(x16, ln_w, ln_b, eps, rope, pos) -> np.ndarray:
+    """Prepared k (fp32 values of bf16) for vectors x16 [n, 64] at positions pos [n]."""
+    x16 = _c(x16, np.uint16).reshape(-1, IDX_DIM)
+    pos = _c(pos, np.int64).reshape(-1)
+    out = np.empty(x16.shape, np.float32)
+    lib().o_k_prep_n(_p(x16), x16.shape[0], _p(_c(ln_w, np.float32)), _p(_c(ln_b, np.float32)),
+                     float(eps), _p(_c(rope, np.uint16)), _p(pos), _p(out))
+    return out
+
+
+# ---- the path's steps ------------------------------------------------------
+
+def q_prep(q16, w, eps, rope, row_pos, nthreads=None) -> np.ndarray:
+    """q16: uint16 [rows, H, 64] -> e4m3 [rows, H, 64]."""
+    q16 = _c(q16, np.uint16)
+    rows, H, D = q16.shape
+    assert D == IDX_DIM
+    rope = _c(rope, np.uint16)
+    out = np.empty(q16.shape, np.uint8)
+    rc = lib().o_q_prep(_p(q16), rows, H, H * D, _p(_c(w, np.float32)), float(eps), _p(rope),
+                        rope.shape[0], _p(_c(row_pos, np.int64)), _p(out),
+                        nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle q_prep rejected its arguments")
+    return out
+
+
+def summarize(k16, z16, t0, ln_w, ln_b, eps, rope, R_cap=None, summary=None, shadow=False,
+              nthreads=None):
+    """k16, z16: uint16 [B, T, G, 64] at absolute positions t0..t0+T-1.
+
+    Returns the e4m3 summary [B, R_cap, G, 64] (regions outside the span are
+    left as they were in `summary`, zero if it is None), and the fp64 shadow
+    of the softmax means when asked for.
+    """
+    k16 = _c(k16, np.uint16)
+    z16 = _c(z16, np.uint16)
+    B, T, G, D = k16.shape
+    assert D == IDX_DIM and z16.shape == k16.shape
+    if R_cap is None:
+        R_cap = (t0 + T) // REGION
+    if summary is None:
+        summary = np.zeros((B, R_cap, G, IDX_DIM), np.uint8)
+    assert summary.shape == (B, R_cap, G, IDX_DIM) and summary.flags["C_CONTIGUOUS"]
+    sh = np.full((B, R_cap, G, IDX_DIM), np.nan) if shadow else None
+    rope = _c(rope, np.uint16)
+    rc = lib().o_summarize(_p(k16), _p(z16), B, T, t0, G, T * G * D, G * D,
+                           _p(_c(ln_w, np.float32)), _p(_c(ln_b, np.float32)), float(eps),
+                           _p(rope), rope.shape[0], _p(summary), R_cap * G * D, R_cap,
+                           _p(sh) if shadow else None, nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle summarize rejected its arguments")
+    return (summary, sh) if shadow else summary
+
+
+def score(q8, w_head, row_seq, row_pos, summary, nthreads=None) -> np.ndarray:
+    """q8 [rows, H, 64] e4m3; w_head [H] or [rows, H]; summary [B, R_cap, G, 64].
+
+    Returns fp32 scores [rows, G, R_cap] (NaN where j >= floor(p/8))."""
+    q8 = _c(q8, np.uint8)
+    rows, H, _ = q8.shape
+    summary = _c(summary, np.uint8)
+    B, R_cap, G, _ = summary.shape
+    w = _c(w_head, np.float32)
+    w_stride = 0 if w.ndim == 1 else w.shape[1]
+    out = np.full((rows, G, R_cap), np.nan, np.float32)
+    rc = lib().o_score(_p(q8), H, G, _p(w), w_stride, _p(_c(row_seq, np.int32)),
+                       _p(_c(row_pos, np.int64)), rows, _p(summary), B, R_cap, R_cap * G * IDX_DIM,
+                       _p(out), nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle score rejected its arguments")
+    return out
+
+
+def select(scores, row_pos, topk=512, nthreads=None):
+    """scores [rows, G, R_cap] -> (ids int32 [rows, G, topk], scores fp32 [rows, G, topk])."""
+    scores = _c(scores, np.float32)
+    rows, G, R_cap = scores.shape
+    ids = np.empty((rows, G, topk), np.int32)
+    ss = np.empty((rows, G, topk), np.float32)
+    rc = lib().o_select(_p(scores), _p(_c(row_pos, np.int64)), rows, G, R_cap, topk, _p(ids),
+                        _p(ss), nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle select rejected its arguments")
+    return ids, ss
+
+
+def attend(q16, k16, v16, sel, row_seq, row_pos, scale, nthreads=None):
+    """q16 [rows, Hq, D]; k16, v16 [B, T_cap, Hkv, D]; sel int32 [rows, Hkv, topk].
+
+    Returns (o fp64 [rows, Hq, D], lse fp64 [rows, Hq])."""
+    q16 = _c(q16, np.uint16)
+    rows, Hq, D = q16.shape
+    k16 = _c(k16, np.uint16)
+    v16 = _c(v16, np.uint16)
+    B, T_cap, Hkv, D2 = k16.shape
+    assert D2 == D and v16.shape == k16.shape
+    sel = _c(sel, np.int32)
+    topk = sel.shape[2]
+    out = np.empty((rows, Hq, D), np.float64)
+    lse = np.empty((rows, Hq), np.float64)
+    rc = lib().o_attend(_p(q16), Hq * D, Hq, Hkv, D, _p(k16), _p(v16), T_cap * Hkv * D, Hkv * D,
+                        T_cap, _p(sel), topk, _p(_c(row_seq, np.int32)), _p(_c(row_pos, np.int64)),
+                        rows, float(scale), _p(out), _p(lse), nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle attend rejected its arguments")
+    return out, lse

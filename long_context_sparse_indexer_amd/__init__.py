@@ -1,0 +1,220 @@
+"""Step-5 sparse-indexer (DSA/CSA) hot path on AMD Instinct MI355X (gfx950).
+
+A thin binding over libstep5.so, the C ABI declared in include/step5.h. The
+functions carry the C names and only marshal arguments: they take torch
+tensors for device memory, pass their pointers, strides and the current HIP
+stream, and raise Step5Error on a non-zero status. Every step of the path runs
+in the library's HIP kernels; there is no other implementation behind these
+functions, and importing them without the built library raises.
+
+Source of the method: TensorFold pull request #903, "Step-5-Preview on one
+256 GB Mac" (indexer commit note), see include/step5.h.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "Step5Error", "GEOM", "lib", "step5_status_str", "step5_index_summarize",
+    "step5_index_score_topk", "step5_index_score_topk_workspace", "step5_sparse_attn",
+    "step5_sparse_attn_workspace", "STEP5_Q_E4M3",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstep5.so")
+STEP5_Q_E4M3 = 1
+
+IDX_HEADS, GROUPS, IDX_DIM, ROPE_DIM, REGION, TOPK = 16, 4, 64, 32, 8, 512
+Q_HEADS, KV_HEADS, HEAD_DIM = 16, 4, 128
+
+
+class Step5Geom(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("idx_heads", "groups", "idx_dim", "rope_dim", "region",
+                                         "topk", "q_heads", "kv_heads", "head_dim")]
+
+
+GEOM = Step5Geom(IDX_HEADS, GROUPS, IDX_DIM, ROPE_DIM, REGION, TOPK, Q_HEADS, KV_HEADS, HEAD_DIM)
+
+
+class Step5Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: status {status} ({step5_status_str(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libstep5.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "or python -m long_context_sparse_indexer_amd._build")
+        L = C.CDLL(LIB_PATH)
+        P, I64, I32, F, U32, SZ = C.c_void_p, C.c_int64, C.c_int32, C.c_float, C.c_uint32, C.c_size_t
+        G = C.POINTER(Step5Geom)
+        L.step5_status_str.restype = C.c_char_p
+        L.step5_status_str.argtypes = [C.c_int]
+        L.step5_index_summarize.restype = C.c_int
+        L.step5_index_summarize.argtypes = [G, P, P, I64, I64, I64, I64, I64, P, P, F, P, I64, P,
+                                            I64, I64, P]
+        L.step5_index_score_topk.restype = C.c_int
+        L.step5_index_score_topk.argtypes = [G, U32, P, I64, P, F, P, I64, P, I64, P, P, I32, P,
+                                             I64, I64, I64, P, P, P, SZ, P]
+        L.step5_index_score_topk_workspace.restype = SZ
+        L.step5_index_score_topk_workspace.argtypes = [G, I32, I64]
+        L.step5_sparse_attn.restype = C.c_int
+        L.step5_sparse_attn.argtypes = [G, P, I64, P, P, I64, I64, I64, I64, P, P, P, I32, F, P,
+                                        P, P, SZ, P]
+        L.step5_sparse_attn_workspace.restype = SZ
+        L.step5_sparse_attn_workspace.argtypes = [G, I32]
+        _lib = L
+    return _lib
+
+
+def step5_status_str(status: int) -> str:
+    return lib().step5_status_str(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _u8(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise Step5Error(fn, status)
+
+
+def step5_index_summarize(k: torch.Tensor, z: torch.Tensor, t0: int, ln_w: torch.Tensor,
+                          ln_b: torch.Tensor, ln_eps: float, rope: torch.Tensor,
+                          summary: torch.Tensor, stream=None) -> None:
+    """Summarise the regions completed in k/z (bf16 [B, T, 4, 64], positions t0..t0+T-1)
+    into summary (e4m3 as uint8 [B, R_cap, 4, 64])."""
+    _need(k.dtype == torch.bfloat16 and z.dtype == torch.bfloat16, "k, z must be bf16")
+    _need(k.dim() == 4 and k.shape == z.shape and tuple(k.shape[2:]) == (GROUPS, IDX_DIM),
+          "k, z must be [B, T, 4, 64]")
+    _need(k.stride() == z.stride() and k.stride(3) == 1 and k.stride(2) == IDX_DIM,
+          "k, z need contiguous (group, dim) and equal strides")
+    summary = _u8(summary)
+    _need(summary.dtype == torch.uint8 and summary.dim() == 4 and
+          tuple(summary.shape[2:]) == (GROUPS, IDX_DIM) and summary.shape[0] == k.shape[0],
+          "summary must be uint8 [B, R_cap, 4, 64]")
+    _need(summary.stride(3) == 1 and summary.stride(2) == IDX_DIM and
+          summary.stride(1) == GROUPS * IDX_DIM, "summary regions must be contiguous")
+    _need(rope.dtype == torch.bfloat16 and rope.dim() == 2 and rope.shape[1] == ROPE_DIM and
+          rope.is_contiguous(), "rope must be contiguous bf16 [rows, 32]")
+    B, T = k.shape[0], k.shape[1]
+    st = lib().step5_index_summarize(
+        C.byref(GEOM), _ptr(k), _ptr(z), B, T, int(t0), k.stride(0), k.stride(1), _ptr(ln_w),
+        _ptr(ln_b), float(ln_eps), _ptr(rope), rope.shape[0], _ptr(summary), summary.stride(0),
+        summary.shape[1], _stream(stream))
+    _check("step5_index_summarize", st)
+
+
+def step5_index_score_topk_workspace(rows: int, R_cap: int) -> int:
+    return int(lib().step5_index_score_topk_workspace(C.byref(GEOM), int(rows), int(R_cap)))
+
+
+def step5_sparse_attn_workspace(rows: int) -> int:
+    return int(lib().step5_sparse_attn_workspace(C.byref(GEOM), int(rows)))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return workspace
+    if workspace is None:
+        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        off = (-workspace.data_ptr()) % 256
+        workspace = workspace[off:off + nbytes]
+    _need(workspace.numel() >= nbytes, f"workspace needs {nbytes} bytes")
+    return workspace
+
+
+def step5_index_score_topk(q: torch.Tensor, w_head: torch.Tensor, row_seq: torch.Tensor,
+                           row_pos: torch.Tensor, summary: torch.Tensor, sel_ids: torch.Tensor,
+                           sel_scores: Optional[torch.Tensor] = None, *,
+                           q_norm_w: Optional[torch.Tensor] = None, q_eps: float = 1e-6,
+                           rope: Optional[torch.Tensor] = None, q_is_e4m3: bool = False,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Scores and top-512 per (row, group) into sel_ids (int32 [rows, 4, 512])."""
+    q = _u8(q) if q_is_e4m3 else q
+    rows = q.shape[0]
+    _need(q.dim() == 3 and tuple(q.shape[1:]) == (IDX_HEADS, IDX_DIM) and q.stride(2) == 1 and
+          q.stride(1) == IDX_DIM, "q must be [rows, 16, 64] with contiguous heads")
+    _need(q.dtype == (torch.uint8 if q_is_e4m3 else torch.bfloat16), "q dtype")
+    summary = _u8(summary)
+    _need(summary.dtype == torch.uint8 and summary.dim() == 4 and summary.stride(1) == 256 and
+          summary.stride(2) == 64 and summary.stride(3) == 1, "summary must be uint8 [B, R_cap, 4, 64]")
+    _need(w_head.dtype == torch.float32 and w_head.shape[-1] == IDX_HEADS and w_head.stride(-1) == 1,
+          "w_head must be fp32 [16] or [rows, 16]")
+    w_stride = 0 if w_head.dim() == 1 else w_head.stride(0)
+    _need(row_seq.dtype == torch.int32 and row_pos.dtype == torch.int64 and
+          row_seq.numel() == rows and row_pos.numel() == rows, "row_seq int32 / row_pos int64 [rows]")
+    _need(sel_ids.dtype == torch.int32 and tuple(sel_ids.shape) == (rows, GROUPS, TOPK) and
+          sel_ids.is_contiguous(), "sel_ids must be int32 [rows, 4, 512]")
+    if sel_scores is not None:
+        _need(sel_scores.dtype == torch.float32 and sel_scores.shape == sel_ids.shape and
+              sel_scores.is_contiguous(), "sel_scores must be fp32 [rows, 4, 512]")
+    if not q_is_e4m3:
+        _need(q_norm_w is not None and rope is not None, "q_norm_w and rope are needed")
+    B, R_cap = summary.shape[0], summary.shape[1]
+    nbytes = step5_index_score_topk_workspace(rows, R_cap)
+    workspace = _workspace(nbytes, q.device, workspace)
+    st = lib().step5_index_score_topk(
+        C.byref(GEOM), STEP5_Q_E4M3 if q_is_e4m3 else 0, _ptr(q), q.stride(0), _ptr(q_norm_w),
+        float(q_eps), _ptr(rope), rope.shape[0] if rope is not None else 0, _ptr(w_head), w_stride,
+        _ptr(row_seq), _ptr(row_pos), rows, _ptr(summary), B, R_cap, summary.stride(0),
+        _ptr(sel_ids), _ptr(sel_scores), _ptr(workspace), nbytes, _stream(stream))
+    _check("step5_index_score_topk", st)
+
+
+def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      sel_ids: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor,
+                      softmax_scale: float, out: torch.Tensor,
+                      out_lse: Optional[torch.Tensor] = None, *,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Attention over selected regions plus the own region into out (bf16 [rows, 16, 128])."""
+    rows = q.shape[0]
+    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and tuple(q.shape[1:]) == (Q_HEADS, HEAD_DIM)
+          and q.stride(2) == 1 and q.stride(1) == HEAD_DIM, "q must be bf16 [rows, 16, 128]")
+    _need(k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16 and
+          k_cache.shape == v_cache.shape and k_cache.stride() == v_cache.stride() and
+          k_cache.dim() == 4 and tuple(k_cache.shape[2:]) == (KV_HEADS, HEAD_DIM) and
+          k_cache.stride(3) == 1 and k_cache.stride(2) == HEAD_DIM,
+          "k_cache, v_cache must be bf16 [B, T, 4, 128] with equal strides")
+    _need(sel_ids.dtype == torch.int32 and tuple(sel_ids.shape) == (rows, GROUPS, TOPK) and
+          sel_ids.is_contiguous(), "sel_ids must be int32 [rows, 4, 512]")
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (rows, Q_HEADS, HEAD_DIM) and
+          out.is_contiguous(), "out must be contiguous bf16 [rows, 16, 128]")
+    if out_lse is not None:
+        _need(out_lse.dtype == torch.float32 and tuple(out_lse.shape) == (rows, Q_HEADS) and
+              out_lse.is_contiguous(), "out_lse must be fp32 [rows, 16]")
+    _need(row_seq.dtype == torch.int32 and row_pos.dtype == torch.int64, "row_seq int32, row_pos int64")
+    nbytes = step5_sparse_attn_workspace(rows)
+    workspace = _workspace(nbytes, q.device, workspace)
+    st = lib().step5_sparse_attn(
+        C.byref(GEOM), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+        k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _ptr(sel_ids), _ptr(row_seq),
+        _ptr(row_pos), rows, float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
+        nbytes, _stream(stream))
+    _check("step5_sparse_attn", st)

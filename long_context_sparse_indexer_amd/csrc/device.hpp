@@ -1,0 +1,160 @@
+// Device helpers shared by the gfx950 kernels of the Step-5 sparse-indexer
+// path: number formats, the path's fixed exp, lane reductions over 8- and
+// 16-lane groups, and MFMA operand types.
+//
+// Every float operation in the bit-exact steps (indexer q/k prep, region
+// summary, score epilogue) must be the single IEEE operation written, so the
+// library is built with -ffp-contract=off and the helpers below use explicit
+// fmaf only where the arithmetic says fused multiply-add.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace s5 {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__host__ __device__ inline float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__host__ __device__ inline float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// fp32 -> bf16 bit pattern, nearest with ties to even (finite values).
+__host__ __device__ inline uint32_t bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// the fp32 value of that bf16
+__host__ __device__ inline float bf16_round(float f) {
+  return __builtin_bit_cast(float, bf16_bits(f) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// e4m3 (OCP E4M3, bias 7, 3 mantissa bits, subnormals, largest finite 448)
+// from a bf16 bit pattern (8 exponent bits, bias 127, 7 mantissa bits),
+// nearest with ties to even; magnitudes from 448 up saturate to 448.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline uint32_t e4m3_from_bf16(uint32_t h) {
+  const uint32_t sign = (h >> 8) & 0x80u;
+  const uint32_t a = h & 0x7fffu;
+  if (a >= 0x43e0u) return sign | 0x7eu;  // |x| >= 448
+  const uint32_t E = a >> 7;              // biased bf16 exponent
+  const uint32_t m7 = a & 0x7fu;
+  if (E >= 121u) {
+    // normal in e4m3: exponent field E - 120, keep the top 3 mantissa bits and
+    // round on the 4 dropped ones; a carry out of the mantissa bumps the
+    // exponent, which is the right next value
+    uint32_t v = ((E - 120u) << 3) | (m7 >> 4);
+    const uint32_t rem = m7 & 0xfu;
+    v += (rem > 8u) | ((rem == 8u) & (v & 1u));
+    return sign | v;
+  }
+  // subnormal in e4m3 (steps of 2^-9): code = round((1.m7) * 2^(E-127) * 2^9)
+  //                                         = round((128 + m7) / 2^(125 - E))
+  if (E + 9u <= 125u) return sign;  // below 2^-10 (or a bf16 subnormal): rounds to 0
+  const uint32_t mant = 128u | m7;
+  const uint32_t sh = 125u - E;     // 5 .. 8
+  uint32_t v = mant >> sh;
+  const uint32_t rem = mant & ((1u << sh) - 1u);
+  const uint32_t half = 1u << (sh - 1u);
+  v += (rem > half) | ((rem == half) & (v & 1u));
+  return sign | v;                  // v == 8 is the smallest normal, as it should be
+}
+
+// ---------------------------------------------------------------------------
+// The path's exp: Cody & Waite's (1980) argument reduction x = n*ln2 + r,
+// |r| <= ln2/2, with ln2 split in a 15-bit head and an fp32 tail; e^r from
+// its degree-7 Taylor polynomial (coefficients 1/k!) in Horner form with
+// fused multiply-adds; then scaling by 2^n. The argument is first clamped to
+// [-87, 88] so every result is a normal float. All steps are correctly
+// rounded IEEE operations, so any conforming implementation of the same
+// steps gives the same bits.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline float exp_fixed(float x) {
+  x = fminf(fmaxf(x, -87.0f), 88.0f);
+  const float t = x * 0x1.715476p+0f;            // fp32(1/ln 2)
+  const float n = rintf(t);
+  float r = fmaf(-n, 0x1.62e4p-1f, x);           // ln 2 cut to 15 significant bits
+  r = fmaf(-n, 0x1.7f7d1cp-20f, r);              // fp32(ln 2 - head)
+  float p = 0x1.a01a02p-13f;                     // 1/5040
+  p = fmaf(p, r, 0x1.6c16c2p-10f);               // 1/720
+  p = fmaf(p, r, 0x1.111112p-7f);                // 1/120
+  p = fmaf(p, r, 0x1.555556p-5f);                // 1/24
+  p = fmaf(p, r, 0x1.555556p-3f);                // 1/6
+  p = fmaf(p, r, 0.5f);
+  p = fmaf(p, r, 1.0f);
+  p = fmaf(p, r, 1.0f);
+  return ldexpf(p, (int)n);
+}
+
+// Pairwise sum of 8 values as a halving tree (strides 4, 2, 1).
+__host__ __device__ inline float pair8(const float* a) {
+  const float b0 = a[0] + a[4], b1 = a[1] + a[5], b2 = a[2] + a[6], b3 = a[3] + a[7];
+  const float c0 = b0 + b2, c1 = b1 + b3;
+  return c0 + c1;
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane moves (DPP). Control codes: quad permutations, and shifts or
+// rotations within rows of 16 lanes (row_shl:n reads lane i+n, row_shr:n
+// reads lane i-n).
+// ---------------------------------------------------------------------------
+enum : int {
+  DPP_QUAD_XOR1 = 0xB1,  // quad_perm [1,0,3,2]
+  DPP_QUAD_XOR2 = 0x4E,  // quad_perm [2,3,0,1]
+  DPP_ROW_SHL4 = 0x104,
+  DPP_ROW_SHR4 = 0x114,
+  DPP_ROW_ROR4 = 0x124,
+  DPP_ROW_ROR8 = 0x128,
+};
+
+template <int CTRL>
+__device__ inline float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Lanes 8k+c (c = 0..7) each hold s_c; every lane of the 8-lane group gets
+// ((s0+s4) + (s2+s6)) + ((s1+s5) + (s3+s7)): the halving tree over the 8
+// lane values. Needs all 8 lanes of the group active.
+__device__ inline float sum8_lanes(float s, int lane) {
+  float t = s + dpp<DPP_ROW_SHL4>(s);   // lanes c < 4: s_c + s_{c+4}
+  t = t + dpp<DPP_QUAD_XOR2>(t);        // lanes c < 4: b_c + b_{c^2}
+  t = t + dpp<DPP_QUAD_XOR1>(t);        // lanes c < 4: (b0+b2) + (b1+b3), addition commutes
+  const float u = dpp<DPP_ROW_SHR4>(t); // lanes c >= 4 take lane c-4's total
+  return (lane & 4) ? u : t;
+}
+
+// max and sum over the 16 lanes of a row; every lane of the row gets the result
+__device__ inline float max16_lanes(float v) {
+  v = fmaxf(v, dpp<DPP_QUAD_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_QUAD_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_ROW_ROR4>(v));
+  v = fmaxf(v, dpp<DPP_ROW_ROR8>(v));
+  return v;
+}
+__device__ inline float sum16_lanes(float v) {
+  v = v + dpp<DPP_QUAD_XOR1>(v);
+  v = v + dpp<DPP_QUAD_XOR2>(v);
+  v = v + dpp<DPP_ROW_ROR4>(v);
+  v = v + dpp<DPP_ROW_ROR8>(v);
+  return v;
+}
+
+__device__ inline float wave_uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+
+// 8 bf16 (16 bytes) -> 8 floats
+__device__ inline void unpack_bf16x8(const uint4 w, float* f) {
+  f[0] = bf_lo(w.x); f[1] = bf_hi(w.x); f[2] = bf_lo(w.y); f[3] = bf_hi(w.y);
+  f[4] = bf_lo(w.z); f[5] = bf_hi(w.z); f[6] = bf_lo(w.w); f[7] = bf_hi(w.w);
+}
+
+__device__ inline uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+}  // namespace s5

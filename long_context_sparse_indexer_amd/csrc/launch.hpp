@@ -1,0 +1,105 @@
+// Internal launch interface between the C ABI (step5.cpp, argument checks and
+// workspace carving) and the kernel files. Arguments arrive here already
+// validated; the launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace s5 {
+
+struct SummarizeArgs {
+  const void* k;
+  const void* z;
+  int64_t B, T, t0, sb, st;
+  const float* ln_w;
+  const float* ln_b;
+  float eps;
+  const void* rope;
+  void* summary;
+  int64_t ssb;
+};
+hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
+
+struct QPrepArgs {
+  const void* q;
+  int64_t q_stride_row;
+  int32_t rows;
+  const float* w;
+  float eps;
+  const void* rope;
+  int64_t rope_rows;
+  const int64_t* row_pos;
+  uint8_t* q8;  // [rows, 16, 64]
+};
+hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream);
+
+struct ScoreArgs {
+  const uint8_t* q8;
+  int64_t q8_stride_row;  // bytes
+  int32_t rows;
+  const float* w_head;
+  int64_t w_stride_row;
+  const int32_t* row_seq;
+  const int64_t* row_pos;
+  const uint8_t* summary;
+  int64_t B, R_cap, ssb;
+  int64_t pos_limit;      // rows at p >= pos_limit are invalid (no rope row)
+  float* scores;          // [rows, 4, R_cap]
+};
+hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
+
+// Top-k selection plan: the candidates of a (row, group) are cut into
+// `nchunks` chunks of `chunk` candidates; with one chunk the selection is
+// done in one pass, otherwise each chunk keeps its best 512 and a second
+// pass picks the best 512 of their union.
+struct TopkPlan {
+  int64_t chunk;
+  int32_t nchunks;
+};
+TopkPlan topk_plan(int32_t rows, int64_t R_cap);
+size_t topk_partial_bytes(int32_t rows, int64_t R_cap);
+
+struct TopkArgs {
+  const float* scores;  // [rows, 4, R_cap]
+  int32_t rows;
+  int64_t R_cap;
+  const int32_t* row_seq;
+  const int64_t* row_pos;
+  int64_t B;
+  int64_t pos_limit;
+  unsigned long long* partial;  // [rows*4, nchunks, 512] when nchunks > 1
+  int32_t* sel_ids;
+  float* sel_scores;
+};
+hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
+
+// Attention plan: a (row, KV head) unit's 513 list entries (own region first,
+// then the 512 selections) are cut into `nsplit` splits of `per_split`
+// entries, each split one workgroup; several splits merge in a second pass.
+struct AttnPlan {
+  int32_t per_split;
+  int32_t nsplit;
+};
+AttnPlan attn_plan(int32_t rows);
+size_t attn_partial_bytes(int32_t rows);
+
+struct AttnArgs {
+  const void* q;
+  int64_t q_stride_row;
+  const void* k;
+  const void* v;
+  int64_t B, kv_sb, kv_st, T_cap;
+  const int32_t* sel;
+  const int32_t* row_seq;
+  const int64_t* row_pos;
+  int32_t rows;
+  float scale;
+  void* out;
+  float* lse;
+  float* partial;
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace s5

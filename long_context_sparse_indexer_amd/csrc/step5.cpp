@@ -1,0 +1,268 @@
+// C ABI of the Step-5 sparse-indexer path: argument checks, workspace
+// layout, and the launch sequence of each call. Every host-checkable
+// condition is checked before the first HIP call, so a rejected call enqueues
+// nothing and writes nothing.
+//
+// Geometry rules: vLLM's Step-5 model page ("vllm.models.step5.nvidia.model",
+// _validate_step5_dsa_parallel_geometry): indexer groups equal the attention
+// KV heads, indexer heads divide into groups, 4/8/16 query heads per KV head.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/step5.h"
+#include "launch.hpp"
+
+#define STEP5_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int32_t kIdxHeads = 16, kGroups = 4, kIdxDim = 64, kRopeDim = 32, kRegion = 8,
+                  kTopk = 512, kQHeads = 16, kKvHeads = 4, kHeadDim = 128;
+constexpr int64_t kRegionBytes = (int64_t)kGroups * kIdxDim;  // e4m3 summary bytes per region
+constexpr int64_t kMaxRcap = 524288;                            // 32 chunks of 16,384 candidates
+constexpr int32_t kMaxScoreRows = 65535 * 4;                    // score grid: 4 rows per block row
+constexpr size_t kAlign = 256;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+size_t up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_geom(const step5_geom* g) {
+  if (!g) return STEP5_E_INVALID;
+  if (g->idx_heads <= 0 || g->groups <= 0 || g->idx_dim <= 0 || g->rope_dim <= 0 ||
+      g->region <= 0 || g->topk <= 0 || g->q_heads <= 0 || g->kv_heads <= 0 || g->head_dim <= 0)
+    return STEP5_E_INVALID;
+  if (g->groups != g->kv_heads) return STEP5_E_INVALID;
+  if (g->idx_heads % g->groups) return STEP5_E_INVALID;
+  if (g->q_heads % g->kv_heads) return STEP5_E_INVALID;
+  const int32_t qpk = g->q_heads / g->kv_heads;
+  if (qpk != 4 && qpk != 8 && qpk != 16) return STEP5_E_INVALID;
+  if (g->rope_dim > g->idx_dim || (g->rope_dim & 1)) return STEP5_E_INVALID;
+  if (g->idx_heads != kIdxHeads || g->groups != kGroups || g->idx_dim != kIdxDim ||
+      g->rope_dim != kRopeDim || g->region != kRegion || g->topk != kTopk ||
+      g->q_heads != kQHeads || g->kv_heads != kKvHeads || g->head_dim != kHeadDim)
+    return STEP5_E_UNSUPPORTED;
+  return STEP5_OK;
+}
+
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+struct ScoreWs {
+  size_t q8 = 0, scores = 0, partial = 0, total = 0;
+};
+ScoreWs score_ws(int32_t rows, int64_t R_cap) {
+  ScoreWs w;
+  size_t off = 0;
+  w.q8 = off;
+  off = up(off + (size_t)rows * kIdxHeads * kIdxDim);
+  w.scores = off;
+  off = up(off + (size_t)rows * kGroups * (size_t)R_cap * sizeof(float));
+  w.partial = off;
+  off = up(off + s5::topk_partial_bytes(rows, R_cap));
+  w.total = off;
+  return w;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? STEP5_OK : STEP5_E_HIP; }
+
+}  // namespace
+
+STEP5_EXPORT const char* step5_status_str(int status) {
+  switch (status) {
+    case STEP5_OK: return "ok";
+    case STEP5_E_INVALID: return "invalid argument";
+    case STEP5_E_UNSUPPORTED: return "unsupported geometry or size";
+    case STEP5_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case STEP5_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+STEP5_EXPORT int step5_index_summarize(const step5_geom* geom, const void* k, const void* z,
+                                       int64_t B, int64_t T, int64_t t0, int64_t kz_stride_b,
+                                       int64_t kz_stride_t, const float* ln_w, const float* ln_b,
+                                       float ln_eps, const void* rope_cs, int64_t rope_rows,
+                                       void* summary, int64_t s_stride_b, int64_t R_cap,
+                                       hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
+  if (B < 0 || T < 0 || t0 < 0 || (t0 % kRegion) != 0) return STEP5_E_INVALID;
+  const int64_t nreg = T / kRegion;
+  if (B == 0 || nreg == 0) return STEP5_OK;
+  if (!k || !z || !ln_w || !ln_b || !rope_cs || !summary) return STEP5_E_INVALID;
+  if (!aligned(k, 16) || !aligned(z, 16) || !aligned(ln_w, 16) || !aligned(ln_b, 16) ||
+      !aligned(rope_cs, 16) || !aligned(summary, 16))
+    return STEP5_E_INVALID;
+  if (kz_stride_t < (int64_t)kGroups * kIdxDim || (kz_stride_t % 8) != 0) return STEP5_E_INVALID;
+  if (kz_stride_b < 0 || (kz_stride_b % 8) != 0) return STEP5_E_INVALID;
+  if (B > 1 && kz_stride_b < nreg * kRegion * kz_stride_t) return STEP5_E_INVALID;
+  if (!finite_pos(ln_eps)) return STEP5_E_INVALID;
+  if (rope_rows < t0 + nreg * kRegion) return STEP5_E_INVALID;
+  if (R_cap < 1 || t0 / kRegion + nreg > R_cap) return STEP5_E_INVALID;
+  if (s_stride_b < 0 || (s_stride_b % 16) != 0) return STEP5_E_INVALID;
+  if (B > 1 && s_stride_b < R_cap * kRegionBytes) return STEP5_E_INVALID;
+
+  s5::SummarizeArgs a;
+  a.k = k;
+  a.z = z;
+  a.B = B;
+  a.T = nreg * kRegion;
+  a.t0 = t0;
+  a.sb = kz_stride_b;
+  a.st = kz_stride_t;
+  a.ln_w = ln_w;
+  a.ln_b = ln_b;
+  a.eps = ln_eps;
+  a.rope = rope_cs;
+  a.summary = summary;
+  a.ssb = s_stride_b;
+  return from_hip(s5::launch_summarize(a, stream));
+}
+
+STEP5_EXPORT size_t step5_index_score_topk_workspace(const step5_geom* geom, int32_t rows,
+                                                     int64_t R_cap) {
+  if (check_geom(geom) || rows < 0 || rows > kMaxScoreRows || R_cap < 1 || R_cap > kMaxRcap)
+    return 0;
+  if (rows == 0) return 0;
+  return score_ws(rows, R_cap).total;
+}
+
+STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, const void* q,
+                                        int64_t q_stride_row, const float* q_norm_w, float q_eps,
+                                        const void* rope_cs, int64_t rope_rows,
+                                        const float* w_head, int64_t w_stride_row,
+                                        const int32_t* row_seq, const int64_t* row_pos,
+                                        int32_t rows, const void* summary, int64_t B,
+                                        int64_t R_cap, int64_t s_stride_b, int32_t* sel_ids,
+                                        float* sel_scores, void* workspace, size_t ws_bytes,
+                                        hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
+  if (flags & ~STEP5_Q_E4M3) return STEP5_E_INVALID;
+  if (rows < 0) return STEP5_E_INVALID;
+  if (rows == 0) return STEP5_OK;
+  if (rows > kMaxScoreRows) return STEP5_E_UNSUPPORTED;
+  const bool q_ready = (flags & STEP5_Q_E4M3) != 0;
+  if (!q || !aligned(q, 16)) return STEP5_E_INVALID;
+  if (q_ready) {
+    if (q_stride_row < (int64_t)kIdxHeads * kIdxDim || (q_stride_row % 16) != 0)
+      return STEP5_E_INVALID;
+  } else {
+    if (q_stride_row < (int64_t)kIdxHeads * kIdxDim || (q_stride_row % 8) != 0)
+      return STEP5_E_INVALID;
+    if (!q_norm_w || !aligned(q_norm_w, 16) || !finite_pos(q_eps)) return STEP5_E_INVALID;
+    if (!rope_cs || !aligned(rope_cs, 16) || rope_rows < 1) return STEP5_E_INVALID;
+  }
+  if (!w_head || !aligned(w_head, 4)) return STEP5_E_INVALID;
+  if (w_stride_row != 0 && w_stride_row < kIdxHeads) return STEP5_E_INVALID;
+  if (!row_seq || !row_pos || !aligned(row_seq, 4) || !aligned(row_pos, 8)) return STEP5_E_INVALID;
+  if (!summary || !aligned(summary, 16)) return STEP5_E_INVALID;
+  if (B < 1 || R_cap < 1) return STEP5_E_INVALID;
+  if (R_cap > kMaxRcap) return STEP5_E_UNSUPPORTED;
+  if (s_stride_b < 0 || (s_stride_b % 16) != 0) return STEP5_E_INVALID;
+  if (B > 1 && s_stride_b < R_cap * kRegionBytes) return STEP5_E_INVALID;
+  if (!sel_ids || !aligned(sel_ids, 4) || (sel_scores && !aligned(sel_scores, 4)))
+    return STEP5_E_INVALID;
+  const ScoreWs w = score_ws(rows, R_cap);
+  if (ws_bytes < w.total || !workspace || !aligned(workspace, kAlign)) return STEP5_E_WORKSPACE;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const uint8_t* q8 = static_cast<const uint8_t*>(q);
+  int64_t q8_stride = q_stride_row;
+  if (!q_ready) {
+    s5::QPrepArgs qa;
+    qa.q = q;
+    qa.q_stride_row = q_stride_row;
+    qa.rows = rows;
+    qa.w = q_norm_w;
+    qa.eps = q_eps;
+    qa.rope = rope_cs;
+    qa.rope_rows = rope_rows;
+    qa.row_pos = row_pos;
+    qa.q8 = ws + w.q8;
+    const int st = from_hip(s5::launch_qprep(qa, stream));
+    if (st) return st;
+    q8 = ws + w.q8;
+    q8_stride = (int64_t)kIdxHeads * kIdxDim;
+  }
+  s5::ScoreArgs sa;
+  sa.q8 = q8;
+  sa.q8_stride_row = q8_stride;
+  sa.rows = rows;
+  sa.w_head = w_head;
+  sa.w_stride_row = w_stride_row;
+  sa.row_seq = row_seq;
+  sa.row_pos = row_pos;
+  sa.summary = static_cast<const uint8_t*>(summary);
+  sa.B = B;
+  sa.R_cap = R_cap;
+  sa.ssb = s_stride_b;
+  sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
+  sa.scores = reinterpret_cast<float*>(ws + w.scores);
+  int st = from_hip(s5::launch_score(sa, stream));
+  if (st) return st;
+  s5::TopkArgs ta;
+  ta.scores = sa.scores;
+  ta.rows = rows;
+  ta.R_cap = R_cap;
+  ta.row_seq = row_seq;
+  ta.row_pos = row_pos;
+  ta.B = B;
+  ta.pos_limit = sa.pos_limit;
+  ta.partial = reinterpret_cast<unsigned long long*>(ws + w.partial);
+  ta.sel_ids = sel_ids;
+  ta.sel_scores = sel_scores;
+  return from_hip(s5::launch_topk(ta, stream));
+}
+
+STEP5_EXPORT size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows) {
+  if (check_geom(geom) || rows <= 0 || rows > (INT32_MAX / 4)) return 0;
+  const size_t b = s5::attn_partial_bytes(rows);
+  return b ? up(b) : 0;
+}
+
+STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_t q_stride_row,
+                                   const void* k_cache, const void* v_cache, int64_t B,
+                                   int64_t kv_stride_b, int64_t kv_stride_t, int64_t T_cap,
+                                   const int32_t* sel_ids, const int32_t* row_seq,
+                                   const int64_t* row_pos, int32_t rows, float softmax_scale,
+                                   void* out, float* out_lse, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
+  if (rows < 0) return STEP5_E_INVALID;
+  if (rows == 0) return STEP5_OK;
+  if (rows > INT32_MAX / 4) return STEP5_E_UNSUPPORTED;
+  if (!q || !aligned(q, 16) || q_stride_row < (int64_t)kQHeads * kHeadDim || (q_stride_row % 8))
+    return STEP5_E_INVALID;
+  if (!k_cache || !v_cache || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return STEP5_E_INVALID;
+  if (B < 1 || T_cap < 1) return STEP5_E_INVALID;
+  if (kv_stride_t < (int64_t)kKvHeads * kHeadDim || (kv_stride_t % 8)) return STEP5_E_INVALID;
+  if (kv_stride_b < 0 || (kv_stride_b % 8)) return STEP5_E_INVALID;
+  if (B > 1 && kv_stride_b < T_cap * kv_stride_t) return STEP5_E_INVALID;
+  if (!sel_ids || !aligned(sel_ids, 4)) return STEP5_E_INVALID;
+  if (!row_seq || !row_pos || !aligned(row_seq, 4) || !aligned(row_pos, 8)) return STEP5_E_INVALID;
+  if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return STEP5_E_INVALID;
+  if (!out || !aligned(out, 16) || (out_lse && !aligned(out_lse, 4))) return STEP5_E_INVALID;
+  const size_t need = step5_sparse_attn_workspace(geom, rows);
+  if (ws_bytes < need || (need && (!workspace || !aligned(workspace, kAlign))))
+    return STEP5_E_WORKSPACE;
+
+  s5::AttnArgs a;
+  a.q = q;
+  a.q_stride_row = q_stride_row;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.B = B;
+  a.kv_sb = kv_stride_b;
+  a.kv_st = kv_stride_t;
+  a.T_cap = T_cap;
+  a.sel = sel_ids;
+  a.row_seq = row_seq;
+  a.row_pos = row_pos;
+  a.rows = rows;
+  a.scale = softmax_scale;
+  a.out = out;
+  a.lse = out_lse;
+  a.partial = static_cast<float*>(workspace);
+  return from_hip(s5::launch_attn(a, stream));
+}

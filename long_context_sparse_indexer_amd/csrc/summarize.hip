@@ -1,0 +1,147 @@
+// Region summaries of the indexer keys, with the k prep fused into the load.
+//
+// TensorFold #903 ("Step-5-Preview on one 256 GB Mac"), indexer commit note:
+// the indexer k is LayerNormed with bias and NEOX-rotated on dims 0..31;
+// every completed 8-token region is summarised per dim as a softmax over the
+// region's z weighting k, rounded through bf16 to e4m3.
+//
+// Fixed rounding points (the path's reading of the note):
+//   k prep, per (token, group), fp32:  mu = sum64(x)/64, d = x - mu,
+//     var = sum64(d*d)/64, r = 1/sqrt(var + eps), y = (d*r)*gamma + beta,
+//     rotation a*c - b*s | b*c + a*s with bf16 cos/sin, then bf16;
+//     sum64 = halving tree within each run of 8 dims, then over the runs.
+//   summary, per (region, group, dim):  m = max_t z_t, e_t = exp_fixed(z_t - m),
+//     den and num summed in token order (num of the rounded products e_t*k_t),
+//     s = num/den, code = e4m3(bf16(s)).
+//
+// Mapping: a region is 4 KB of k and 4 KB of z (8 tokens x 4 groups x 64
+// bf16, contiguous). 32 lanes own it: lane (g, c) holds dims 8c..8c+7 of group
+// g for all 8 tokens, so the 64 dims of a (token, group) sit on 8 adjacent
+// lanes (reduced with DPP) and the 8 tokens of a dim sit in one lane. A wave
+// covers 2 regions, a 256-thread block 8; every load is 16 B per lane and a
+// wave's loads cover whole 512-B token rows. The 256 B of e4m3 a region
+// produces are stored 8 B per lane, contiguous across the 32 lanes.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace s5 {
+
+__global__ __launch_bounds__(256) void summarize_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ z, int64_t nreg, int64_t total,
+    int64_t t0, int64_t sb, int64_t st, const float* __restrict__ lnw,
+    const float* __restrict__ lnb, float eps, const uint16_t* __restrict__ rope,
+    uint8_t* __restrict__ S, int64_t ssb) {
+  const int lane = threadIdx.x & 63;
+  const int sub = threadIdx.x & 31;
+  const int g = sub >> 3, c = sub & 7;
+  float gw[8], gb[8];
+  {
+    const float4 w0 = reinterpret_cast<const float4*>(lnw)[2 * c];
+    const float4 w1 = reinterpret_cast<const float4*>(lnw)[2 * c + 1];
+    const float4 b0 = reinterpret_cast<const float4*>(lnb)[2 * c];
+    const float4 b1 = reinterpret_cast<const float4*>(lnb)[2 * c + 1];
+    gw[0] = w0.x; gw[1] = w0.y; gw[2] = w0.z; gw[3] = w0.w;
+    gw[4] = w1.x; gw[5] = w1.y; gw[6] = w1.z; gw[7] = w1.w;
+    gb[0] = b0.x; gb[1] = b0.y; gb[2] = b0.z; gb[3] = b0.w;
+    gb[4] = b1.x; gb[5] = b1.y; gb[6] = b1.z; gb[7] = b1.w;
+  }
+  const bool rotated = c < 4;        // dims 0..31
+  const bool first_half = c < 2;     // dims 0..15 hold the pair's first element
+  const int fi = (c & 1) * 8;        // frequency index of this lane's first dim
+  const int64_t j0 = t0 >> 3;
+
+  for (int64_t u = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); u < total;
+       u += (int64_t)gridDim.x * 8) {
+    const int64_t b = u / nreg, jr = u - b * nreg;
+    const int64_t off = b * sb + jr * 8 * st + g * 64 + c * 8;
+    const uint16_t* kp = k + off;
+    const uint16_t* zp = z + off;
+
+    uint4 zr[8], kr[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) zr[t] = ldg16(zp + t * st);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kr[t] = ldg16(kp + t * st);
+
+    float zf[8][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) unpack_bf16x8(zr[t], zf[t]);
+    float m[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      m[i] = zf[0][i];
+#pragma unroll
+      for (int t = 1; t < 8; ++t) m[i] = fmaxf(m[i], zf[t][i]);
+    }
+
+    float den[8], num[8];
+    const uint16_t* cs = rope + (t0 + jr * 8) * 32;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      float x[8], d[8], d2[8], y[8];
+      unpack_bf16x8(kr[t], x);
+      const float mu = sum8_lanes(pair8(x), lane) / 64.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        d[i] = x[i] - mu;
+        d2[i] = d[i] * d[i];
+      }
+      const float var = sum8_lanes(pair8(d2), lane) / 64.0f;
+      const float r = 1.0f / sqrtf(var + eps);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float tt = (d[i] * r) * gw[i];
+        y[i] = tt + gb[i];
+      }
+      // NEOX rotation: lanes c and c^2 (c < 4) hold the two halves of the pairs
+      float cf[8], sf[8];
+      unpack_bf16x8(ldg16(cs + t * 32 + fi), cf);
+      unpack_bf16x8(ldg16(cs + t * 32 + 16 + fi), sf);
+      float kv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float other = dpp<DPP_QUAD_XOR2>(y[i]);
+        const float own_c = y[i] * cf[i];
+        const float oth_s = other * sf[i];
+        const float rot = first_half ? (own_c - oth_s) : (own_c + oth_s);
+        kv[i] = bf16_round(rotated ? rot : y[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = exp_fixed(zf[t][i] - m[i]);
+        const float pr = e * kv[i];
+        if (t == 0) {
+          den[i] = e;
+          num[i] = pr;
+        } else {
+          den[i] = den[i] + e;
+          num[i] = num[i] + pr;
+        }
+      }
+    }
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float s = num[i] / den[i];
+      const uint32_t code = e4m3_from_bf16(bf16_bits(s));
+      if (i < 4) lo |= code << (8 * i);
+      else hi |= code << (8 * (i - 4));
+    }
+    uint2* dst = reinterpret_cast<uint2*>(S + b * ssb + (j0 + jr) * 256 + g * 64 + c * 8);
+    *dst = make_uint2(lo, hi);
+  }
+}
+
+hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream) {
+  const int64_t nreg = a.T / 8;
+  const int64_t total = a.B * nreg;
+  if (total <= 0) return hipSuccess;
+  int64_t blocks = (total + 7) / 8;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(summarize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint16_t*)a.k, (const uint16_t*)a.z, nreg, total, a.t0, a.sb, a.st,
+                     a.ln_w, a.ln_b, a.eps, (const uint16_t*)a.rope, (uint8_t*)a.summary, a.ssb);
+  return hipGetLastError();
+}
+
+}  // namespace s5

@@ -1,0 +1,231 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+entry point include/step5.h declares, and rejects bad arguments with the
+documented status before anything reaches the HIP runtime (a call that got as
+far as a launch would return STEP5_E_HIP here, where there is no GPU).
+Rejection rules follow the geometry checks of vLLM's Step-5 model page
+(_validate_step5_dsa_parallel_geometry) and the header's argument contract.
+"""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "step5.h")
+
+OK, E_INVALID, E_UNSUPPORTED, E_WORKSPACE, E_HIP = 0, 1, 2, 3, 4
+A = 0x10000  # an aligned fake device address; never dereferenced by a rejected call
+
+
+@pytest.fixture(scope="module")
+def s5():
+    import long_context_sparse_indexer_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from long_context_sparse_indexer_amd import _build
+        _build.build()
+    m.lib()
+    return m
+
+
+def geom(s5, **kw):
+    g = s5.Step5Geom(16, 4, 64, 32, 8, 512, 16, 4, 128)
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+def test_exports_every_declared_symbol(s5):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(step5_\w+)\s*\(", text, re.M))
+    assert {"step5_index_summarize", "step5_index_score_topk", "step5_sparse_attn",
+            "step5_index_score_topk_workspace", "step5_sparse_attn_workspace",
+            "step5_status_str"} <= declared
+    nm = subprocess.run(["nm", "-D", "--defined-only", s5.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (step5_\w+)$", nm, re.M))
+    assert declared == exported
+    for name in declared:
+        assert hasattr(s5.lib(), name)
+
+
+def test_status_strings(s5):
+    assert s5.step5_status_str(0) == "ok"
+    for c in (1, 2, 3, 4):
+        assert s5.step5_status_str(c) != "unknown status"
+    assert s5.step5_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK),
+    ({"groups": 2}, E_INVALID),                 # groups != kv_heads
+    ({"idx_heads": 18}, E_INVALID),             # indexer heads do not divide into groups
+    ({"q_heads": 8}, E_INVALID),                # 2 query heads per KV head
+    ({"q_heads": 12}, E_INVALID),               # 3 per KV head
+    ({"rope_dim": 33}, E_INVALID),
+    ({"topk": 0}, E_INVALID),
+    ({"q_heads": 32}, E_UNSUPPORTED),           # 8 per KV head: valid, not built
+    ({"q_heads": 64}, E_UNSUPPORTED),           # 16 per KV head
+    ({"head_dim": 192}, E_UNSUPPORTED),
+    ({"topk": 256}, E_UNSUPPORTED),
+])
+def test_geometry_rules(s5, kw, code):
+    g = geom(s5, **kw)
+    L = s5.lib()
+    # B = 0 is an empty call: with good geometry it succeeds without touching the GPU
+    st = L.step5_index_summarize(C.byref(g), None, None, 0, 0, 0, 0, 0, None, None, 1e-6,
+                                 None, 0, None, 0, 0, None)
+    assert st == code
+    assert L.step5_index_summarize(None, None, None, 0, 0, 0, 0, 0, None, None, 1e-6, None, 0,
+                                   None, 0, 0, None) == E_INVALID
+
+
+def _summ(s5, **over):
+    g = geom(s5)
+    a = dict(k=A, z=A, B=2, T=64, t0=0, sb=64 * 256, st=256, lnw=A, lnb=A, eps=1e-6, rope=A,
+             rope_rows=64, summary=A, ssb=8 * 256, R_cap=8)
+    a.update(over)
+    return s5.lib().step5_index_summarize(
+        C.byref(g), a["k"], a["z"], a["B"], a["T"], a["t0"], a["sb"], a["st"], a["lnw"],
+        a["lnb"], a["eps"], a["rope"], a["rope_rows"], a["summary"], a["ssb"], a["R_cap"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"t0": 4}, E_INVALID),
+    ({"t0": -8}, E_INVALID),
+    ({"B": -1}, E_INVALID),
+    ({"T": -8}, E_INVALID),
+    ({"T": 7}, OK),                 # no completed region: nothing to do
+    ({"B": 0}, OK),
+    ({"k": None}, E_INVALID),
+    ({"z": A + 8}, E_INVALID),      # misaligned
+    ({"lnw": None}, E_INVALID),
+    ({"rope": None}, E_INVALID),
+    ({"summary": A + 4}, E_INVALID),
+    ({"st": 255}, E_INVALID),
+    ({"st": 260}, E_INVALID),       # not a multiple of 8
+    ({"sb": 64 * 256 - 8}, E_INVALID),
+    ({"eps": 0.0}, E_INVALID),
+    ({"eps": float("nan")}, E_INVALID),
+    ({"rope_rows": 63}, E_INVALID),
+    ({"R_cap": 7}, E_INVALID),
+    ({"t0": 8, "rope_rows": 72}, E_INVALID),   # regions 1..8 need R_cap >= 9
+    ({"ssb": 8 * 256 - 16}, E_INVALID),
+    ({"ssb": 8 * 256 + 8}, E_INVALID),
+])
+def test_summarize_rejections(s5, over, code):
+    assert _summ(s5, **over) == code
+
+
+def _score(s5, **over):
+    g = geom(s5)
+    rows = over.pop("rows", 4)
+    R_cap = over.pop("R_cap", 64)
+    need = s5.lib().step5_index_score_topk_workspace(C.byref(g), rows, R_cap)
+    a = dict(flags=0, q=A, qs=1024, qw=A, eps=1e-6, rope=A, rope_rows=1024, w=A, ws_row=0,
+             seq=A, pos=A, summary=A, B=1, ssb=R_cap * 256, ids=A, scores=None, ws=A, wsb=need)
+    a.update(over)
+    return s5.lib().step5_index_score_topk(
+        C.byref(g), a["flags"], a["q"], a["qs"], a["qw"], a["eps"], a["rope"], a["rope_rows"],
+        a["w"], a["ws_row"], a["seq"], a["pos"], rows, a["summary"], a["B"], R_cap, a["ssb"],
+        a["ids"], a["scores"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"rows": 0}, OK),
+    ({"rows": -1}, E_INVALID),
+    ({"flags": 2}, E_INVALID),
+    ({"q": None}, E_INVALID),
+    ({"qs": 1000}, E_INVALID),
+    ({"qw": None}, E_INVALID),
+    ({"flags": 1, "qw": None, "rope": None, "qs": 1024}, E_WORKSPACE),   # prepared q needs no prep args
+    ({"flags": 1, "qs": 1032}, E_INVALID),                                # e4m3 rows 16-byte aligned
+    ({"eps": -1.0}, E_INVALID),
+    ({"rope_rows": 0}, E_INVALID),
+    ({"w": None}, E_INVALID),
+    ({"ws_row": 8}, E_INVALID),
+    ({"seq": None}, E_INVALID),
+    ({"pos": A + 4}, E_INVALID),
+    ({"summary": None}, E_INVALID),
+    ({"B": 0}, E_INVALID),
+    ({"B": 2, "ssb": 63 * 256}, E_INVALID),
+    ({"R_cap": 524289}, E_UNSUPPORTED),
+    ({"R_cap": 0}, E_INVALID),
+    ({"ids": None}, E_INVALID),
+    ({"ws": None}, E_WORKSPACE),
+    ({"ws": A + 128}, E_WORKSPACE),
+    ({"rows": 300000}, E_UNSUPPORTED),
+])
+def test_score_topk_rejections(s5, over, code):
+    if over.get("flags") == 1 and "wsb" not in over:
+        over["wsb"] = 0          # then the call stops at the workspace check
+    assert _score(s5, **over) == code
+
+
+def test_score_topk_workspace_too_small(s5):
+    g = geom(s5)
+    need = s5.lib().step5_index_score_topk_workspace(C.byref(g), 4, 64)
+    assert need > 0 and need % 256 == 0
+    assert _score(s5, wsb=need - 1) == E_WORKSPACE
+
+
+def test_workspace_sizes(s5):
+    L = s5.lib()
+    g = geom(s5)
+    assert L.step5_index_score_topk_workspace(C.byref(g), 0, 100) == 0
+    assert L.step5_index_score_topk_workspace(C.byref(g), 4, 0) == 0
+    assert L.step5_index_score_topk_workspace(C.byref(geom(s5, groups=2)), 4, 64) == 0
+    # q8 (rows*1024) + scores (rows*4*R_cap*4), 256-aligned, plus chunk lists when split
+    w1 = L.step5_index_score_topk_workspace(C.byref(g), 2048, 4096)
+    assert w1 >= 2048 * 1024 + 2048 * 4 * 4096 * 4
+    w4 = L.step5_index_score_topk_workspace(C.byref(g), 16, 16384)
+    assert w4 >= 16 * 1024 + 16 * 4 * 16384 * 4 + 16 * 4 * 4 * 512 * 8
+    assert L.step5_sparse_attn_workspace(C.byref(g), 2048) == 0          # prefill: unsplit
+    assert L.step5_sparse_attn_workspace(C.byref(g), 16) > 0             # decode: split states
+    assert L.step5_sparse_attn_workspace(C.byref(g), 0) == 0
+
+
+def _attn(s5, **over):
+    g = geom(s5)
+    rows = over.pop("rows", 16)
+    need = s5.lib().step5_sparse_attn_workspace(C.byref(g), rows)
+    a = dict(q=A, qs=2048, k=A, v=A, B=16, kvb=4096 * 512, kvt=512, T=4096, sel=A, seq=A, pos=A,
+             scale=0.088, out=A, lse=None, ws=A, wsb=need)
+    a.update(over)
+    return s5.lib().step5_sparse_attn(
+        C.byref(g), a["q"], a["qs"], a["k"], a["v"], a["B"], a["kvb"], a["kvt"], a["T"], a["sel"],
+        a["seq"], a["pos"], rows, a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"rows": 0}, OK),
+    ({"rows": -3}, E_INVALID),
+    ({"q": None}, E_INVALID),
+    ({"qs": 2040}, E_INVALID),
+    ({"k": A + 2}, E_INVALID),
+    ({"v": None}, E_INVALID),
+    ({"B": 0}, E_INVALID),
+    ({"T": 0}, E_INVALID),
+    ({"kvt": 500}, E_INVALID),
+    ({"kvb": 4095 * 512}, E_INVALID),
+    ({"sel": None}, E_INVALID),
+    ({"pos": None}, E_INVALID),
+    ({"scale": 0.0}, E_INVALID),
+    ({"scale": float("inf")}, E_INVALID),
+    ({"scale": float("nan")}, E_INVALID),
+    ({"out": None}, E_INVALID),
+    ({"lse": A + 2}, E_INVALID),
+    ({"ws": None}, E_WORKSPACE),
+    ({"wsb": 16}, E_WORKSPACE),
+])
+def test_sparse_attn_rejections(s5, over, code):
+    assert _attn(s5, **over) == code
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import long_context_sparse_indexer_amd as m
+    monkeypatch.setattr(m, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(m, "_lib", None)
+    with pytest.raises(ImportError):
+        m.lib()

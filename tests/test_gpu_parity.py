@@ -1,0 +1,316 @@
+"""GPU parity: the HIP path (called through the C ABI) against the CPU oracle on
+the same seeded inputs, for the five workloads, with edge cases.
+
+Rules (see tests/parity.py): summaries bit-exact; ids bit-exact except counted
+near-ties (none allowed on the tie-heavy workload, whose arithmetic is exact);
+attention within 2e-3 + 1e-2|ref| of the fp64 oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _case(name, seed, device="cpu", **kw):
+    d = W.make_case(W.WORKLOADS[name], seed, device, **kw)
+    P.say(f"[case] {name} seed={seed} device={device} {kw}")
+    return d
+
+
+# ---- summaries ------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["decode1_ctx6000", "decode8_ctx3000"])
+@pytest.mark.parametrize("seed", [17, 41])
+def test_summary_bitexact(name, seed):
+    d = _case(name, seed)
+    S = P.gpu_summary(d).cpu().numpy()
+    O = P.oracle_summary(d)
+    mism = int((S != O).sum())
+    P.say(f"  summaries {O.size} values, mismatches {mism}")
+    assert mism == 0
+
+
+def test_summary_offsets_ragged_and_strided():
+    """t0 > 0, a trailing partial region, sequences that are views of a larger
+    cache: only the completed regions are written, every other byte kept."""
+    d = _case("decode8_ctx3000", 5, cache_tokens=64 + 8 * 37 + 5, rows=3, batch=3)
+    big_k = d["k_idx"].to(DEV)
+    big_z = d["z_idx"].to(DEV)
+    t0 = 64
+    k, z = big_k[:, t0:], big_z[:, t0:]            # views: batch stride of the full cache
+    R_cap = 50
+    S = torch.full((3, R_cap, 4, 64), 0xA5, dtype=torch.uint8, device=DEV)
+    import long_context_sparse_indexer_amd as s5
+    s5.step5_index_summarize(k, z, t0, d["ln_w"].to(DEV), d["ln_b"].to(DEV), P.EPS,
+                             d["rope"].to(DEV), S)
+    S = S.cpu().numpy()
+    base = np.full((3, R_cap, 4, 64), 0xA5, np.uint8)
+    O = P.orc.summarize(P.host16(d["k_idx"])[:, t0:], P.host16(d["z_idx"])[:, t0:], t0,
+                        d["ln_w"].numpy(), d["ln_b"].numpy(), P.EPS, P.host16(d["rope"]),
+                        R_cap=R_cap, summary=base)
+    assert np.array_equal(S, O)
+    assert np.all(S[:, :8] == 0xA5) and np.all(S[:, 8 + 37:] == 0xA5)
+
+
+def test_summary_full_size_decode16_ctx128k():
+    """The 16 x 131,072-token Student-t cache: the GPU summarises all of it;
+    two whole sequences are checked against the oracle."""
+    d = _case("decode16_ctx128k", 17, DEV, with_kv=False)
+    S = P.gpu_summary(d)
+    torch.cuda.synchronize()
+    for b in (0, 15):
+        O = P.oracle_summary({**d, "k_idx": d["k_idx"][b:b + 1], "z_idx": d["z_idx"][b:b + 1]})
+        got = S[b:b + 1].cpu().numpy()
+        mism = int((got != O).sum())
+        P.say(f"  seq {b}: {O.size} values, mismatches {mism}")
+        assert mism == 0
+
+
+def test_summary_fresh_span_1m_workload():
+    d = _case("decode1_ctx1m", 41, DEV, cache_tokens=8, with_kv=False)
+    S = P.gpu_summary(d, k="fresh_k", z="fresh_z")
+    O = P.oracle_summary(d, k="fresh_k", z="fresh_z")
+    assert int((S.cpu().numpy() != O).sum()) == 0
+
+
+# ---- selection ------------------------------------------------------------
+
+def _select_check(d, S_gpu, O_summary, rows, seq_map=None, exact=False):
+    ids, sc = P.gpu_select(d, S_gpu)
+    torch.cuda.synchronize()
+    osc = P.oracle_scores(d, O_summary, rows, seq_map)
+    pos = d["row_pos"].cpu().numpy()[rows]
+    ex = P.compare_selection(ids.cpu().numpy()[rows], sc.cpu().numpy()[rows], osc, pos, exact=exact)
+    P.say(f"  rows {len(rows)}: near-tie excusals {ex}")
+    return ids, ex
+
+
+@pytest.mark.parametrize("seed", [17, 41])
+def test_select_decode1_ctx6000(seed):
+    d = _case("decode1_ctx6000", seed)
+    S = P.gpu_summary(d)
+    O = P.oracle_summary(d)
+    assert np.array_equal(S.cpu().numpy(), O)
+    _select_check(d, S, O, [0])
+
+
+@pytest.mark.parametrize("seed", [17, 41])
+def test_select_all_below_512_decode8_ctx3000(seed):
+    d = _case("decode8_ctx3000", seed)
+    S = P.gpu_summary(d)
+    O = P.oracle_summary(d)
+    ids, _ = _select_check(d, S, O, list(range(8)))
+    got = ids.cpu().numpy()
+    for r in range(8):
+        for g in range(4):
+            assert sorted(got[r, g, :374].tolist()) == list(range(374))
+            assert np.all(got[r, g, 374:] == -1)
+
+
+def test_select_prefill2048_ctx32k_sampled():
+    d = _case("prefill2048_ctx32k", 17, DEV, with_kv=False)
+    S = P.gpu_summary(d)
+    O = P.oracle_summary(d)
+    assert int((S.cpu().numpy() != O).sum()) == 0
+    rows = [0, 1, 2, 3, 7, 100, 511, 512, 1023, 1500, 2044, 2045, 2046, 2047]
+    _select_check(d, S, O, rows)
+
+
+def test_select_decode16_ctx128k_sampled():
+    d = _case("decode16_ctx128k", 41, DEV, with_kv=False)
+    S = P.gpu_summary(d)
+    rows = [0, 9]
+    O = np.concatenate([P.oracle_summary({**d, "k_idx": d["k_idx"][b:b + 1],
+                                          "z_idx": d["z_idx"][b:b + 1]}) for b in rows])
+    assert np.array_equal(S[rows].cpu().numpy(), O)
+    _select_check(d, S, O, rows, seq_map={0: 0, 9: 1})
+
+
+def test_select_tie_heavy_1m_exact():
+    d = _case("decode1_ctx1m", 17, DEV, with_kv=False)
+    S = d["summary"]
+    _, ex = _select_check(d, S, P.host8(S), [0], exact=True)
+    assert ex == 0
+
+
+def test_fp8_products_exhaustive_through_scores():
+    """Every product of two finite e4m3 values, read back through the score
+    path: row a has q = code a in dim 0 of the first head of each group (all
+    else 0), candidate b has summary code b in dim 0 of every group, and only
+    the first head of a group has weight 1, so a score is relu(v(a) * v(b))."""
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    n = len(codes)
+    q8 = np.zeros((n, 16, 64), np.uint8)
+    q8[:, 0::4, 0] = codes[:, None]
+    S = np.zeros((1, n, 4, 64), np.uint8)
+    S[0, :, :, 0] = codes[:, None]
+    w = np.zeros(16, np.float32)
+    w[0::4] = 1.0
+    d = {"rows": n, "q8": torch.from_numpy(q8), "w_head": torch.from_numpy(w),
+         "row_seq": torch.zeros(n, dtype=torch.int32),
+         "row_pos": torch.full((n,), 8 * n, dtype=torch.int64)}
+    ids, sc = P.gpu_select(d, torch.from_numpy(S).to(DEV))
+    ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
+    vals = P.orc.e4m3_to_f64(codes)
+    for a in range(n):
+        prod = np.maximum(vals[a] * vals, 0.0)
+        for g in range(4):
+            got = np.zeros(n)
+            got[ids[a, g]] = sc[a, g]
+            assert np.array_equal(got, prod), (hex(codes[a]), g)
+
+
+# ---- edge rows ------------------------------------------------------------
+
+def test_edge_positions_and_invalid_rows():
+    """Rows at positions with 0, 1, 511, 512 and 513 candidates, a row in
+    another sequence inside the same 4-row tile, and two invalid rows (a
+    sequence past B, a position past the cache): ids -1 and zero output for
+    those, oracle parity for the rest."""
+    T = 8 * 520
+    d = _case("decode8_ctx3000", 11, cache_tokens=T, rows=2, batch=2)
+    pos = [0, 5, 8, 4095, 4103, 4111, 4159, 4101, 17, T - 1]
+    seq = [0, 0, 0, 0, 0, 0, 1, 0, 2, 0]
+    pos_bad = list(pos)
+    pos_bad[-1] = T                      # position past the cache
+    rows = len(pos)
+    g = torch.Generator().manual_seed(3)
+    d["q_idx"] = torch.randn((rows, 16, 64), generator=g).to(torch.bfloat16)
+    d["q"] = torch.randn((rows, 16, 128), generator=g).to(torch.bfloat16)
+    d["rows"] = rows
+    d["row_seq"] = torch.tensor(seq, dtype=torch.int32)
+    d["row_pos"] = torch.tensor(pos_bad, dtype=torch.int64)
+    S = P.gpu_summary(d)
+    O = P.oracle_summary(d)
+    assert np.array_equal(S.cpu().numpy(), O)
+    ids, sc = P.gpu_select(d, S)
+    out, lse = P.gpu_attn(d, ids)
+    torch.cuda.synchronize()
+    ids_h, sc_h = ids.cpu().numpy(), sc.cpu().numpy()
+    good = [i for i in range(rows) if seq[i] < 2 and pos_bad[i] < T]
+    for bad in (8, 9):
+        assert np.all(ids_h[bad] == -1) and np.all(sc_h[bad] == 0)
+        assert torch.all(out[bad] == 0) and torch.all(torch.isneginf(lse[bad]))
+    osc = P.oracle_scores(d, O, good)
+    P.compare_selection(ids_h[good], sc_h[good], osc, np.array(pos)[good])
+    oo, ol = P.orc.attend(P.host16(d["q"])[good], P.host16(d["k_cache"]), P.host16(d["v_cache"]),
+                          ids_h[good], np.array(seq, np.int32)[good], np.array(pos)[good], P.SCALE)
+    P.compare_attention(out[good], lse[good], oo, ol, "edge rows")
+    # position 0: the output is v_0 of each KV head
+    v0 = d["v_cache"][0, 0].float()
+    assert torch.equal(out[0].cpu().float(), v0.repeat_interleave(4, 0))
+
+
+# ---- attention ------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [17, 41])
+def test_attention_decode1_ctx6000(seed):
+    d = _case("decode1_ctx6000", seed)
+    S = P.gpu_summary(d)
+    ids, _ = P.gpu_select(d, S)
+    out, lse = P.gpu_attn(d, ids)
+    oo, ol = P.orc.attend(P.host16(d["q"]), P.host16(d["k_cache"]), P.host16(d["v_cache"]),
+                          ids.cpu().numpy(), d["row_seq"].numpy(), d["row_pos"].numpy(), P.SCALE)
+    e = P.compare_attention(out, lse, oo, ol, "decode1_ctx6000")
+    P.say(f"  max abs err {e:.3g}")
+
+
+def test_attention_equals_dense_decode8_ctx3000():
+    """374 candidates: every region is selected, so the sparse output must be
+    dense causal attention; checked against the oracle and against a plain
+    fp64 dense computation."""
+    d = _case("decode8_ctx3000", 17)
+    S = P.gpu_summary(d)
+    ids, _ = P.gpu_select(d, S)
+    out, lse = P.gpu_attn(d, ids)
+    q = d["q"].double()
+    k = d["k_cache"].double()
+    v = d["v_cache"].double()
+    ref = torch.empty((8, 16, 128), dtype=torch.float64)
+    ref_lse = torch.empty((8, 16), dtype=torch.float64)
+    for r in range(8):
+        for h in range(16):
+            lg = (k[r, :3000, h // 4] @ q[r, h]) * P.SCALE
+            ref_lse[r, h] = torch.logsumexp(lg, 0)
+            ref[r, h] = torch.softmax(lg, 0) @ v[r, :3000, h // 4]
+    e = P.compare_attention(out, lse, ref.numpy(), ref_lse.numpy(), "dense")
+    P.say(f"  max abs err vs dense {e:.3g}")
+
+
+def test_attention_prefill2048_ctx32k_sampled():
+    d = _case("prefill2048_ctx32k", 41, DEV)
+    S = P.gpu_summary(d)
+    ids, _ = P.gpu_select(d, S)
+    out, lse = P.gpu_attn(d, ids)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 31, 32, 777, 1024, 2046, 2047])
+    oo, ol = P.orc.attend(P.host16(d["q"])[rows], P.host16(d["k_cache"]), P.host16(d["v_cache"]),
+                          ids.cpu().numpy()[rows], np.zeros(len(rows), np.int32),
+                          d["row_pos"].cpu().numpy()[rows], P.SCALE)
+    e = P.compare_attention(out[rows], lse[rows], oo, ol, "prefill")
+    P.say(f"  max abs err {e:.3g}")
+
+
+def test_attention_decode16_ctx128k_sampled():
+    d = _case("decode16_ctx128k", 17, DEV)
+    S = P.gpu_summary(d)
+    ids, _ = P.gpu_select(d, S)
+    out, lse = P.gpu_attn(d, ids)
+    torch.cuda.synchronize()
+    rows = [3, 12]
+    kh = np.concatenate([P.host16(d["k_cache"][b:b + 1]) for b in rows])
+    vh = np.concatenate([P.host16(d["v_cache"][b:b + 1]) for b in rows])
+    oo, ol = P.orc.attend(P.host16(d["q"])[rows], kh, vh, ids.cpu().numpy()[rows],
+                          np.arange(len(rows), dtype=np.int32), d["row_pos"].cpu().numpy()[rows],
+                          P.SCALE)
+    e = P.compare_attention(out[rows], lse[rows], oo, ol, "decode16_ctx128k")
+    P.say(f"  max abs err {e:.3g}")
+
+
+def test_attention_tie_heavy_1m():
+    d = _case("decode1_ctx1m", 41, DEV)
+    ids, _ = P.gpu_select(d, d["summary"])
+    out, lse = P.gpu_attn(d, ids)
+    torch.cuda.synchronize()
+    oo, ol = P.orc.attend(P.host16(d["q"]), P.host16(d["k_cache"]), P.host16(d["v_cache"]),
+                          ids.cpu().numpy(), np.zeros(1, np.int32), d["row_pos"].cpu().numpy(),
+                          P.SCALE)
+    e = P.compare_attention(out, lse, oo, ol, "decode1_ctx1m")
+    P.say(f"  max abs err {e:.3g}")
+
+
+# ---- determinism and contracts ----------------------------------------------
+
+def test_run_twice_bitwise_decode16_ctx128k():
+    d = _case("decode16_ctx128k", 1234, DEV)
+    S1 = P.gpu_summary(d)
+    S2 = P.gpu_summary(d)
+    assert torch.equal(S1, S2)
+    i1, s1 = P.gpu_select(d, S1)
+    i2, s2 = P.gpu_select(d, S1)
+    assert torch.equal(i1, i2) and torch.equal(s1, s2)
+    o1, l1 = P.gpu_attn(d, i1)
+    o2, l2 = P.gpu_attn(d, i1)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_rejected_calls_write_nothing():
+    import long_context_sparse_indexer_amd as s5
+    d = _case("decode1_ctx6000", 17)
+    S = torch.full((1, 750, 4, 64), 0x5A, dtype=torch.uint8, device=DEV)
+    with pytest.raises(s5.Step5Error):
+        s5.step5_index_summarize(d["k_idx"].to(DEV)[:, 4:], d["z_idx"].to(DEV)[:, 4:], 4,
+                                 d["ln_w"].to(DEV), d["ln_b"].to(DEV), P.EPS, d["rope"].to(DEV), S)
+    ids = torch.full((1, 4, 512), 7, dtype=torch.int32, device=DEV)
+    with pytest.raises(s5.Step5Error):
+        s5.step5_index_score_topk(d["q_idx"].to(DEV), d["w_head"].to(DEV), d["row_seq"].to(DEV),
+                                  d["row_pos"].to(DEV), S, ids, q_norm_w=d["q_norm_w"].to(DEV),
+                                  q_eps=-1.0, rope=d["rope"].to(DEV))
+    torch.cuda.synchronize()
+    assert torch.all(S == 0x5A) and torch.all(ids == 7)

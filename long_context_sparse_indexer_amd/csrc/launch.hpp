@@ -23,6 +23,7 @@ struct SummarizeArgs {
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
 
 struct QPrepArgs {
+  bool prepared;          // q is already e4m3 (row stride in bytes); else bf16 (elements)
   const void* q;
   int64_t q_stride_row;
   int32_t rows;
@@ -31,13 +32,12 @@ struct QPrepArgs {
   const void* rope;
   int64_t rope_rows;
   const int64_t* row_pos;
-  uint8_t* q8;  // [rows, 16, 64]
+  double* q64;            // [rows, 4 groups, 64 dims, 4 heads]: exact values of the e4m3 q
 };
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream);
 
 struct ScoreArgs {
-  const uint8_t* q8;
-  int64_t q8_stride_row;  // bytes
+  const double* q64;      // from launch_qprep
   int32_t rows;
   const float* w_head;
   int64_t w_stride_row;

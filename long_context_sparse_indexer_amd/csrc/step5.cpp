@@ -47,13 +47,13 @@ int check_geom(const step5_geom* g) {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 struct ScoreWs {
-  size_t q8 = 0, scores = 0, partial = 0, total = 0;
+  size_t q64 = 0, scores = 0, partial = 0, total = 0;
 };
 ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   ScoreWs w;
   size_t off = 0;
-  w.q8 = off;
-  off = up(off + (size_t)rows * kIdxHeads * kIdxDim);
+  w.q64 = off;  // exact fp64 query, [rows, groups, idx_dim, heads per group]
+  off = up(off + (size_t)rows * kIdxHeads * kIdxDim * sizeof(double));
   w.scores = off;
   off = up(off + (size_t)rows * kGroups * (size_t)R_cap * sizeof(float));
   w.partial = off;
@@ -166,27 +166,22 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   if (ws_bytes < w.total || !workspace || !aligned(workspace, kAlign)) return STEP5_E_WORKSPACE;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  const uint8_t* q8 = static_cast<const uint8_t*>(q);
-  int64_t q8_stride = q_stride_row;
-  if (!q_ready) {
-    s5::QPrepArgs qa;
-    qa.q = q;
-    qa.q_stride_row = q_stride_row;
-    qa.rows = rows;
-    qa.w = q_norm_w;
-    qa.eps = q_eps;
-    qa.rope = rope_cs;
-    qa.rope_rows = rope_rows;
-    qa.row_pos = row_pos;
-    qa.q8 = ws + w.q8;
-    const int st = from_hip(s5::launch_qprep(qa, stream));
-    if (st) return st;
-    q8 = ws + w.q8;
-    q8_stride = (int64_t)kIdxHeads * kIdxDim;
-  }
+  double* q64 = reinterpret_cast<double*>(ws + w.q64);
+  s5::QPrepArgs qa;
+  qa.prepared = q_ready;
+  qa.q = q;
+  qa.q_stride_row = q_stride_row;
+  qa.rows = rows;
+  qa.w = q_norm_w;
+  qa.eps = q_eps;
+  qa.rope = rope_cs;
+  qa.rope_rows = q_ready ? 0 : rope_rows;
+  qa.row_pos = row_pos;
+  qa.q64 = q64;
+  int st = from_hip(s5::launch_qprep(qa, stream));
+  if (st) return st;
   s5::ScoreArgs sa;
-  sa.q8 = q8;
-  sa.q8_stride_row = q8_stride;
+  sa.q64 = q64;
   sa.rows = rows;
   sa.w_head = w_head;
   sa.w_stride_row = w_stride_row;
@@ -198,7 +193,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   sa.ssb = s_stride_b;
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
   sa.scores = reinterpret_cast<float*>(ws + w.scores);
-  int st = from_hip(s5::launch_score(sa, stream));
+  st = from_hip(s5::launch_score(sa, stream));
   if (st) return st;
   s5::TopkArgs ta;
   ta.scores = sa.scores;

@@ -176,11 +176,11 @@ def test_workspace_sizes(s5):
     assert L.step5_index_score_topk_workspace(C.byref(g), 0, 100) == 0
     assert L.step5_index_score_topk_workspace(C.byref(g), 4, 0) == 0
     assert L.step5_index_score_topk_workspace(C.byref(geom(s5, groups=2)), 4, 64) == 0
-    # q8 (rows*1024) + scores (rows*4*R_cap*4), 256-aligned, plus chunk lists when split
+    # q64 (rows*8192) + scores (rows*4*R_cap*4), 256-aligned, plus chunk lists when split
     w1 = L.step5_index_score_topk_workspace(C.byref(g), 2048, 4096)
-    assert w1 >= 2048 * 1024 + 2048 * 4 * 4096 * 4
+    assert w1 >= 2048 * 8192 + 2048 * 4 * 4096 * 4
     w4 = L.step5_index_score_topk_workspace(C.byref(g), 16, 16384)
-    assert w4 >= 16 * 1024 + 16 * 4 * 16384 * 4 + 16 * 4 * 4 * 512 * 8
+    assert w4 >= 16 * 8192 + 16 * 4 * 16384 * 4 + 16 * 4 * 4 * 512 * 8
     assert L.step5_sparse_attn_workspace(C.byref(g), 2048) == 0          # prefill: unsplit
     assert L.step5_sparse_attn_workspace(C.byref(g), 16) > 0             # decode: split states
     assert L.step5_sparse_attn_workspace(C.byref(g), 0) == 0

@@ -158,11 +158,13 @@ def test_fp8_products_exhaustive_through_scores():
     ids, sc = P.gpu_select(d, torch.from_numpy(S).to(DEV))
     ids, sc = ids.cpu().numpy(), sc.cpu().numpy()
     vals = P.orc.e4m3_to_f64(codes)
+    assert np.all(ids[:, :, n:] == -1) and np.all(sc[:, :, n:] == 0)
     for a in range(n):
         prod = np.maximum(vals[a] * vals, 0.0)
         for g in range(4):
-            got = np.zeros(n)
-            got[ids[a, g]] = sc[a, g]
+            assert sorted(ids[a, g, :n].tolist()) == list(range(n))
+            got = np.full(n, np.nan)
+            got[ids[a, g, :n]] = sc[a, g, :n]
             assert np.array_equal(got, prod), (hex(codes[a]), g)
 
 

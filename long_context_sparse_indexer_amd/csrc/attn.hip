@@ -230,30 +230,54 @@ __global__ __launch_bounds__(256) void attn_kernel(
   }
 }
 
+// Merge of a unit's split states, in split order. Wave r handles head r:
+// lane s reads split s's (m, l) (64 splits at most), the wave reduces max and
+// weighted sum, and the weights go through LDS to the o pass, where lane d
+// accumulates dims 2d, 2d+1 over the splits in order with loads kept in flight.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ partial,
                                                          int nsplit, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
+  __shared__ float f_lds[4][64];
   const int64_t unit = blockIdx.x;
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
-  const int r = threadIdx.x >> 6;
-  const int d0 = 2 * (threadIdx.x & 63);
-  const float* base = partial + (unit * nsplit * 4 + r) * AT_PART;
-  float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[(int64_t)s * 4 * AT_PART]);
+  const int r = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d0 = 2 * lane;
+  const float* base = partial + (unit * nsplit * 4 + r) * AT_PART;  // split s at + s*4*AT_PART
+  const bool have = lane < nsplit;
+  const float ms = have ? base[(int64_t)lane * 4 * AT_PART] : -INFINITY;
+  const float ls = have ? base[(int64_t)lane * 4 * AT_PART + 1] : 0.f;
+  float M = ms;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, O0 = 0.f, O1 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* ps = base + (int64_t)s * 4 * AT_PART;
-    const float f = __builtin_amdgcn_exp2f(ps[0] - Mu);
-    L = L + f * ps[1];
-    O0 = O0 + f * ps[2 + d0];
-    O1 = O1 + f * ps[3 + d0];
+  const float f = have ? __builtin_amdgcn_exp2f(ms - Mu) : 0.f;
+  float L = f * ls;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+  f_lds[r][lane] = f;
+  __syncthreads();
+  float O0 = 0.f, O1 = 0.f;
+  int s = 0;
+  for (; s + 4 <= nsplit; s += 4) {
+    float2 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float2*>(base + (int64_t)(s + u) * 4 * AT_PART + 2 + d0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      O0 = O0 + f_lds[r][s + u] * v[u].x;
+      O1 = O1 + f_lds[r][s + u] * v[u].y;
+    }
+  }
+  for (; s < nsplit; ++s) {
+    const float2 v = *reinterpret_cast<const float2*>(base + (int64_t)s * 4 * AT_PART + 2 + d0);
+    O0 = O0 + f_lds[r][s] * v.x;
+    O1 = O1 + f_lds[r][s] * v.y;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const uint32_t packed = bf16_bits(O0 * inv) | (bf16_bits(O1 * inv) << 16);
   *reinterpret_cast<uint32_t*>(out + (row * 16 + 4 * g + r) * 128 + d0) = packed;
-  if (lse && d0 == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+  if (lse && lane == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
 AttnPlan attn_plan(int32_t rows) {

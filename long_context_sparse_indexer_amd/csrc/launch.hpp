@@ -32,12 +32,14 @@ struct QPrepArgs {
   const void* rope;
   int64_t rope_rows;
   const int64_t* row_pos;
+  uint8_t* q8;            // [rows, 16, 64] e4m3
   double* q64;            // [rows, 4 groups, 64 dims, 4 heads]: exact values of the e4m3 q
 };
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream);
 
 struct ScoreArgs {
-  const double* q64;      // from launch_qprep
+  const uint8_t* q8;      // from launch_qprep, [rows, 16, 64]
+  int64_t q8_stride_row;  // bytes
   int32_t rows;
   const float* w_head;
   int64_t w_stride_row;
@@ -46,7 +48,7 @@ struct ScoreArgs {
   const uint8_t* summary;
   int64_t B, R_cap, ssb;
   int64_t pos_limit;      // rows at p >= pos_limit are invalid (no rope row)
-  float* scores;          // [rows, 4, R_cap]
+  float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score
 };
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 
@@ -62,7 +64,12 @@ TopkPlan topk_plan(int32_t rows, int64_t R_cap);
 size_t topk_partial_bytes(int32_t rows, int64_t R_cap);
 
 struct TopkArgs {
-  const float* scores;  // [rows, 4, R_cap]
+  const float2* bounds;  // [rows, 4, R_cap] from launch_score
+  const double* q64;     // exact query, for rescoring
+  const float* w_head;
+  int64_t w_stride_row;
+  const uint8_t* summary;
+  int64_t ssb;
   int32_t rows;
   int64_t R_cap;
   const int32_t* row_seq;

@@ -1,4 +1,4 @@
-// Indexer query prep and region scoring.
+// Indexer query prep and region scoring (bounds).
 //
 // TensorFold #903 ("Step-5-Preview on one 256 GB Mac"), indexer commit note:
 // the indexer q has 16 heads, RMSNorm with scale (1 + w) and NEOX rotation of
@@ -8,29 +8,40 @@
 //
 // q prep rounding points (fp32): ms = sum64(x*x)/64, r = 1/sqrt(ms + eps),
 // y = (x*r)*(1 + w), rotation a*c - b*s | b*c + a*s from bf16 cos/sin, bf16,
-// then e4m3.
+// then e4m3. It writes the e4m3 query (for the matrix cores) and its exact
+// fp64 values laid out [row][group][dim][4 heads] (for exact rescoring).
 //
-// Exact dot products. Every e4m3 x e4m3 product has at most 8 significant
-// bits, and any partial sum of 64 of them is a multiple of 2^-18 below 2^24
-// in magnitude (at most 42 significant bits), so fp64 fused multiply-adds
-// accumulate the dot product with no rounding at all, in any order. The one
-// rounding is the final fp64 -> fp32, which makes every score the exact
-// value rounded once: identical to any other exact implementation, so the
-// (-score, id) order and therefore the selected ids are reproducible bit for
-// bit. (fp8 matrix cores accumulate in fp32 and reorder candidates whose
-// scores differ by a few fp32 ulps, which is common among 10^4..10^5
-// candidates.)
+// Scoring is a 64-dim contraction of e4m3 vectors, run on the matrix cores:
+// every e4m3 value is exactly a bf16 value, so the operands are widened in
+// registers (hardware fp8 -> fp32 conversion, keep the high half) and fed to
+// the 16x16x32 bf16 MFMA, two per dot, fp32 accumulation. (Measured on
+// gfx950: the fp8 MFMA's accumulation loses up to 2^-10.8 of sum |q s|,
+// while the bf16 MFMA on the same values stays within 2^-21.8 of it and
+// returns the correctly rounded exact dot for normal and heavy-tailed data.)
+// Accumulation can still round, and scores of 10^4..10^5 candidates can be a
+// few ulps apart, so the kernel emits an interval that holds the exact score:
+// the same MFMA on absolute values (sign bits cleared) gives A = sum |q s|,
+// and with delta = 2^-18 * sum_h |w_h| A_h + 2^-22 |s~| the exact score lies
+// in [s~ - delta, s~ + delta] (a margin of 4 over eight truncating additions
+// per dot, 14 over the measured worst case). The selection pass uses the
+// intervals to find which candidates can reach the top 512 and rescores only
+// those exactly (exact.hpp), so exactness never rests on the accumulator.
 //
-// Mapping: q prep writes the e4m3 query as exact fp64 values laid out
-// [row][group][dim][4 heads], so that a wave reads its group's query through
-// scalar loads. In the score kernel wave w of a block handles group w and
-// lane l one candidate: the lane reads the candidate's 64-byte group vector
-// (four 16-byte loads), converts it to fp64 once, and reuses it for every
-// row of the block's row tile that reads the same sequence (a prefill chunk
-// shares it across the tile; decode rows each bring their own).
-// Epilogue per (row, group, candidate): t_h = max(fp32(dot_h), +0), then
-// ((t0*w0 + t1*w1) + t2*w2) + t3*w3 with separately rounded products.
+// Operand lanes: lane l = 16q + n holds row/column n and the 16 contiguous
+// e4m3 bytes 16q..16q+15 of the 64-byte vector, widened to 16 bf16; the first
+// MFMA takes elements 0..7 of each lane's slice and the second 8..15,
+// identically for both operands. Output lane (n, q) holds column n, rows
+// 4q..4q+3.
+//
+// Two tilings, chosen per block of 4 rows at run time:
+//  - rows sharing one sequence (a prefill chunk): A = 4 rows x the 4 heads of
+//    group g (16 MFMA rows), B = 16 candidates of group g: every output is
+//    used and each summary byte loaded serves 4 rows;
+//  - rows of different sequences (decode): per row, A = its 16 heads,
+//    B = 4 candidates x 4 groups (1 KB contiguous); lanes whose head group
+//    matches the column's group keep their result.
 #include "device.hpp"
+#include "exact.hpp"
 #include "launch.hpp"
 
 namespace s5 {
@@ -51,7 +62,6 @@ __device__ inline double e4m3_f64(uint32_t c) {
 // ---------------------------------------------------------------------------
 // q prep: one 8-lane group per (row, head); lane c holds dims 8c..8c+7.
 // mode 0: bf16 input, full prep; mode 1: the input is already e4m3.
-// Writes q64[row][h/4][dim][h%4] (fp64 values of the e4m3 codes).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __restrict__ qin,
                                                     int64_t qs, int32_t rows,
@@ -59,6 +69,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
                                                     const uint16_t* __restrict__ rope,
                                                     int64_t rope_rows,
                                                     const int64_t* __restrict__ row_pos,
+                                                    uint8_t* __restrict__ q8,
                                                     double* __restrict__ q64) {
   const int lane = threadIdx.x & 63;
   const int c = threadIdx.x & 7;
@@ -106,6 +117,13 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
       code[i] = e4m3_from_bf16(bf16_bits(rotated ? rot : y[i]));
     }
   }
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo |= code[i] << (8 * i);
+    hi |= code[4 + i] << (8 * i);
+  }
+  *reinterpret_cast<uint2*>(q8 + vec * 64 + c * 8) = make_uint2(lo, hi);
   double* dst = q64 + ((r * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
 #pragma unroll
   for (int i = 0; i < 8; ++i) dst[i * 4] = e4m3_f64(code[i]);
@@ -116,34 +134,76 @@ hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream) {
   if (vecs == 0) return hipSuccess;
   hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)((vecs + 31) / 32)), dim3(256), 0, stream,
                      a.prepared ? 1 : 0, a.q, a.q_stride_row, a.rows, a.w, a.eps,
-                     (const uint16_t*)a.rope, a.rope_rows, a.row_pos, a.q64);
+                     (const uint16_t*)a.rope, a.rope_rows, a.row_pos, a.q8, a.q64);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// scores
+// score intervals
 // ---------------------------------------------------------------------------
-constexpr int SC_RT = 8;   // rows per tile
-constexpr int SC_CB = 64;  // candidates per block (one per lane)
+constexpr int SC_CB = 64;  // candidates per block (decode: one per wave-row; prefill: 16 per wave)
 
-__device__ inline float relu0(float v) { return v > 0.0f ? v : 0.0f; }
+// 16 e4m3 bytes -> 16 bf16 (two 8-element MFMA operands), exactly
+struct Bf16x16 {
+  uint4 lo, hi;
+};
+template <bool UPPER>
+__device__ inline uint32_t widen2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, UPPER);
+  // the high halves of the two fp32 values are their exact bf16 values;
+  // element 2k goes to the low half. The elements are copied to scalars
+  // before the bit casts: clang compiles a bit cast of a member access on an
+  // ext_vector_type value (f.y) as a cast of the vector's first element.
+  const float fx = f[0], fy = f[1];
+  const uint32_t a = __builtin_bit_cast(uint32_t, fx), b = __builtin_bit_cast(uint32_t, fy);
+  return (a >> 16) | (b & 0xffff0000u);
+}
+__device__ inline Bf16x16 widen16(uint4 v) {
+  Bf16x16 r;
+  r.lo = make_uint4(widen2<false>(v.x), widen2<true>(v.x), widen2<false>(v.y), widen2<true>(v.y));
+  r.hi = make_uint4(widen2<false>(v.z), widen2<true>(v.z), widen2<false>(v.w), widen2<true>(v.w));
+  return r;
+}
+__device__ inline uint4 abs_bf16(uint4 v) {
+  return make_uint4(v.x & 0x7fff7fffu, v.y & 0x7fff7fffu, v.z & 0x7fff7fffu, v.w & 0x7fff7fffu);
+}
+__device__ inline f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// dot over the 64 dims and the same over absolute values
+__device__ inline void dot64(const Bf16x16& a, const Bf16x16& b, f32x4& d, f32x4& ad) {
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  d = mfma_bf16(a.hi, b.hi, mfma_bf16(a.lo, b.lo, z));
+  ad = mfma_bf16(abs_bf16(a.hi), abs_bf16(b.hi), mfma_bf16(abs_bf16(a.lo), abs_bf16(b.lo), z));
+}
+
+// interval [lo, hi] around the approximate score of one (row, group, candidate)
+__device__ inline float2 score_interval(f32x4 d, f32x4 a, const float* w4) {
+  const float s = group_score4(d[0], d[1], d[2], d[3], w4);
+  const float aw = fabsf(w4[0]) * a[0] + fabsf(w4[1]) * a[1] + fabsf(w4[2]) * a[2] +
+                   fabsf(w4[3]) * a[3];
+  const float delta = 0x1p-18f * aw + 0x1p-22f * fabsf(s);
+  return make_float2(s - delta, s + delta);
+}
 
 __global__ __launch_bounds__(256) void score_kernel(
-    const double* __restrict__ q64, int32_t rows, const float* __restrict__ w_head,
+    const uint8_t* __restrict__ q8, int64_t qs8, int32_t rows, const float* __restrict__ w_head,
     int64_t w_stride, const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
     const uint8_t* __restrict__ S, int64_t B, int64_t R_cap, int64_t ssb, int64_t pos_limit,
-    float* __restrict__ scores) {
-  const int g = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // the wave's group
-  const int lane = threadIdx.x & 63;
-  const int r0 = blockIdx.y * SC_RT;
-  const int64_t j = (int64_t)blockIdx.x * SC_CB + lane;
-  const int nr = min(SC_RT, rows - r0);
+    float2* __restrict__ bounds) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  const int r0 = blockIdx.y * 4;
+  const int64_t cb0 = (int64_t)blockIdx.x * SC_CB;
+  const int nr = min(4, rows - r0);
 
-  int32_t seq[SC_RT];
-  int64_t ncand[SC_RT];
+  int32_t seq[4];
+  int64_t ncand[4];
   int64_t maxc = 0;
+  bool shared = true;
 #pragma unroll
-  for (int i = 0; i < SC_RT; ++i) {
+  for (int i = 0; i < 4; ++i) {
     seq[i] = -1;
     ncand[i] = 0;
     if (i < nr) {
@@ -155,72 +215,83 @@ __global__ __launch_bounds__(256) void score_kernel(
       maxc = ncand[i] > maxc ? ncand[i] : maxc;
     }
   }
-  if ((int64_t)blockIdx.x * SC_CB >= maxc) return;
-
-  uint32_t done = 0;
-  for (int i = 0; i < nr; ++i) {
-    if (seq[i] < 0 || ((done >> i) & 1u)) continue;
-    const int32_t s = seq[i];
-    int64_t nc_s = 0;  // candidates any row of this sequence needs
+  if (cb0 >= maxc) return;
+  int32_t s0 = -1;
 #pragma unroll
-    for (int i2 = 0; i2 < SC_RT; ++i2)
-      if (seq[i2] == s && ncand[i2] > nc_s) nc_s = ncand[i2];
-    // this lane's candidate vector for group g, as exact fp64
-    double sv[64];
-    if (j < nc_s) {
-      const uint8_t* src = S + (int64_t)s * ssb + j * 256 + g * 64;
-#pragma unroll
-      for (int part = 0; part < 4; ++part) {
-        const uint4 raw = ldg16(src + 16 * part);
-        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[k], false);
-          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[k], true);
-          sv[16 * part + 4 * k + 0] = (double)lo.x;
-          sv[16 * part + 4 * k + 1] = (double)lo.y;
-          sv[16 * part + 4 * k + 2] = (double)hi.x;
-          sv[16 * part + 4 * k + 3] = (double)hi.y;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int d = 0; d < 64; ++d) sv[d] = 0.0;
+  for (int i = 0; i < 4; ++i) {
+    if (seq[i] >= 0) {
+      if (s0 < 0) s0 = seq[i];
+      else if (seq[i] != s0) shared = false;
     }
-    for (int i2 = i; i2 < nr; ++i2) {
-      if (seq[i2] != s) continue;
-      done |= 1u << i2;
-      const int row = r0 + i2;
-      const double* qg = q64 + ((int64_t)row * 4 + g) * 256;  // [64 dims][4 heads], wave-uniform
-      double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  }
+
+  if (shared) {
+    // ---- one sequence: A = (4 rows x 4 heads of group g), B = 16 candidates of g
+    const uint8_t* Sb = S + (int64_t)s0 * ssb;
+    const int rr = n >> 2, hh = n & 3;
+    Bf16x16 aq[4];
 #pragma unroll
-      for (int d = 0; d < 64; ++d) {
-        a0 = fma(qg[4 * d + 0], sv[d], a0);
-        a1 = fma(qg[4 * d + 1], sv[d], a1);
-        a2 = fma(qg[4 * d + 2], sv[d], a2);
-        a3 = fma(qg[4 * d + 3], sv[d], a3);
-      }
-      if (j < ncand[i2]) {
-        const float* w4 = w_head + (int64_t)row * w_stride + 4 * g;
-        const float t0 = relu0((float)a0) * w4[0];
-        const float t1 = relu0((float)a1) * w4[1];
-        const float t2 = relu0((float)a2) * w4[2];
-        const float t3 = relu0((float)a3) * w4[3];
-        float sc = t0 + t1;
-        sc = sc + t2;
-        sc = sc + t3;
-        scores[((int64_t)row * 4 + g) * R_cap + j] = sc;
-      }
+    for (int g = 0; g < 4; ++g) {
+      uint4 raw = make_uint4(0, 0, 0, 0);
+      if (rr < nr && seq[rr] >= 0) raw = ldg16(q8 + (int64_t)(r0 + rr) * qs8 + (4 * g + hh) * 64 + 16 * qd);
+      aq[g] = widen16(raw);
+    }
+    const int orow = r0 + qd;
+    const bool orow_ok = qd < nr && seq[qd] >= 0;
+    const int64_t onc = orow_ok ? ncand[qd] : 0;
+    float w4[4][4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w4[g][i] = orow_ok ? w_head[(int64_t)orow * w_stride + 4 * g + i] : 0.f;
+
+    const int64_t j = cb0 + wave * 16 + n;  // this lane's candidate column
+    uint4 bq[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      bq[g] = (j < maxc) ? ldg16(Sb + j * 256 + g * 64 + 16 * qd) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 d, a;
+      dot64(aq[g], widen16(bq[g]), d, a);
+      if (j < onc) bounds[((int64_t)orow * 4 + g) * R_cap + j] = score_interval(d, a, w4[g]);
+    }
+  } else {
+    // ---- rows of different sequences: wave w scores row r0 + w
+    if (wave >= nr || seq[wave] < 0) return;
+    const int row = r0 + wave;
+    const int64_t nc = ncand[wave];
+    if (cb0 >= nc) return;
+    const uint8_t* Sb = S + (int64_t)seq[wave] * ssb;
+    const Bf16x16 aq = widen16(ldg16(q8 + (int64_t)row * qs8 + n * 64 + 16 * qd));
+    float w4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w4[i] = w_head[(int64_t)row * w_stride + 4 * qd + i];
+    const bool keep = qd == (n & 3);
+    const int64_t jend = (cb0 + SC_CB < nc) ? cb0 + SC_CB : nc;
+    // all 64 candidates' loads in flight at once (16 per lane)
+    uint4 bq[SC_CB / 4];
+#pragma unroll
+    for (int u = 0; u < SC_CB / 4; ++u) {
+      const int64_t j = cb0 + u * 4 + (n >> 2);
+      bq[u] = (j < jend) ? ldg16(Sb + (cb0 + u * 4) * 256 + n * 64 + 16 * qd) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < SC_CB / 4; ++u) {
+      const int64_t j = cb0 + u * 4 + (n >> 2);
+      f32x4 d, a;
+      dot64(aq, widen16(bq[u]), d, a);
+      if (keep && j < jend) bounds[((int64_t)row * 4 + qd) * R_cap + j] = score_interval(d, a, w4);
     }
   }
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.rows == 0 || a.R_cap == 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + SC_RT - 1) / SC_RT));
-  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, a.q64, a.rows, a.w_head,
-                     a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                     a.pos_limit, a.scores);
+  const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));
+  hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, a.q8, a.q8_stride_row, a.rows,
+                     a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap,
+                     a.ssb, a.pos_limit, a.bounds);
   return hipGetLastError();
 }
 

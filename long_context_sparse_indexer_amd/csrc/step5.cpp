@@ -47,15 +47,17 @@ int check_geom(const step5_geom* g) {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 struct ScoreWs {
-  size_t q64 = 0, scores = 0, partial = 0, total = 0;
+  size_t q8 = 0, q64 = 0, bounds = 0, partial = 0, total = 0;
 };
 ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   ScoreWs w;
   size_t off = 0;
-  w.q64 = off;  // exact fp64 query, [rows, groups, idx_dim, heads per group]
+  w.q8 = off;   // prepared e4m3 query, [rows, idx_heads, idx_dim]
+  off = up(off + (size_t)rows * kIdxHeads * kIdxDim);
+  w.q64 = off;  // its exact fp64 values, [rows, groups, idx_dim, heads per group]
   off = up(off + (size_t)rows * kIdxHeads * kIdxDim * sizeof(double));
-  w.scores = off;
-  off = up(off + (size_t)rows * kGroups * (size_t)R_cap * sizeof(float));
+  w.bounds = off;  // score interval per (row, group, candidate)
+  off = up(off + (size_t)rows * kGroups * (size_t)R_cap * 2 * sizeof(float));
   w.partial = off;
   off = up(off + s5::topk_partial_bytes(rows, R_cap));
   w.total = off;
@@ -167,6 +169,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   double* q64 = reinterpret_cast<double*>(ws + w.q64);
+  uint8_t* q8 = ws + w.q8;
   s5::QPrepArgs qa;
   qa.prepared = q_ready;
   qa.q = q;
@@ -177,11 +180,13 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   qa.rope = rope_cs;
   qa.rope_rows = q_ready ? 0 : rope_rows;
   qa.row_pos = row_pos;
+  qa.q8 = q8;
   qa.q64 = q64;
   int st = from_hip(s5::launch_qprep(qa, stream));
   if (st) return st;
   s5::ScoreArgs sa;
-  sa.q64 = q64;
+  sa.q8 = q8;
+  sa.q8_stride_row = (int64_t)kIdxHeads * kIdxDim;
   sa.rows = rows;
   sa.w_head = w_head;
   sa.w_stride_row = w_stride_row;
@@ -192,11 +197,16 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   sa.R_cap = R_cap;
   sa.ssb = s_stride_b;
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
-  sa.scores = reinterpret_cast<float*>(ws + w.scores);
+  sa.bounds = reinterpret_cast<float2*>(ws + w.bounds);
   st = from_hip(s5::launch_score(sa, stream));
   if (st) return st;
   s5::TopkArgs ta;
-  ta.scores = sa.scores;
+  ta.bounds = sa.bounds;
+  ta.q64 = q64;
+  ta.w_head = w_head;
+  ta.w_stride_row = w_stride_row;
+  ta.summary = static_cast<const uint8_t*>(summary);
+  ta.ssb = s_stride_b;
   ta.rows = rows;
   ta.R_cap = R_cap;
   ta.row_seq = row_seq;

@@ -3,11 +3,11 @@ Python binding) and the CPU oracle on the same input bytes, and compare them
 under the path's acceptance rules:
 
   summaries   e4m3 codes bit-exact;
-  selections  region ids bit-exact position by position, except where the
-              oracle's own scores of the two ids differ by less than 1e-6 of
-              the oracle's score at the last kept position (float noise of
-              the MFMA's fp32 accumulation can swap such near-ties); those
-              excusals are counted and reported;
+  selections  region ids and their scores bit-exact position by position
+              (the GPU rescores every possible member exactly). The
+              comparison can also excuse near-ties (oracle scores of the two
+              ids within 1e-6 of the last kept score) and count them; the
+              tests run it strict, with no excusal allowed;
   attention   |gpu - oracle| <= 2e-3 + 1e-2 |oracle| element by element, the
               oracle run in fp64 on the GPU's own selection.
 """
@@ -116,7 +116,7 @@ def oracle_scores(d, summary_np, rows, seq_map=None):
 
 # ---- comparisons ------------------------------------------------------------
 
-def compare_selection(gids, gsc, oscores, pos, topk=512, exact=False):
+def compare_selection(gids, gsc, oscores, pos, topk=512, exact=True):
     """gids/gsc: GPU ids and scores [n, 4, topk]; oscores: oracle scores of all
     candidates [n, 4, R_cap]; pos: positions [n]. Returns the excusal count;
     raises AssertionError on a failure."""

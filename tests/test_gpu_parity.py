@@ -1,9 +1,9 @@
 """GPU parity: the HIP path (called through the C ABI) against the CPU oracle on
 the same seeded inputs, for the five workloads, with edge cases.
 
-Rules (see tests/parity.py): summaries bit-exact; ids bit-exact except counted
-near-ties (none allowed on the tie-heavy workload, whose arithmetic is exact);
-attention within 2e-3 + 1e-2|ref| of the fp64 oracle.
+Rules (see tests/parity.py): summaries bit-exact; selected ids and their
+scores bit-exact (no near-tie excusals); attention within 2e-3 + 1e-2|ref| of
+the fp64 oracle.
 """
 import numpy as np
 import pytest
@@ -81,7 +81,7 @@ def test_summary_fresh_span_1m_workload():
 
 # ---- selection ------------------------------------------------------------
 
-def _select_check(d, S_gpu, O_summary, rows, seq_map=None, exact=False):
+def _select_check(d, S_gpu, O_summary, rows, seq_map=None, exact=True):
     ids, sc = P.gpu_select(d, S_gpu)
     torch.cuda.synchronize()
     osc = P.oracle_scores(d, O_summary, rows, seq_map)
@@ -166,6 +166,48 @@ def test_fp8_products_exhaustive_through_scores():
             got = np.full(n, np.nan)
             got[ids[a, g, :n]] = sc[a, g, :n]
             assert np.array_equal(got, prod), (hex(codes[a]), g)
+
+
+def _bounds_view(ws, rows, R_cap):
+    """The score intervals inside step5_index_score_topk's workspace (white-box:
+    e4m3 q [rows*1024 B], fp64 q [rows*8192 B], then float2 [rows, 4, R_cap],
+    each part 256-byte aligned)."""
+    up = lambda x: (x + 255) // 256 * 256
+    off = up(up(rows * 1024) + rows * 8192)
+    n = rows * 4 * R_cap * 2
+    return ws[off:off + n * 4].view(torch.float32).view(rows, 4, R_cap, 2)
+
+
+@pytest.mark.parametrize("name,rows", [("decode16_ctx128k", [0, 5, 10]),
+                                       ("prefill2048_ctx32k", [0, 1, 1000, 2047])])
+def test_score_intervals_hold_exact_scores(name, rows):
+    """The matrix-core scores come with intervals derived from an error bound
+    of fp32 accumulation; every interval must hold the exact score."""
+    import long_context_sparse_indexer_amd as s5
+    d = _case(name, 23, DEV, with_kv=False)
+    S = P.gpu_summary(d)
+    R_cap = S.shape[1]
+    nb = s5.step5_index_score_topk_workspace(d["rows"], R_cap)
+    ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    ids = torch.empty((d["rows"], 4, 512), dtype=torch.int32, device=DEV)
+    s5.step5_index_score_topk(d["q_idx"], d["w_head"], d["row_seq"], d["row_pos"], S, ids,
+                              q_norm_w=d["q_norm_w"], q_eps=P.EPS, rope=d["rope"], workspace=ws)
+    torch.cuda.synchronize()
+    bnd = _bounds_view(ws, d["rows"], R_cap).cpu().numpy()[rows]
+    seqs = sorted({int(d["row_seq"][r]) for r in rows})
+    O = np.concatenate([P.oracle_summary({**d, "k_idx": d["k_idx"][s:s + 1],
+                                          "z_idx": d["z_idx"][s:s + 1]}) for s in seqs])
+    osc = P.oracle_scores(d, O, rows, {s: i for i, s in enumerate(seqs)})
+    worst = 0.0
+    for i, r in enumerate(rows):
+        nc = int(d["row_pos"][r]) // 8
+        lo, hi, ex = bnd[i, :, :nc, 0], bnd[i, :, :nc, 1], osc[i, :, :nc]
+        assert np.all(lo <= ex) and np.all(ex <= hi), (name, r)
+        half = (hi - lo) / 2
+        mid = (hi + lo) / 2
+        ok = half > 0
+        worst = max(worst, float(np.max(np.abs(mid[ok] - ex[ok]) / half[ok])))
+    P.say(f"  largest |approx - exact| / half-width = {worst:.4f}")
 
 
 # ---- edge rows ------------------------------------------------------------

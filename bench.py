@@ -126,18 +126,10 @@ def main():
         s5.step5_sparse_attn(d["q"], d["k_cache"], d["v_cache"], ids, d["row_seq"], d["row_pos"],
                              scale, out, lse, workspace=ws2)
 
-    side = torch.cuda.Stream()
-
     def call_indexer():
-        # the own-region summary does not feed this step's selection (a row's
-        # own region is never a candidate), so it runs on a forked branch
-        if k_own is not None:
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                call_summarize()
+        # own-region summary (feeds the next step), then this step's selection
+        call_summarize()
         call_score()
-        if k_own is not None:
-            torch.cuda.current_stream().wait_stream(side)
 
     calls = [("indexer", call_indexer), ("sparse_attn", call_attn)]
     for _ in range(args.warmup):

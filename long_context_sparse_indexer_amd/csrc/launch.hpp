@@ -34,6 +34,7 @@ struct QPrepArgs {
   const int64_t* row_pos;
   uint8_t* q8;            // [rows, 16, 64] e4m3
   double* q64;            // [rows, 4 groups, 64 dims, 4 heads]: exact values of the e4m3 q
+  unsigned* arrivals;     // [rows*4] top-k arrival counters, zeroed here
 };
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream);
 
@@ -76,7 +77,8 @@ struct TopkArgs {
   const int64_t* row_pos;
   int64_t B;
   int64_t pos_limit;
-  unsigned long long* partial;  // [rows*4, nchunks, 512] when nchunks > 1
+  unsigned long long* partial;  // [rows*4, nchunks, 512] chunk lists when nchunks > 1
+  unsigned* arrivals;    // [rows*4], zero on entry (q prep zeroes them)
   int32_t* sel_ids;
   float* sel_scores;
 };

@@ -70,10 +70,16 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
                                                     int64_t rope_rows,
                                                     const int64_t* __restrict__ row_pos,
                                                     uint8_t* __restrict__ q8,
-                                                    double* __restrict__ q64) {
+                                                    double* __restrict__ q64,
+                                                    unsigned* __restrict__ arrivals) {
   const int lane = threadIdx.x & 63;
   const int c = threadIdx.x & 7;
   const int64_t vec = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  {
+    // the selection pass of this call counts chunk arrivals per (row, group)
+    const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (u < (int64_t)rows * 4) arrivals[u] = 0u;
+  }
   if (vec >= (int64_t)rows * 16) return;  // whole 8-lane groups leave together
   const int64_t r = vec >> 4;
   const int h = (int)(vec & 15);
@@ -134,7 +140,7 @@ hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream) {
   if (vecs == 0) return hipSuccess;
   hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)((vecs + 31) / 32)), dim3(256), 0, stream,
                      a.prepared ? 1 : 0, a.q, a.q_stride_row, a.rows, a.w, a.eps,
-                     (const uint16_t*)a.rope, a.rope_rows, a.row_pos, a.q8, a.q64);
+                     (const uint16_t*)a.rope, a.rope_rows, a.row_pos, a.q8, a.q64, a.arrivals);
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@ int check_geom(const step5_geom* g) {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 struct ScoreWs {
-  size_t q8 = 0, q64 = 0, bounds = 0, partial = 0, total = 0;
+  size_t q8 = 0, q64 = 0, bounds = 0, partial = 0, arrivals = 0, total = 0;
 };
 ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   ScoreWs w;
@@ -60,6 +60,8 @@ ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   off = up(off + (size_t)rows * kGroups * (size_t)R_cap * 2 * sizeof(float));
   w.partial = off;
   off = up(off + s5::topk_partial_bytes(rows, R_cap));
+  w.arrivals = off;  // chunk arrival counters per (row, group)
+  off = up(off + (size_t)rows * kGroups * sizeof(unsigned));
   w.total = off;
   return w;
 }
@@ -182,6 +184,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   qa.row_pos = row_pos;
   qa.q8 = q8;
   qa.q64 = q64;
+  qa.arrivals = reinterpret_cast<unsigned*>(ws + w.arrivals);
   int st = from_hip(s5::launch_qprep(qa, stream));
   if (st) return st;
   s5::ScoreArgs sa;
@@ -214,6 +217,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   ta.B = B;
   ta.pos_limit = sa.pos_limit;
   ta.partial = reinterpret_cast<unsigned long long*>(ws + w.partial);
+  ta.arrivals = qa.arrivals;
   ta.sel_ids = sel_ids;
   ta.sel_scores = sel_scores;
   return from_hip(s5::launch_topk(ta, stream));

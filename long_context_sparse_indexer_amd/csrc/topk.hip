@@ -13,9 +13,11 @@
 //      hi >= exact score >= K-th largest exact score >= K-th largest lo = T;
 //   3. every member of C is rescored exactly (exact.hpp);
 //   4. the best K of C by (-exact score, id) are selected and sorted.
-// Candidate ranges past 16,384 are cut into chunks of at most that: each
-// chunk keeps its exact best 512 in order, and a merge pass ranks the
-// elements of the chunk lists against each other.
+// Candidate ranges past 16,384, and batches too small to fill the GPU, are
+// cut into chunks: each chunk keeps its exact best 512 in order; the last
+// chunk of a (row, group) to finish (an arrival counter per unit, zeroed by
+// the query prep of the same call) ranks the elements of the chunk lists
+// against each other.
 //
 // Selecting the best K of N exact keys (scores mapped to 32-bit keys that
 // order like the scores, -0 taken as +0; ties broken by id):
@@ -249,6 +251,10 @@ __device__ void rank_sort(const TkShared& sm, int K) {
   __syncthreads();
 }
 
+__device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int K,
+                            int64_t unit, unsigned char* smem, int32_t* __restrict__ sel_ids,
+                            float* __restrict__ sel_scores);
+
 __device__ inline void unit_row(const int32_t* row_seq, const int64_t* row_pos, int64_t B,
                                 int64_t R_cap, int64_t pos_limit, int64_t row, int32_t* seq,
                                 int64_t* ncand) {
@@ -276,8 +282,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     const int64_t* __restrict__ row_pos, int64_t B, int64_t pos_limit,
     const double* __restrict__ q64, const float* __restrict__ w_head, int64_t w_stride,
     const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
-    unsigned long long* __restrict__ partial, int32_t* __restrict__ sel_ids,
-    float* __restrict__ sel_scores) {
+    unsigned long long* __restrict__ partial, unsigned* __restrict__ arrivals,
+    int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t unit = blockIdx.x;
   const int c = blockIdx.y;
@@ -295,20 +301,34 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   const float2* bsrc = bounds + unit * R_cap + j0;
   int M = 0;
   if (K > 0) {
-    // 1. K-th largest lower bound
-    for (int i = tid; i < N; i += TK_THREADS) sm.keys[i] = ord_key(bsrc[i].x);
+    // 1. K-th largest lower bound (upper bounds parked in ids[] meanwhile)
+    for (int i = tid; i < N; i += TK_THREADS) {
+      const float2 b = bsrc[i];
+      sm.keys[i] = ord_key(b.x);
+      sm.ids[i] = (int32_t)ord_key(b.y);
+    }
     __syncthreads();
     const Boundary bd = radix_boundary(sm, N, K, false);
     const uint32_t T = bd.P;
-    // 2. candidates whose upper bound reaches T, in id order
-    const int seg = (N + TK_THREADS - 1) / TK_THREADS;
+    // 2. candidates whose upper bound reaches T, in id order: each thread
+    //    takes its segment's upper bounds into registers, the scan orders the
+    //    writes (its barriers separate every read from every write)
+    const int seg = (N + TK_THREADS - 1) / TK_THREADS;  // <= TK_MAX_N / TK_THREADS
     const int i0 = min(N, tid * seg), i1 = min(N, i0 + seg);
-    uint32_t cnt = 0;
-    for (int i = i0; i < i1; ++i) cnt += ord_key(bsrc[i].y) >= T;
+    uint32_t flags = 0, cnt = 0;
+#pragma unroll
+    for (int k = 0; k < (int)(TK_MAX_N / TK_THREADS); ++k) {
+      const int i = i0 + k;
+      if (i < i1 && (uint32_t)sm.ids[i] >= T) {
+        flags |= 1u << k;
+        ++cnt;
+      }
+    }
     uint32_t total;
     uint32_t off = block_excl_scan(cnt, sm.misc, &total);
-    for (int i = i0; i < i1; ++i)
-      if (ord_key(bsrc[i].y) >= T) sm.ids[off++] = (int32_t)(j0 + i);
+#pragma unroll
+    for (int k = 0; k < (int)(TK_MAX_N / TK_THREADS); ++k)
+      if ((flags >> k) & 1u) sm.ids[off++] = (int32_t)(j0 + i0 + k);
     M = (int)total;
     __syncthreads();
     // 3. exact scores of the survivors: two threads per candidate (dims
@@ -336,34 +356,39 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   select_sorted(sm, M, K, sm.ids, 0);
   if (mode == 0) {
     write_final(sm, K, unit, sel_ids, sel_scores);
-  } else {
-    unsigned long long* dst = partial + (unit * nchunks + c) * TK;
-    for (int i = tid; i < TK; i += TK_THREADS) dst[i] = sm.out[i];
+    return;
   }
+  // chunk list out; the unit's last block to arrive merges all of them
+  unsigned long long* dst = partial + (unit * nchunks + c) * TK;
+  for (int i = tid; i < TK; i += TK_THREADS) dst[i] = sm.out[i];
+  __shared__ int sh_last;
+  __syncthreads();  // every thread's list stores have completed
+  if (tid == 0) {
+    __threadfence();  // release: the block's stores become visible device-wide
+    sh_last = atomicAdd(&arrivals[unit], 1u) == (unsigned)(nchunks - 1);
+    if (sh_last) __threadfence();  // acquire: drop stale copies before reading the lists
+  }
+  __syncthreads();
+  if (!sh_last) return;
+  const int Kall = ncand < TK ? (int)ncand : TK;
+  merge_lists(partial + unit * (int64_t)nchunks * TK, nchunks, Kall, unit, smem, sel_ids,
+              sel_scores);
 }
 
 // Merge of the chunk lists of one (row, group): each list is sorted best
 // first and composites are distinct, so an element's rank in the union is its
 // index in its own list plus, for every other list, the number of elements
-// above it there (a binary search). Elements ranked below 512 go to their
-// rank: the output is sorted.
-__global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
-    int64_t R_cap, const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
-    int64_t B, int64_t pos_limit, int nchunks, const unsigned long long* __restrict__ partial,
-    int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores) {
-  extern __shared__ __align__(16) unsigned char smem[];
+// above it there (a binary search). Elements ranked below K go to their rank:
+// the output is sorted. smem holds (nchunks + 1) * TK composites.
+__device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int K,
+                            int64_t unit, unsigned char* smem, int32_t* __restrict__ sel_ids,
+                            float* __restrict__ sel_scores) {
   unsigned long long* lists = reinterpret_cast<unsigned long long*>(smem);  // [nchunks][TK]
   unsigned long long* outl = lists + (int64_t)nchunks * TK;                 // [TK]
-  const int64_t unit = blockIdx.x;
   const int N = nchunks * TK;
-  int32_t seq;
-  int64_t ncand;
-  unit_row(row_seq, row_pos, B, R_cap, pos_limit, unit >> 2, &seq, &ncand);
-  const unsigned long long* src = partial + unit * (int64_t)nchunks * TK;
   for (int i = threadIdx.x; i < N; i += TK_THREADS) lists[i] = src[i];
   for (int i = threadIdx.x; i < TK; i += TK_THREADS) outl[i] = 0ull;
   __syncthreads();
-  const int K = ncand < TK ? (int)ncand : TK;
   for (int i = threadIdx.x; i < N; i += TK_THREADS) {
     const unsigned long long x = lists[i];
     if (x == 0ull) continue;  // padding
@@ -391,8 +416,15 @@ __global__ __launch_bounds__(TK_THREADS) void topk_merge_kernel(
 }
 
 TopkPlan topk_plan(int32_t rows, int64_t R_cap) {
-  (void)rows;
-  int64_t n = (R_cap + TK_MAX_N - 1) / TK_MAX_N;  // chunks of at most 16,384 candidates
+  // at most 16,384 candidates per chunk; a batch too small to fill the GPU
+  // (rows * 4 units) is cut further, into chunks of at least 2,048, up to 16
+  const int64_t units = (int64_t)rows * 4;
+  const int64_t nmin = (R_cap + TK_MAX_N - 1) / TK_MAX_N;
+  int64_t want = units > 0 ? (256 + units - 1) / units : 1;
+  const int64_t by_size = (R_cap + 2047) / 2048;
+  if (want > by_size) want = by_size;
+  if (want > 16) want = 16;
+  int64_t n = want > nmin ? want : nmin;
   if (n < 1) n = 1;
   TopkPlan p;
   p.nchunks = (int32_t)n;
@@ -414,24 +446,17 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   const TopkPlan p = topk_plan(a.rows, a.R_cap);
   const unsigned units = (unsigned)a.rows * 4u;
-  const size_t sm1 = tk_smem_bytes((int)p.chunk);
+  size_t sm = tk_smem_bytes((int)p.chunk);
+  const size_t sm_merge = (size_t)(p.nchunks + 1) * TK * sizeof(unsigned long long);
+  if (p.nchunks > 1 && sm_merge > sm) sm = sm_merge;
   hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm1);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const int mode = p.nchunks == 1 ? 0 : 1;
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(units, (unsigned)p.nchunks), dim3(TK_THREADS), sm1,
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3(units, (unsigned)p.nchunks), dim3(TK_THREADS), sm,
                      stream, mode, a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit,
                      a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks,
-                     a.partial, a.sel_ids, a.sel_scores);
-  e = hipGetLastError();
-  if (e != hipSuccess || p.nchunks == 1) return e;
-  const size_t sm2 = (size_t)(p.nchunks + 1) * TK * sizeof(unsigned long long);
-  e = hipFuncSetAttribute((const void*)topk_merge_kernel,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm2);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_merge_kernel, dim3(units), dim3(TK_THREADS), sm2, stream, a.R_cap,
-                     a.row_seq, a.row_pos, a.B, a.pos_limit, p.nchunks,
-                     (const unsigned long long*)a.partial, a.sel_ids, a.sel_scores);
+                     a.partial, a.arrivals, a.sel_ids, a.sel_scores);
   return hipGetLastError();
 }
 

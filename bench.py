@@ -1,19 +1,23 @@
 """Benchmark of the Step-5 sparse-indexer hot path on one MI355X.
 
-A step is one decode pass of the whole path over a batch of rows, with every
-input resident in HBM (each call captured once as a HIP graph and replayed,
-so the step measures the GPU and not the Python launch path):
-  1. step5_index_summarize   the region each row just completed (k prep +
-                             summary, steps a2/a3)
+A step is one pass of the whole path over a batch of rows, with every input
+resident in HBM (each call captured once as a HIP graph and replayed, so the
+step measures the GPU and not the Python launch path; the whole step is one
+graph, launched once per step):
+  1. step5_index_summarize   the regions the step completes (k prep + summary)
   2. step5_index_score_topk  q prep, scores over all candidates, top 512 per
-                             KV group (steps a1/a4/a5)
-  3. step5_sparse_attn       attention over the picks plus the own region (a6)
-The cache summaries of the whole context are built once before timing (one
-step5_index_summarize over every token, itself timed and reported as the
+                             KV group
+  3. step5_sparse_attn       attention over the picks plus the own region
+The summaries of the context before the step are built once before timing
+(one step5_index_summarize over every token, itself timed and reported as the
 summary phase).
 
-Default workload: decode16_ctx128k (16 rows, each with its own 131,072-token
-context, Student-t inputs). One JSON line goes to stdout.
+Headline workload: decode16_ctx128k (16 decode rows, each with its own
+131,072-token context, Student-t inputs) -> decode rows/s. Also reported
+(see --extra): a 2,048-row chunked prefill at 32K (prefill tokens/s),
+one decode row at a 1M-token context with a summary pass over a fresh
+65,536-token span, and a plain device copy as the measured HBM ceiling. One
+JSON line goes to stdout.
 """
 from __future__ import annotations
 
@@ -28,7 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"
+HEADLINE = "decode16_ctx128k"
 
 
 def parse():
@@ -36,12 +43,242 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="decode16_ctx128k")
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2)
+    ap.add_argument("--cpu-rows", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle's sample until this much time has passed")
+    ap.add_argument("--extra", default="prefill2048_ctx32k,decode1_ctx1m,hbm_copy",
+                    help="comma-separated extra lines to measure after the headline "
+                         "(workload names and/or hbm_copy; 'none' for none)")
     ap.add_argument("--eager", action="store_true", help="launch the calls directly, no HIP graphs")
     return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Times a step made of several calls on the stream the calls run on.
+
+    step(): the whole step captured as ONE HIP graph (unless eager) and
+    replayed once per step, with a HIP event before every replay.
+    per_call(): each call captured `reps` times back to back in its own graph,
+    replayed a few times; per-call time = event-timed replay / reps (what the
+    call's kernels take, without the launch gap of a graph replay)."""
+
+    def __init__(self, torch, calls, warmup, eager):
+        self.torch = torch
+        self.calls = calls
+        self.eager = eager
+        self.stream = torch.cuda.current_stream()
+        for _ in range(warmup):
+            for _, f in calls:
+                f()
+        torch.cuda.synchronize()
+        if eager:
+            self.step_fn = lambda: [f() for _, f in calls]
+        else:
+            self.g_step = self._capture([f for _, f in calls], 1)
+            self.step_fn = self.g_step.replay
+        for _ in range(warmup):
+            self.step_fn()
+        torch.cuda.synchronize()
+
+    def _capture(self, fns, reps):
+        g = self.torch.cuda.CUDAGraph()
+        with self.torch.cuda.graph(g):
+            for _ in range(reps):
+                for f in fns:
+                    f()
+        return g
+
+    def step(self, steps):
+        torch = self.torch
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            evs[i].record(self.stream)
+            self.step_fn()
+        evs[steps].record(self.stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        gpu_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+        return elapsed, sum(gpu_ms) / steps
+
+    def per_call(self, reps=20, rounds=5):
+        torch = self.torch
+        out = {}
+        for name, f in self.calls:
+            if self.eager:
+                run = lambda: [f() for _ in range(reps)]
+            else:
+                g = self._capture([f], reps)
+                run = g.replay
+            run()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            for _ in range(rounds):
+                run()
+            e1.record(self.stream)
+            torch.cuda.synchronize()
+            out[name] = e0.elapsed_time(e1) * 1000.0 / (rounds * reps)
+        return out
+
+
+def event_time_us(torch, fn, reps):
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1000.0 / reps
+
+
+def workspaces(torch, s5, rows, R_cap, dev):
+    ws1 = torch.empty(s5.step5_index_score_topk_workspace(rows, R_cap) + 256, dtype=torch.uint8,
+                      device=dev)
+    ws2 = torch.empty(max(1, s5.step5_sparse_attn_workspace(rows)) + 256, dtype=torch.uint8,
+                      device=dev)
+    return ws1[(-ws1.data_ptr()) % 256:], ws2[(-ws2.data_ptr()) % 256:]
+
+
+def attn_bytes(rows_pos):
+    """Algorithmic K+V bytes of one sparse-attention launch: per (row, KV head),
+    the 8 tokens of every selected region plus the own region's p%8+1 tokens,
+    256 bytes each for K and for V."""
+    tot = 0
+    for p in rows_pos:
+        nsel = min(512, p // 8)
+        tot += 4 * (8 * nsel + p % 8 + 1) * 256 * 2
+    return tot
+
+
+def run_workload(name, args, torch, s5, W):
+    """Builds the inputs, the summaries before the step, and times the step.
+    Returns (result dict, inputs dict, summaries) for the caller."""
+    wl = W.WORKLOADS[name]
+    dev = "cuda"
+    log(f"{name}: generating inputs")
+    d = W.make_case(wl, args.seed, dev)
+    rows, T, B = d["rows"], d["cache_tokens"], d["batch"]
+    R_cap = T // 8
+    eps = W.NORM_EPS
+    scale = 1.0 / math.sqrt(W.HEAD_DIM)
+    pos = [int(x) for x in d["row_pos"].cpu()]
+    res = {"workload": name, "rows": rows, "context_tokens": T, "sequences": B}
+
+    # ---- summaries before the step (and the summary-phase measurement)
+    if wl.tie_heavy:
+        S = d["summary"]
+        S_fresh = torch.zeros((1, wl.fresh_tokens // 8, 4, 64), dtype=torch.uint8, device=dev)
+        full_pass = lambda: s5.step5_index_summarize(d["fresh_k"], d["fresh_z"], 0, d["ln_w"],
+                                                     d["ln_b"], eps, d["rope"], S_fresh)
+        pass_tokens = wl.fresh_tokens
+        pass_name = f"fresh span of {wl.fresh_tokens} tokens"
+    else:
+        S = torch.zeros((B, R_cap, 4, 64), dtype=torch.uint8, device=dev)
+        prefix = T - wl.prefill_chunk if wl.prefill_chunk else T
+        kp, zp = d["k_idx"][:, :prefix], d["z_idx"][:, :prefix]
+        full_pass = lambda: s5.step5_index_summarize(kp, zp, 0, d["ln_w"], d["ln_b"], eps,
+                                                     d["rope"], S)
+        pass_tokens = B * prefix
+        pass_name = f"{B} x {prefix} tokens"
+    log(f"{name}: summary pass over {pass_name}")
+    summ_us = event_time_us(torch, full_pass, 5)
+    summ_bytes = pass_tokens * 1024 + (pass_tokens // 8) * 256
+    res["summary_pass"] = {"span": pass_name, "us": round(summ_us, 1),
+                           "GBs": round(summ_bytes / summ_us / 1e3, 1),
+                           "frac_hbm": round(summ_bytes / summ_us / 1e3 / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes": summ_bytes}
+
+    # ---- the step
+    ids = torch.empty((rows, 4, 512), dtype=torch.int32, device=dev)
+    out = torch.empty((rows, 16, 128), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((rows, 16), dtype=torch.float32, device=dev)
+    ws1, ws2 = workspaces(torch, s5, rows, R_cap, dev)
+    calls = []
+    summ_step_tokens = 0
+    if wl.prefill_chunk:
+        t0 = T - wl.prefill_chunk
+        kc_, zc_ = d["k_idx"][:, t0:], d["z_idx"][:, t0:]
+        summ_step_tokens = wl.prefill_chunk
+        calls.append(("summarize", lambda: s5.step5_index_summarize(
+            kc_, zc_, t0, d["ln_w"], d["ln_b"], eps, d["rope"], S)))
+    elif not wl.tie_heavy:
+        own0 = (T - 1) // 8 * 8
+        if T - own0 == 8:
+            ko, zo = d["k_idx"][:, own0:own0 + 8], d["z_idx"][:, own0:own0 + 8]
+            summ_step_tokens = 8 * B
+            calls.append(("summarize", lambda: s5.step5_index_summarize(
+                ko, zo, own0, d["ln_w"], d["ln_b"], eps, d["rope"], S)))
+    if wl.tie_heavy:
+        calls.append(("score_topk", lambda: s5.step5_index_score_topk(
+            d["q8"], d["w_head"], d["row_seq"], d["row_pos"], S, ids, q_is_e4m3=True,
+            workspace=ws1)))
+    else:
+        calls.append(("score_topk", lambda: s5.step5_index_score_topk(
+            d["q_idx"], d["w_head"], d["row_seq"], d["row_pos"], S, ids, q_norm_w=d["q_norm_w"],
+            q_eps=eps, rope=d["rope"], workspace=ws1)))
+    calls.append(("sparse_attn", lambda: s5.step5_sparse_attn(
+        d["q"], d["k_cache"], d["v_cache"], ids, d["row_seq"], d["row_pos"], scale, out, lse,
+        workspace=ws2)))
+    steps = args.steps if name == HEADLINE else max(5, min(args.steps, 20))
+    log(f"{name}: timing {steps} steps")
+    timer = Timer(torch, calls, args.warmup, args.eager)
+    elapsed, gpu_step_ms = timer.step(steps)
+    log(f"{name}: per-call times")
+    per_call = timer.per_call()
+    del timer
+    ms_per_step = elapsed * 1000.0 / steps
+
+    a_bytes = attn_bytes(pos)
+    sc_bytes = sum(p // 8 for p in pos) * 256
+    sc_flops = sum(p // 8 for p in pos) * 16 * 64 * 2
+    res.update({
+        "steps": steps,
+        "ms_per_step": round(ms_per_step, 4),
+        "gpu_ms_per_step": round(gpu_step_ms, 4),
+        "rows_per_s": round(rows * steps / elapsed, 1),
+        "call_us": {k: round(v, 2) for k, v in per_call.items()},
+        "sparse_attn": {"algorithmic_bytes": a_bytes,
+                        "GBs": round(a_bytes / per_call["sparse_attn"] / 1e3, 1),
+                        "frac_hbm": round(a_bytes / per_call["sparse_attn"] / 1e3 / HBM_PEAK_GBS, 4)},
+        "score_topk": {"summary_bytes": sc_bytes, "score_flops": sc_flops,
+                       "GBs": round(sc_bytes / per_call["score_topk"] / 1e3, 1),
+                       "frac_hbm": round(sc_bytes / per_call["score_topk"] / 1e3 / HBM_PEAK_GBS, 4),
+                       "TFLOPs": round(sc_flops / per_call["score_topk"] / 1e6, 2),
+                       "frac_fp8_mfma": round(sc_flops / per_call["score_topk"] / 1e6 / FP8_PEAK_TFLOPS, 5),
+                       "frac_bf16_mfma": round(sc_flops / per_call["score_topk"] / 1e6 / BF16_PEAK_TFLOPS, 5)},
+    })
+    if "summarize" in per_call:
+        b = summ_step_tokens * 1024 + (summ_step_tokens // 8) * 256
+        res["summarize_in_step"] = {"tokens": summ_step_tokens, "algorithmic_bytes": b,
+                                    "GBs": round(b / per_call["summarize"] / 1e3, 1)}
+    if wl.prefill_chunk:
+        res["prefill_tokens_per_s"] = round(wl.prefill_chunk * steps / elapsed, 1)
+    return res, d, S
+
+
+def copy_ceiling(torch):
+    """A plain device-to-device copy of 1 GiB: the HBM rate a streaming kernel
+    reaches on this GPU (read + write bytes per second)."""
+    n = 1 << 28
+    x = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    us = event_time_us(torch, lambda: y.copy_(x), 10)
+    gbs = 2 * 4 * n / us / 1e3
+    del x, y
+    return {"bytes_per_copy": 2 * 4 * n, "us": round(us, 1), "GBs": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -54,176 +291,64 @@ def main():
     import long_context_sparse_indexer_amd as s5
     import workloads as W
 
-    wl = W.WORKLOADS[args.workload]
-    dev = "cuda"
     torch.cuda.init()
-    d = W.make_case(wl, args.seed, dev)
-    rows, T, B = d["rows"], d["cache_tokens"], d["batch"]
-    R_cap = T // 8
-    eps = W.NORM_EPS
-    scale = 1.0 / math.sqrt(W.HEAD_DIM)
-    stream = torch.cuda.current_stream()
+    head, d, S = run_workload(args.workload, args, torch, s5, W)
+    wl = W.WORKLOADS[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("oracle baseline on the host")
+        cpu = cpu_baseline(d, wl, args.cpu_rows, args.cpu_seconds, torch)
+    del d, S
+    torch.cuda.empty_cache()
 
-    # ---- one-time: summaries of the whole cache (also the summary-phase measurement)
-    if wl.tie_heavy:
-        S = d["summary"]
-        sum_k, sum_z, sum_t0 = d["fresh_k"], d["fresh_z"], 0
-        S_fresh = torch.zeros((1, wl.fresh_tokens // 8, 4, 64), dtype=torch.uint8, device=dev)
-        full_pass = lambda: s5.step5_index_summarize(sum_k, sum_z, 0, d["ln_w"], d["ln_b"], eps,
-                                                     d["rope"], S_fresh)
-        full_tokens = wl.fresh_tokens
-    else:
-        S = torch.zeros((B, R_cap, 4, 64), dtype=torch.uint8, device=dev)
-        full_pass = lambda: s5.step5_index_summarize(d["k_idx"], d["z_idx"], 0, d["ln_w"],
-                                                     d["ln_b"], eps, d["rope"], S)
-        full_tokens = B * T
-    full_pass()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 5
-    ev0.record(stream)
-    for _ in range(reps):
-        full_pass()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    summ_us = ev0.elapsed_time(ev1) * 1000.0 / reps
-    summ_bytes = full_tokens * 1024 + (full_tokens // 8) * 256
-    summ_gbs = summ_bytes / summ_us / 1e3
+    extra = {}
+    for name in [x for x in args.extra.split(",") if x and x != "none"]:
+        if name == "hbm_copy":
+            log("plain copy of 1 GiB")
+            extra[name] = copy_ceiling(torch)
+        elif name != args.workload:
+            r, dd, SS = run_workload(name, args, torch, s5, W)
+            del dd, SS
+            torch.cuda.empty_cache()
+            extra[name] = r
 
-    # ---- the decode step
-    p_last = T - 1
-    own0 = (p_last // 8) * 8
-    own_T = p_last + 1 - own0          # tokens of the own region present (8 at these workloads)
-    ids = torch.empty((rows, 4, 512), dtype=torch.int32, device=dev)
-    out = torch.empty((rows, 16, 128), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((rows, 16), dtype=torch.float32, device=dev)
-    ws1 = torch.empty(s5.step5_index_score_topk_workspace(rows, R_cap) + 256, dtype=torch.uint8,
-                      device=dev)
-    ws2 = torch.empty(max(1, s5.step5_sparse_attn_workspace(rows)) + 256, dtype=torch.uint8,
-                      device=dev)
-    ws1 = ws1[(-ws1.data_ptr()) % 256:]
-    ws2 = ws2[(-ws2.data_ptr()) % 256:]
-    if not wl.tie_heavy and own_T == 8 and not wl.prefill_chunk:
-        k_own = d["k_idx"][:, own0:own0 + 8]
-        z_own = d["z_idx"][:, own0:own0 + 8]
-    else:
-        k_own = z_own = None
-
-    def call_summarize():
-        if k_own is not None:
-            s5.step5_index_summarize(k_own, z_own, own0, d["ln_w"], d["ln_b"], eps, d["rope"], S)
-
-    def call_score():
-        if wl.tie_heavy:
-            s5.step5_index_score_topk(d["q8"], d["w_head"], d["row_seq"], d["row_pos"], S, ids,
-                                      q_is_e4m3=True, workspace=ws1)
-        else:
-            s5.step5_index_score_topk(d["q_idx"], d["w_head"], d["row_seq"], d["row_pos"], S, ids,
-                                      q_norm_w=d["q_norm_w"], q_eps=eps, rope=d["rope"],
-                                      workspace=ws1)
-
-    def call_attn():
-        s5.step5_sparse_attn(d["q"], d["k_cache"], d["v_cache"], ids, d["row_seq"], d["row_pos"],
-                             scale, out, lse, workspace=ws2)
-
-    def call_indexer():
-        # own-region summary (feeds the next step), then this step's selection
-        call_summarize()
-        call_score()
-
-    calls = [("indexer", call_indexer), ("sparse_attn", call_attn)]
-    for _ in range(args.warmup):
-        for _, f in calls:
-            f()
-    torch.cuda.synchronize()
-    runners = dict(calls)
-    if not args.eager:
-        graphs = {}
-        for name, f in calls:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                f()
-            graphs[name] = g
-        runners = {name: g.replay for name, g in graphs.items()}
-        for _ in range(args.warmup):
-            for name, _ in calls:
-                runners[name]()
-        torch.cuda.synchronize()
-    nev = args.steps
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev * (len(calls) + 1))]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        base = i * (len(calls) + 1)
-        evs[base].record(stream)
-        for c, (name, _) in enumerate(calls):
-            runners[name]()
-            evs[base + c + 1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    per_call = {}
-    for c, (name, _) in enumerate(calls):
-        tot = 0.0
-        for i in range(nev):
-            base = i * (len(calls) + 1)
-            tot += evs[base + c].elapsed_time(evs[base + c + 1])
-        per_call[name] = tot * 1000.0 / nev
-    ms_per_step = elapsed * 1000.0 / args.steps
-    rows_per_s = rows * args.steps / elapsed
-
-    # algorithmic bytes per launch
-    nsel = min(512, p_last // 8)
-    tok_per_unit = 8 * nsel + (p_last % 8) + 1
-    attn_bytes = rows * 4 * tok_per_unit * 128 * 2 * 2
-    score_bytes = rows * (p_last // 8) * 256
-    own_bytes = (B * 8 * 1024 + B * 256) if k_own is not None else 0
-    attn_gbs = attn_bytes / per_call["sparse_attn"] / 1e3
-    score_gbs = score_bytes / per_call["indexer"] / 1e3
-
+    sa = head["sparse_attn"]
     result = {
         "metric": METRIC,
-        "value": round(rows_per_s, 1),
+        "value": head["rows_per_s"],
         "unit": "rows/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": head["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "rows": rows, "context_tokens": T, "sequences": B,
-                   "topk": 512, "region": 8, "idx_heads": 16, "kv_groups": 4, "q_heads": 16,
-                   "head_dim": 128, "inputs": wl.dist},
-        "roofline": {"bound": "hbm", "kernel": "step5_sparse_attn (attn_kernel + attn_merge_kernel)",
-                     "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": attn_bytes},
-        "phases": {
-            "graph_replay": not args.eager,
-            "indexer_us": round(per_call["indexer"], 2),
-            "sparse_attn_us": round(per_call["sparse_attn"], 2),
-            "score_stream_GBs": round(score_gbs, 1),
-            "score_stream_frac_hbm": round(score_gbs / HBM_PEAK_GBS, 4),
-            "own_region_bytes": own_bytes,
-            "summary_pass": {"tokens": full_tokens, "us": round(summ_us, 1),
-                             "GBs": round(summ_gbs, 1),
-                             "frac_hbm": round(summ_gbs / HBM_PEAK_GBS, 4),
-                             "algorithmic_bytes": summ_bytes},
-        },
+        "config": {"workload": wl.name, "rows": head["rows"], "context_tokens": head["context_tokens"],
+                   "sequences": head["sequences"], "topk": 512, "region": 8, "idx_heads": 16,
+                   "kv_groups": 4, "q_heads": 16, "head_dim": 128, "inputs": wl.dist},
+        "roofline": {"bound": "hbm", "kernel": "step5_sparse_attn (attn_kernel)",
+                     "achieved": sa["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": sa["frac_hbm"], "traffic": None,
+                     "algorithmic_bytes_per_launch": sa["algorithmic_bytes"]},
+        "phases": {"graph_replay": not args.eager, **{k: v for k, v in head.items()
+                                                      if k not in ("workload",)}},
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(d, wl, S, args.cpu_rows, torch)
+    if extra:
+        result["extra"] = extra
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(d, wl, S_gpu, nrows, torch):
+def cpu_baseline(d, wl, nrows, seconds, torch):
     """The oracle (unchanged) on a bounded sample of the same decode step: the
-    first `nrows` rows, each over its own sequence. The oracle builds its own
-    summaries of those sequences first (untimed, like the GPU's cache); then the
-    timed part is the same step: own-region summary, q prep, scores, top-512
-    selection and attention."""
+    first `nrows` rows, each over its own sequence, repeated until `seconds`
+    have passed. The oracle builds its own summaries of those sequences first
+    (untimed, like the GPU's cache); the timed part is the step: own-region
+    summary, q prep, scores, top-512 selection and attention."""
     import numpy as np
     from oracle import oracle as orc
     import workloads as W
@@ -247,22 +372,33 @@ def cpu_baseline(d, wl, S_gpu, nrows, torch):
     seq = np.array([smap[int(d["row_seq"][r])] for r in rows], np.int32)
     w = d["w_head"].cpu().numpy()
     q = W.bits16(d["q"])[rows]
+    own0 = (T - 1) // 8 * 8
+
+    def one_step():
+        if not wl.tie_heavy:
+            orc.summarize(k16[:, own0:own0 + 8], z16[:, own0:own0 + 8], own0, lnw, lnb,
+                          W.NORM_EPS, rope, R_cap=Sh.shape[1], summary=Sh, nthreads=nth)
+            q8 = orc.q_prep(W.bits16(d["q_idx"])[rows], d["q_norm_w"].cpu().numpy(), W.NORM_EPS,
+                            rope, pos, nthreads=nth)
+        else:
+            q8 = W.bits8(d["q8"])[rows]
+        sc = orc.score(q8, w, seq, pos, Sh, nthreads=nth)
+        ids, _ = orc.select(sc, pos, 512, nthreads=nth)
+        orc.attend(q, kc, vc, ids, seq, pos, 1.0 / math.sqrt(W.HEAD_DIM), nthreads=nth)
+
+    reps = 0
     t0 = time.perf_counter()
-    if not wl.tie_heavy:
-        own0 = (T - 1) // 8 * 8
-        orc.summarize(k16[:, own0:own0 + 8], z16[:, own0:own0 + 8], own0, lnw, lnb, W.NORM_EPS,
-                      rope, R_cap=Sh.shape[1], summary=Sh, nthreads=nth)
-        q8 = orc.q_prep(W.bits16(d["q_idx"])[rows], d["q_norm_w"].cpu().numpy(), W.NORM_EPS, rope,
-                        pos, nthreads=nth)
-    else:
-        q8 = W.bits8(d["q8"])[rows]
-    sc = orc.score(q8, w, seq, pos, Sh, nthreads=nth)
-    ids, _ = orc.select(sc, pos, 512, nthreads=nth)
-    orc.attend(q, kc, vc, ids, seq, pos, 1.0 / math.sqrt(W.HEAD_DIM), nthreads=nth)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(rows) / dt, 3), "unit": "rows/s", "cores": nth, "kind": "oracle",
-            "sample": f"{len(rows)} of {d['rows']} rows of {wl.name} (own-region summary, q prep, "
-                      f"scores, top-512, attention); {dt:.2f} s"}
+    while True:
+        one_step()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": round(len(rows) * reps / dt, 3), "unit": "rows/s", "cores": nth,
+            "kind": "oracle",
+            "sample": f"rows 0..{len(rows) - 1} of {wl.name} ({len(rows)} of {d['rows']} rows, "
+                      f"each its own {T}-token sequence): own-region summary, q prep, scores, "
+                      f"top-512, attention; repeated {reps} times in {dt:.1f} s"}
 
 
 if __name__ == "__main__":

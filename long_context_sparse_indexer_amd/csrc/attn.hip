@@ -42,6 +42,113 @@ __device__ inline f32x4 mfma_bf16(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// One 32-token chunk of a wave's list: K/V registers and the token counts of
+// its four entries (8, the own region's p%8+1, or 0 for an empty slot).
+struct AtChunk {
+  uint4 k[2][4];
+  uint4 v[8];
+  bool kok[2];  // this lane's key token 16*st + n is present
+};
+
+// the i-th of four wave-uniform values, for a lane-dependent i
+template <typename T>
+__device__ inline T pick4(int i, T a, T b, T c, T d) {
+  return i < 2 ? (i == 0 ? a : b) : (i == 2 ? c : d);
+}
+
+// Issues the loads of chunk `i` of this wave; entry e4 of the chunk is
+// described by lane 4i+e4 of (lj, lcnt). Lanes whose token is absent load the
+// row's own token (always in range) and are masked later.
+__device__ __attribute__((always_inline)) inline void at_fetch(AtChunk& c, int i, int64_t lj, int lcnt, const uint16_t* kb,
+                                const uint16_t* vb, int64_t kv_st, int64_t pc, int n, int qd) {
+  int64_t jr[4];
+  int cnt[4];
+#pragma unroll
+  for (int e4 = 0; e4 < 4; ++e4) {
+    const int src = 4 * i + e4;
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)lj, src);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(lj >> 32), src);
+    jr[e4] = (int64_t)(((uint64_t)hi << 32) | lo);
+    cnt[e4] = __builtin_amdgcn_readlane(lcnt, src);
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int e4 = 2 * st + (n >> 3), ti = n & 7;
+    const int ce = pick4(e4, cnt[0], cnt[1], cnt[2], cnt[3]);
+    const int64_t je = pick4(e4, jr[0], jr[1], jr[2], jr[3]);
+    c.kok[st] = ti < ce;
+    const int64_t tok = c.kok[st] ? 8 * je + ti : pc;
+    const uint16_t* kp = kb + tok * kv_st + 32 * qd;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c.k[st][u] = ldg16(kp + 8 * u);
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int e4 = k >> 1, ti = 4 * (k & 1) + qd;  // e4 is the same in every lane
+    const int64_t tok = (ti < cnt[e4]) ? 8 * jr[e4] + ti : pc;
+    c.v[k] = ldg16(vb + tok * kv_st + 8 * n);
+  }
+}
+
+struct AtState {
+  float m[4], l[4], o[4][8];
+};
+
+// QK^T, online softmax and PV for one chunk.
+__device__ __attribute__((always_inline)) inline void at_consume(const AtChunk& c, AtState& s, const uint4 (&qa)[4],
+                                  float scale_log2, float4 (*p_w)[32], int n, int qd) {
+  f32x4 acc[2];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    acc[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[st] = mfma_bf16(qa[u], c.k[st][u], acc[st]);
+  }
+  // lanes 0..15: acc[st][r] = score of head r with token 16*st + n
+  float sv[2][4];
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[st][r] = c.kok[st] ? acc[st][r] * scale_log2 : -INFINITY;
+  }
+  float alpha[4], pv[2][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float cmax = wave_uniform(max16_lanes(fmaxf(sv[0][r], sv[1][r])));
+    const float mnew = fmaxf(s.m[r], cmax);
+    const float mu = (mnew == -INFINITY) ? 0.f : mnew;
+    alpha[r] = __builtin_amdgcn_exp2f(s.m[r] - mu);
+    pv[0][r] = __builtin_amdgcn_exp2f(sv[0][r] - mu);
+    pv[1][r] = __builtin_amdgcn_exp2f(sv[1][r] - mu);
+    const float psum = wave_uniform(sum16_lanes(pv[0][r] + pv[1][r]));
+    s.l[r] = s.l[r] * alpha[r] + psum;
+    s.m[r] = mnew;
+  }
+  if (qd == 0) {
+    (*p_w)[n] = make_float4(pv[0][0], pv[0][1], pv[0][2], pv[0][3]);
+    (*p_w)[16 + n] = make_float4(pv[1][0], pv[1][1], pv[1][2], pv[1][3]);
+  }
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s.o[r][i] *= alpha[r];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 pw = (*p_w)[4 * k + qd];
+    float vf[8];
+    unpack_bf16x8(c.v[k], vf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      s.o[0][i] = fmaf(pw.x, vf[i], s.o[0][i]);
+      s.o[1][i] = fmaf(pw.y, vf[i], s.o[1][i]);
+      s.o[2][i] = fmaf(pw.z, vf[i], s.o[2][i]);
+      s.o[3][i] = fmaf(pw.w, vf[i], s.o[3][i]);
+    }
+  }
+  wave_lds_sync();
+}
+
 __global__ __launch_bounds__(256) void attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t B, int64_t kv_sb, int64_t kv_st, int64_t T_cap,
@@ -67,6 +174,32 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int e0 = split * per_split;
   const int e1 = min(e0 + per_split, nent);
 
+  // this wave's entries: wb + 16 i + e4 (i < niter, e4 < 4); lane 4(i%16) + e4
+  // describes one of them, the table reloaded every 16 chunks
+  const int wb = e0 + 4 * wave;
+  const int niter = wb < e1 ? (e1 - wb + 15) >> 4 : 0;
+  const int32_t* sl = sel + unit * 512;
+  int64_t lj;
+  int lcnt;
+  auto load_table = [&](int ibase) {
+    const int e = wb + 16 * (ibase + (lane >> 2)) + (lane & 3);
+    lj = 0;
+    lcnt = 0;
+    if (e < e1) {
+      if (e == 0) {
+        lj = p >> 3;
+        lcnt = (int)(p & 7) + 1;
+      } else {
+        const int32_t j = sl[e - 1];
+        if (j >= 0 && j < ncand) {
+          lj = j;
+          lcnt = 8;
+        }
+      }
+    }
+  };
+  load_table(0);
+
   uint4 qa[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) qa[i] = make_uint4(0, 0, 0, 0);
@@ -78,123 +211,49 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int64_t sb = valid ? (int64_t)seq * kv_sb : 0;
   const uint16_t* kb = kc + sb + g * 128;
   const uint16_t* vb = vc + sb + g * 128;
-  const int32_t* sl = sel + unit * 512;
   const int64_t pc = valid ? p : 0;  // a token that is always in range
 
-  float m_run[4], l_run[4], o[4][8];
+  AtState s;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
+    s.m[r] = -INFINITY;
+    s.l[r] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[r][i] = 0.f;
+    for (int i = 0; i < 8; ++i) s.o[r][i] = 0.f;
   }
+  float4 (*p_w)[32] = &p_lds[wave];
 
-  for (int ec = e0 + wave * 4; ec < e1; ec += 16) {
-    int64_t jr[4];
-    int cnt[4];
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int e = ec + e4;
-      jr[e4] = 0;
-      cnt[e4] = 0;
-      if (e < e1) {
-        if (e == 0) {
-          jr[e4] = p >> 3;
-          cnt[e4] = (int)(p & 7) + 1;
-        } else {
-          const int32_t j = sl[e - 1];
-          if (j >= 0 && j < ncand) {
-            jr[e4] = j;
-            cnt[e4] = 8;
-          }
-        }
-      }
+  // two chunks in flight: the loads of chunk i+1 are issued before chunk i is
+  // consumed
+  AtChunk ca, cb;
+  if (niter > 0) at_fetch(ca, 0, lj, lcnt, kb, vb, kv_st, pc, n, qd);
+  for (int i = 0; i < niter; i += 2) {
+    if (i + 1 < niter) {
+      if (((i + 1) & 15) == 0) load_table(i + 1);
+      at_fetch(cb, (i + 1) & 15, lj, lcnt, kb, vb, kv_st, pc, n, qd);
     }
-    uint4 kr[2][4], vr[8];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int tt = 16 * st + n;
-      const int e4 = tt >> 3, ti = tt & 7;
-      const int64_t tok = (ti < cnt[e4]) ? 8 * jr[e4] + ti : pc;
-      const uint16_t* kp = kb + tok * kv_st + 32 * qd;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kr[st][i] = ldg16(kp + 8 * i);
+    at_consume(ca, s, qa, scale_log2, p_w, n, qd);
+    if (i + 1 >= niter) break;
+    if (i + 2 < niter) {
+      if (((i + 2) & 15) == 0) load_table(i + 2);
+      at_fetch(ca, (i + 2) & 15, lj, lcnt, kb, vb, kv_st, pc, n, qd);
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int e4 = k >> 1, ti = 4 * (k & 1) + qd;
-      const int64_t tok = (ti < cnt[e4]) ? 8 * jr[e4] + ti : pc;
-      vr[k] = ldg16(vb + tok * kv_st + 8 * n);
-    }
-
-    f32x4 acc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      acc[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[st] = mfma_bf16(qa[i], kr[st][i], acc[st]);
-    }
-    // lanes 0..15: acc[st][r] = score of head r with token 16*st + n
-    float sv[2][4];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int tt = 16 * st + n;
-      const bool ok = (tt & 7) < cnt[tt >> 3];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[st][r] = ok ? acc[st][r] * scale_log2 : -INFINITY;
-    }
-    float alpha[4], pv[2][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float cmax = wave_uniform(max16_lanes(fmaxf(sv[0][r], sv[1][r])));
-      const float mnew = fmaxf(m_run[r], cmax);
-      const float mu = (mnew == -INFINITY) ? 0.f : mnew;
-      alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - mu);
-      pv[0][r] = __builtin_amdgcn_exp2f(sv[0][r] - mu);
-      pv[1][r] = __builtin_amdgcn_exp2f(sv[1][r] - mu);
-      const float psum = wave_uniform(sum16_lanes(pv[0][r] + pv[1][r]));
-      l_run[r] = l_run[r] * alpha[r] + psum;
-      m_run[r] = mnew;
-    }
-    if (qd == 0) {
-      p_lds[wave][n] = make_float4(pv[0][0], pv[0][1], pv[0][2], pv[0][3]);
-      p_lds[wave][16 + n] = make_float4(pv[1][0], pv[1][1], pv[1][2], pv[1][3]);
-    }
-    wave_lds_sync();
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[r][i] *= alpha[r];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 pw = p_lds[wave][4 * k + qd];
-      float vf[8];
-      unpack_bf16x8(vr[k], vf);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        o[0][i] = fmaf(pw.x, vf[i], o[0][i]);
-        o[1][i] = fmaf(pw.y, vf[i], o[1][i]);
-        o[2][i] = fmaf(pw.z, vf[i], o[2][i]);
-        o[3][i] = fmaf(pw.w, vf[i], o[3][i]);
-      }
-    }
-    wave_lds_sync();
+    at_consume(cb, s, qa, scale_log2, p_w, n, qd);
   }
 
   // ---- merge the four waves (fixed order)
   if (lane == 0) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      ml_lds[wave][0][r] = m_run[r];
-      ml_lds[wave][1][r] = l_run[r];
+      ml_lds[wave][0][r] = s.m[r];
+      ml_lds[wave][1][r] = s.l[r];
     }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float4* dst = reinterpret_cast<float4*>(&o_lds[wave][qd][r][8 * n]);
-    dst[0] = make_float4(o[r][0], o[r][1], o[r][2], o[r][3]);
-    dst[1] = make_float4(o[r][4], o[r][5], o[r][6], o[r][7]);
+    dst[0] = make_float4(s.o[r][0], s.o[r][1], s.o[r][2], s.o[r][3]);
+    dst[1] = make_float4(s.o[r][4], s.o[r][5], s.o[r][6], s.o[r][7]);
   }
   __syncthreads();
   const int r = threadIdx.x >> 6;
@@ -202,7 +261,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, ml_lds[w][0][r]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float Mu = (M == -INFINITY) ? 0.f : M;
   float L = 0.f, O0 = 0.f, O1 = 0.f;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -214,65 +273,53 @@ __global__ __launch_bounds__(256) void attn_kernel(
     O0 = O0 + f * s0;
     O1 = O1 + f * s1;
   }
-  if (nsplit == 1) {
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    const uint32_t packed = bf16_bits(O0 * inv) | (bf16_bits(O1 * inv) << 16);
-    *reinterpret_cast<uint32_t*>(out + (row * 16 + 4 * g + r) * 128 + d0) = packed;
-    if (lse && d0 == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
-  } else {
+  if (nsplit > 1) {
     float* dst = partial + ((unit * nsplit + split) * 4 + r) * AT_PART;
     if (d0 == 0) {
       dst[0] = M;
       dst[1] = L;
     }
-    dst[2 + d0] = O0;
-    dst[3 + d0] = O1;
+    *reinterpret_cast<float2*>(dst + 2 + d0) = make_float2(O0, O1);
+    return;
   }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const uint32_t packed = bf16_bits(O0 * inv) | (bf16_bits(O1 * inv) << 16);
+  *reinterpret_cast<uint32_t*>(out + (row * 16 + 4 * g + r) * 128 + d0) = packed;
+  if (lse && d0 == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
-// Merge of a unit's split states, in split order. Wave r handles head r:
-// lane s reads split s's (m, l) (64 splits at most), the wave reduces max and
-// weighted sum, and the weights go through LDS to the o pass, where lane d
-// accumulates dims 2d, 2d+1 over the splits in order with loads kept in flight.
+// Merge of a unit's split states, in split order. The block first copies the
+// unit's states into LDS with all loads in flight at once (splits hold at
+// least 16 entries, so there are at most ceil(513 / 16) = 33 of them), then wave r merges head r: the max of the splits' m, and
+// lane d accumulates dims 2d, 2d+1 and the weighted l over the splits in order.
+constexpr int AT_MERGE_MAX = (AT_ENTRIES + 15) / 16;
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ partial,
                                                          int nsplit, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse) {
-  __shared__ float f_lds[4][64];
+  __shared__ float4 st_lds[AT_MERGE_MAX * 4 * AT_PART / 4];
   const int64_t unit = blockIdx.x;
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
   const int r = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int d0 = 2 * lane;
-  const float* base = partial + (unit * nsplit * 4 + r) * AT_PART;  // split s at + s*4*AT_PART
-  const bool have = lane < nsplit;
-  const float ms = have ? base[(int64_t)lane * 4 * AT_PART] : -INFINITY;
-  const float ls = have ? base[(int64_t)lane * 4 * AT_PART + 1] : 0.f;
-  float M = ms;
+  const int n4 = nsplit * AT_PART;  // float4s of the unit's states (4 heads x 130 floats each)
+  const float4* src = reinterpret_cast<const float4*>(partial + unit * nsplit * 4 * AT_PART);
+  for (int i = threadIdx.x; i < n4; i += 256) st_lds[i] = src[i];
+  __syncthreads();
+  const float* st = reinterpret_cast<const float*>(st_lds) + r * AT_PART;  // split s at + s*4*AT_PART
+  float M = -INFINITY;
+  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, st[s * 4 * AT_PART]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  const float f = have ? __builtin_amdgcn_exp2f(ms - Mu) : 0.f;
-  float L = f * ls;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-  f_lds[r][lane] = f;
-  __syncthreads();
-  float O0 = 0.f, O1 = 0.f;
-  int s = 0;
-  for (; s + 4 <= nsplit; s += 4) {
-    float2 v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float2*>(base + (int64_t)(s + u) * 4 * AT_PART + 2 + d0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      O0 = O0 + f_lds[r][s + u] * v[u].x;
-      O1 = O1 + f_lds[r][s + u] * v[u].y;
-    }
-  }
-  for (; s < nsplit; ++s) {
-    const float2 v = *reinterpret_cast<const float2*>(base + (int64_t)s * 4 * AT_PART + 2 + d0);
-    O0 = O0 + f_lds[r][s] * v.x;
-    O1 = O1 + f_lds[r][s] * v.y;
+  float L = 0.f, O0 = 0.f, O1 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* sp = st + s * 4 * AT_PART;
+    const float f = __builtin_amdgcn_exp2f(sp[0] - Mu);
+    const float2 v = *reinterpret_cast<const float2*>(sp + 2 + d0);
+    L = L + f * sp[1];
+    O0 = O0 + f * v.x;
+    O1 = O1 + f * v.y;
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const uint32_t packed = bf16_bits(O0 * inv) | (bf16_bits(O1 * inv) << 16);
@@ -280,9 +327,15 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   if (lse && lane == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
+// Decode units are few (rows x 4): each gets enough splits for about
+// S5_ATTN_BLOCKS workgroups in all, each split a multiple of 16 entries (four
+// per wave per chunk); prefill units are many and run unsplit.
+#ifndef S5_ATTN_BLOCKS
+#define S5_ATTN_BLOCKS 256
+#endif
 AttnPlan attn_plan(int32_t rows) {
   const int64_t units = (int64_t)rows * 4;
-  int64_t ns = units > 0 ? (4096 + units - 1) / units : 1;
+  int64_t ns = units > 0 ? (S5_ATTN_BLOCKS + units - 1) / units : 1;
   int64_t per = (AT_ENTRIES + ns - 1) / ns;
   per = (per + 15) / 16 * 16;
   if (per < 16) per = 16;
@@ -292,7 +345,7 @@ AttnPlan attn_plan(int32_t rows) {
   return a;
 }
 
-size_t attn_partial_bytes(int32_t rows) {
+size_t attn_workspace_bytes(int32_t rows) {
   const AttnPlan a = attn_plan(rows);
   if (a.nsplit <= 1) return 0;
   return (size_t)rows * 4 * a.nsplit * 4 * AT_PART * sizeof(float);

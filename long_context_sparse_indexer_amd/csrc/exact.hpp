@@ -28,16 +28,15 @@ __device__ inline float group_score4(float d0, float d1, float d2, float d3, con
   return s;
 }
 
-// Exact score of one candidate: sv = the 64 bytes of its group vector,
-// qg = the row's query for the group as exact fp64, laid out [64 dims][4 heads].
-__device__ inline float exact_group_score(const uint8_t* __restrict__ sv,
-                                          const double* __restrict__ qg,
-                                          const float* __restrict__ w4) {
+// Exact score of one candidate from the 64 bytes of its group vector (raw,
+// already loaded) and the row's query for the group as exact fp64, laid out
+// [64 dims][4 heads].
+__device__ inline float exact_group_score_raw(const uint4 (&raw)[4], const double* __restrict__ qg,
+                                              const float* __restrict__ w4) {
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
 #pragma unroll
   for (int part = 0; part < 4; ++part) {
-    const uint4 raw = ldg16(sv + 16 * part);
-    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t wds[4] = {raw[part].x, raw[part].y, raw[part].z, raw[part].w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wds[k], false);
@@ -55,6 +54,14 @@ __device__ inline float exact_group_score(const uint8_t* __restrict__ sv,
     }
   }
   return group_score4((float)a0, (float)a1, (float)a2, (float)a3, w4);
+}
+
+// the same, loading the 64 bytes at sv
+__device__ inline float exact_group_score(const uint8_t* __restrict__ sv,
+                                          const double* __restrict__ qg,
+                                          const float* __restrict__ w4) {
+  const uint4 raw[4] = {ldg16(sv), ldg16(sv + 16), ldg16(sv + 32), ldg16(sv + 48)};
+  return exact_group_score_raw(raw, qg, w4);
 }
 
 // Exact partial dots over 32 dims for the 4 heads: sv = 32 bytes of the

@@ -49,8 +49,15 @@ struct ScoreArgs {
   const uint8_t* summary;
   int64_t B, R_cap, ssb;
   int64_t pos_limit;      // rows at p >= pos_limit are invalid (no rope row)
-  float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score
+  const double* q64;      // from launch_qprep, exact query [rows, 4 groups, 64 dims, 4 heads]
+  bool exact;             // exact scores (score_exact_mode) instead of intervals
+  float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score, or (exact)
+                          // the exact scores as float [rows, 4, R_cap]
 };
+// Few rows (decode) are scored exactly, each candidate by one lane; many rows
+// (prefill) get intervals from the matrix cores and exact rescoring of the
+// few candidates near each selection boundary.
+inline bool score_exact_mode(int32_t rows) { return rows <= 64; }
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 
 // Top-k selection plan: the candidates of a (row, group) are cut into
@@ -66,6 +73,7 @@ size_t topk_partial_bytes(int32_t rows, int64_t R_cap);
 
 struct TopkArgs {
   const float2* bounds;  // [rows, 4, R_cap] from launch_score
+  bool exact;            // bounds holds exact scores (see ScoreArgs)
   const double* q64;     // exact query, for rescoring
   const float* w_head;
   int64_t w_stride_row;
@@ -92,7 +100,7 @@ struct AttnPlan {
   int32_t nsplit;
 };
 AttnPlan attn_plan(int32_t rows);
-size_t attn_partial_bytes(int32_t rows);
+size_t attn_workspace_bytes(int32_t rows);
 
 struct AttnArgs {
   const void* q;

@@ -292,8 +292,134 @@ __global__ __launch_bounds__(256) void score_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// exact scores: one block per (row, 64 * SX_NB candidates); wave g takes KV
+// group g, so the row's query for the group (exact fp64) is the same in every
+// lane and sits in scalar registers; each lane scores one candidate per
+// 64-candidate batch with fp64 fused multiply-adds, exact at every step
+// (exact.hpp). The block loads its candidates' 256-byte rows with contiguous
+// 16-byte loads (all batches in flight at once) and hands each wave its
+// group's 64 bytes per candidate through LDS (rows padded to 272 bytes, so
+// the per-lane reads do not collide in the banks).
+// ---------------------------------------------------------------------------
+constexpr int SX_NB = 4;       // 64-candidate batches per block
+constexpr int SX_ROW = 272;    // LDS bytes per candidate row
+
+__global__ __launch_bounds__(256) void score_exact_kernel(
+    const double* __restrict__ q64, const float* __restrict__ w_head, int64_t w_stride,
+    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
+    const uint8_t* __restrict__ S, int64_t B, int64_t R_cap, int64_t ssb, int64_t pos_limit,
+    float* __restrict__ scores) {
+  __shared__ __align__(16) uint8_t rows_lds[64 * SX_ROW];
+  const int tid = threadIdx.x;
+  const int g = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int lane = tid & 63;
+  const int64_t row = blockIdx.y;
+  const int32_t seq = row_seq[row];
+  const int64_t p = row_pos[row];
+  if (!(seq >= 0 && seq < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap)) return;
+  const int64_t nc = p >> 3;
+  const int64_t j0 = (int64_t)blockIdx.x * (64 * SX_NB);
+  if (j0 >= nc) return;
+  const uint8_t* Sb = S + (int64_t)seq * ssb;
+  const double* qg = q64 + (row * 4 + g) * 256;
+  float w4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
+
+  // thread t loads part t%16 of candidates t/16 + 16i of every batch;
+  // candidates past the row's last are loaded as its last one (not stored)
+  uint4 ld[SX_NB][4];
+  const int part = tid & 15;
+#pragma unroll
+  for (int b = 0; b < SX_NB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t j = j0 + 64 * b + (tid >> 4) + 16 * i;
+      const int64_t jl = j < nc ? j : nc - 1;
+      ld[b][i] = ldg16(Sb + jl * 256 + 16 * part);
+    }
+  uint4 raw[SX_NB][4];  // this lane's candidate, group g, per batch
+#pragma unroll
+  for (int b = 0; b < SX_NB; ++b) {
+    if (b > 0) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(rows_lds + ((tid >> 4) + 16 * i) * SX_ROW + 16 * part) = ld[b][i];
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      raw[b][u] = *reinterpret_cast<const uint4*>(rows_lds + lane * SX_ROW + g * 64 + 16 * u);
+  }
+
+  // dims outer, batches inner: each query value is loaded once (scalar) and
+  // used for the lane's SX_NB candidates; the fp64 sums are exact in any
+  // order. Empty asm statements that take the accumulators and clobber memory
+  // between 4-dim chunks keep the compiler to this order (it would otherwise
+  // run one batch over all dims first and keep the whole 2 KB query in scalar
+  // registers, which spills).
+  double acc[SX_NB][4];
+#pragma unroll
+  for (int b = 0; b < SX_NB; ++b)
+#pragma unroll
+    for (int h = 0; h < 4; ++h) acc[b][h] = 0.0;
+  double qc[16], qn[16];  // query values of dims 4w..4w+3 (x 4 heads), and the next four
+#pragma unroll
+  for (int i = 0; i < 16; ++i) qc[i] = qg[i];
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {  // 4-byte word w holds dims 4w..4w+3
+#pragma unroll
+    for (int b = 0; b < SX_NB; ++b)
+      asm volatile("" : "+v"(acc[b][0]), "+v"(acc[b][1]), "+v"(acc[b][2]), "+v"(acc[b][3])::"memory");
+    if (w < 15) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qn[i] = qg[16 * (w + 1) + i];
+    }
+    double sv[SX_NB][4];
+#pragma unroll
+    for (int b = 0; b < SX_NB; ++b) {
+      const uint4 r4 = raw[b][w >> 2];
+      const uint32_t word = (w & 3) == 0 ? r4.x : (w & 3) == 1 ? r4.y : (w & 3) == 2 ? r4.z : r4.w;
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+      sv[b][0] = (double)lo[0];
+      sv[b][1] = (double)lo[1];
+      sv[b][2] = (double)hi[0];
+      sv[b][3] = (double)hi[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int b = 0; b < SX_NB; ++b) acc[b][h] = fma(qc[4 * e + h], sv[b][e], acc[b][h]);
+    if (w < 15) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qc[i] = qn[i];
+    }
+  }
+  asm volatile("" ::: "memory");
+  float* out = scores + (row * 4 + g) * R_cap;
+#pragma unroll
+  for (int b = 0; b < SX_NB; ++b) {
+    const int64_t j = j0 + 64 * b + lane;
+    float sc = group_score4((float)acc[b][0], (float)acc[b][1], (float)acc[b][2],
+                            (float)acc[b][3], w4);
+    // computed in every lane (an opaque use), not sunk into the guarded store
+    asm volatile("" : "+v"(sc));
+    if (j < nc) out[j] = sc;
+  }
+}
+
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.rows == 0 || a.R_cap == 0) return hipSuccess;
+  if (a.exact) {
+    const dim3 grid((unsigned)((a.R_cap + 64 * SX_NB - 1) / (64 * SX_NB)), (unsigned)a.rows);
+    hipLaunchKernelGGL(score_exact_kernel, grid, dim3(256), 0, stream, a.q64, a.w_head,
+                       a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
+                       a.pos_limit, reinterpret_cast<float*>(a.bounds));
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));
   hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, a.q8, a.q8_stride_row, a.rows,
                      a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap,

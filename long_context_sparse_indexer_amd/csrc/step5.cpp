@@ -9,7 +9,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/step5.h"
+#include "step5.h"
 #include "launch.hpp"
 
 #define STEP5_EXPORT extern "C" __attribute__((visibility("default")))
@@ -200,11 +200,14 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   sa.R_cap = R_cap;
   sa.ssb = s_stride_b;
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
+  sa.q64 = q64;
+  sa.exact = s5::score_exact_mode(rows);
   sa.bounds = reinterpret_cast<float2*>(ws + w.bounds);
   st = from_hip(s5::launch_score(sa, stream));
   if (st) return st;
   s5::TopkArgs ta;
   ta.bounds = sa.bounds;
+  ta.exact = sa.exact;
   ta.q64 = q64;
   ta.w_head = w_head;
   ta.w_stride_row = w_stride_row;
@@ -225,7 +228,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
 
 STEP5_EXPORT size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows) {
   if (check_geom(geom) || rows <= 0 || rows > (INT32_MAX / 4)) return 0;
-  const size_t b = s5::attn_partial_bytes(rows);
+  const size_t b = s5::attn_workspace_bytes(rows);
   return b ? up(b) : 0;
 }
 

@@ -4,20 +4,21 @@
 // keep the top 512 regions by (-score, id), ascending: best score first,
 // equal scores by the smaller region id. Fewer than 512 candidates keep all.
 //
-// Input: the score kernel's interval [lo, hi] per candidate, which holds the
-// exact score. Per (row, group) and chunk of candidates (one 1024-thread
-// workgroup, everything in LDS; gfx950 gives a workgroup up to 160 KB):
-//   1. T = the K-th largest lower bound (K = min(512, candidates));
+// Input: the score kernel's exact score per candidate (few rows), which is
+// selected from directly, or its interval [lo, hi] holding the exact score. Per (row, group) and chunk of candidates (one 1024-thread
+// workgroup, everything in LDS; gfx950 gives a workgroup up to 160 KB), from
+// intervals:
+//   1. T = the top 22 bits of the K-th largest lower bound, the rest zero
+//      (K = min(512, candidates)), so T <= that bound;
 //   2. C = the candidates whose upper bound reaches T, kept in id order.
 //      C holds every candidate of the exact top K: each of those has
-//      hi >= exact score >= K-th largest exact score >= K-th largest lo = T;
+//      hi >= exact score >= K-th largest exact score >= K-th largest lo >= T;
 //   3. every member of C is rescored exactly (exact.hpp);
 //   4. the best K of C by (-exact score, id) are selected and sorted.
 // Candidate ranges past 16,384, and batches too small to fill the GPU, are
-// cut into chunks: each chunk keeps its exact best 512 in order; the last
+// cut into chunks: each chunk keeps its exact best 512, sorted; the last
 // chunk of a (row, group) to finish (an arrival counter per unit, zeroed by
-// the query prep of the same call) ranks the elements of the chunk lists
-// against each other.
+// the query prep of the same call) merges the chunk lists pairwise.
 //
 // Selecting the best K of N exact keys (scores mapped to 32-bit keys that
 // order like the scores, -0 taken as +0; ties broken by id):
@@ -25,9 +26,8 @@
 //   prefix P under a mask, such that keys above P are all taken and `need`
 //   keys with prefix P are taken in list order (list order is id order); the
 //   passes stop early when the boundary bin is taken whole. The bins are
-//   scanned by all threads at once (two bins each, a block-wide scan). Then
-//   every selected element gets its rank by counting the selected elements
-//   above it, which sorts them without a sorting network.
+//   scanned by all threads at once (two bins each, a block-wide scan). The
+//   selected elements are then sorted by a bitonic network.
 #include "device.hpp"
 #include "exact.hpp"
 #include "launch.hpp"
@@ -60,18 +60,16 @@ struct TkShared {
   uint32_t* hist;           // [TK_BINS]
   uint32_t* misc;           // [64]
   unsigned long long* out;  // [TK]
-  uint32_t* rank;           // [TK]
 };
 
 __host__ __device__ inline size_t tk_smem_bytes(int nmax) {
-  return (size_t)TK * 8 + (size_t)TK * 4 + (size_t)(TK_BINS + 64) * 4 + (size_t)nmax * 8;
+  return (size_t)TK * 8 + (size_t)(TK_BINS + 64) * 4 + (size_t)nmax * 8;
 }
 
 __device__ inline TkShared carve(unsigned char* base, int nmax) {
   TkShared s;
   s.out = reinterpret_cast<unsigned long long*>(base);
-  s.rank = reinterpret_cast<uint32_t*>(base + TK * 8);
-  s.hist = s.rank + TK;
+  s.hist = reinterpret_cast<uint32_t*>(base + TK * 8);
   s.misc = s.hist + TK_BINS;
   s.keys = s.misc + 64;
   s.ids = reinterpret_cast<int32_t*>(s.keys + nmax);
@@ -113,13 +111,14 @@ struct Boundary {
 
 // Radix select over keys[0..N), 1 <= K <= N: keys with (k & mask) > P are
 // the K - need best; `need` more come from the keys with (k & mask) == P.
-// With early = false all 32 bits are resolved (P is then the K-th best key).
-__device__ Boundary radix_boundary(const TkShared& sm, int N, int K, bool early) {
+// With early = false and passes = 3 all 32 bits are resolved (P is then the
+// K-th best key); fewer passes leave P = the K-th best key's top bits.
+__device__ Boundary radix_boundary(const TkShared& sm, int N, int K, bool early, int passes = 3) {
   const int tid = threadIdx.x;
   uint32_t P = 0, mask = 0, need = (uint32_t)K;
   const int shifts[3] = {21, 10, 0};
   const int bits[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < passes; ++pass) {
     const int shift = shifts[pass];
     const uint32_t nb = 1u << bits[pass];
     for (int i = tid; i < (int)nb; i += TK_THREADS) sm.hist[i] = 0;
@@ -218,40 +217,81 @@ __device__ void collect_best(const TkShared& sm, int N, int K, const int32_t* id
   __syncthreads();
 }
 
+// Bitonic network on 512 composites held one per thread by a group of 512
+// threads (i = index in the group; groups are whole waves). Stage (k, j):
+// compare with element i ^ j, keep the larger where the k-block runs
+// descending and i is the lower index of the pair (or neither), else the
+// smaller. Partners closer than 64 are in the wave (DPP or a lane permute);
+// farther ones go through xb (the group's 2 x 512 slots, alternated so one
+// barrier per stage suffices). Every thread of the block runs the stages
+// (the barriers); inactive ones exchange nothing.
+struct BitonicCtx {
+  int i, lane;
+  unsigned long long* xb;
+  bool active;
+  int flip;
+};
+
+template <int K, int J>
+__device__ inline unsigned long long bitonic_stage(unsigned long long v, BitonicCtx& c) {
+  unsigned long long p;
+  if constexpr (J >= 64) {
+    unsigned long long* b = c.xb + 512 * c.flip;
+    c.flip ^= 1;
+    if (c.active) b[c.i] = v;
+    __syncthreads();
+    p = c.active ? b[c.i ^ J] : 0ull;
+  } else {
+    p = lane_xor64<J>(v, c.lane);
+  }
+  const bool desc = (c.i & K) == 0;
+  const bool lower = (c.i & J) == 0;
+  return (desc == lower) ? (v > p ? v : p) : (v < p ? v : p);
+}
+
+// stages J, J/2, ..., 1 of merge size K
+template <int K, int J>
+struct BitonicMerge {
+  __device__ static inline unsigned long long run(unsigned long long v, BitonicCtx& c) {
+    v = bitonic_stage<K, J>(v, c);
+    return BitonicMerge<K, J / 2>::run(v, c);
+  }
+};
+template <int K>
+struct BitonicMerge<K, 0> {
+  __device__ static inline unsigned long long run(unsigned long long v, BitonicCtx&) { return v; }
+};
+// full sort of blocks of K (descending where (i & K) == 0)
+template <int K>
+struct BitonicSort {
+  __device__ static inline unsigned long long run(unsigned long long v, BitonicCtx& c) {
+    v = BitonicSort<K / 2>::run(v, c);
+    return BitonicMerge<K, K / 2>::run(v, c);
+  }
+};
+template <>
+struct BitonicSort<1> {
+  __device__ static inline unsigned long long run(unsigned long long v, BitonicCtx&) { return v; }
+};
+
 // sm.out[0..K) (distinct composites, any order) -> sorted best first;
-// sm.out[K..TK) = 0
+// sm.out[K..TK) = 0. Threads 0..511 sort, with the histogram as exchange space.
 __device__ void rank_sort(const TkShared& sm, int K) {
   const int tid = threadIdx.x;
-  // rank of each selected composite (all distinct): two threads per element,
-  // each counting half of the list; 16-byte LDS reads, eight in flight
-  const int e = tid & (TK - 1), half = tid >> 9;
-  uint32_t r = 0;
-  unsigned long long mine = 0;
-  if (e < K) {
-    mine = sm.out[e];
-    const int j0 = half * (TK / 2);
-    const int j1 = min(K, j0 + TK / 2);
-    const ulonglong2* o2 = reinterpret_cast<const ulonglong2*>(sm.out);
-    int j = j0;
-    for (; j + 16 <= j1; j += 16) {
-      ulonglong2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = o2[(j >> 1) + u];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) r += (v[u].x > mine) + (v[u].y > mine);
-    }
-    for (; j < j1; ++j) r += sm.out[j] > mine;
-  }
-  if (half == 1) sm.rank[e] = r;
+  BitonicCtx c;
+  c.i = tid & (TK - 1);
+  c.lane = tid & 63;
+  c.active = tid < TK;
+  c.xb = reinterpret_cast<unsigned long long*>(sm.hist);  // 2 x 512 slots
+  c.flip = 0;
+  unsigned long long v = (c.active && c.i < K) ? sm.out[c.i] : 0ull;
+  v = BitonicSort<TK>::run(v, c);
   __syncthreads();
-  if (half == 0 && e < K) r += sm.rank[e];
-  __syncthreads();
-  if (half == 0 && e < K) sm.out[r] = mine;  // distinct ranks: a permutation of 0..K-1
-  if (half == 1 && K + e < TK) sm.out[K + e] = 0ull;
+  if (c.active) sm.out[c.i] = v;
   __syncthreads();
 }
 
-__device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int K,
+__device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int64_t ncand,
                             int64_t unit, unsigned char* smem, int32_t* __restrict__ sel_ids,
                             float* __restrict__ sel_scores);
 
@@ -278,7 +318,7 @@ __device__ inline void write_final(const TkShared& sm, int K, int64_t unit, int3
 // One chunk of a (row, group)'s candidates: interval filter, exact rescoring,
 // exact selection. mode 0: the whole range, final output; mode 1: partial list.
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
-    int mode, const float2* __restrict__ bounds, int64_t R_cap, const int32_t* __restrict__ row_seq,
+    int mode, int exact, const float2* __restrict__ bounds, int64_t R_cap, const int32_t* __restrict__ row_seq,
     const int64_t* __restrict__ row_pos, int64_t B, int64_t pos_limit,
     const double* __restrict__ q64, const float* __restrict__ w_head, int64_t w_stride,
     const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
@@ -300,7 +340,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   const int K = N < TK ? N : TK;
   const float2* bsrc = bounds + unit * R_cap + j0;
   int M = 0;
-  if (K > 0) {
+  const int32_t* sel_from = sm.ids;  // ids of keys[0..M), or j0 + index when exact
+  int32_t id_base = 0;
+  if (exact) {
+    // exact scores: select straight from them
+    const float* ssrc = reinterpret_cast<const float*>(bounds) + unit * R_cap + j0;
+    for (int i = tid; i < N; i += TK_THREADS) sm.keys[i] = ord_key(ssrc[i]);
+    __syncthreads();
+    M = N;
+    sel_from = nullptr;
+    id_base = (int32_t)j0;
+  } else if (K > 0) {
     // 1. K-th largest lower bound (upper bounds parked in ids[] meanwhile)
     for (int i = tid; i < N; i += TK_THREADS) {
       const float2 b = bsrc[i];
@@ -308,7 +358,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
       sm.ids[i] = (int32_t)ord_key(b.y);
     }
     __syncthreads();
-    const Boundary bd = radix_boundary(sm, N, K, false);
+    // two passes fix the top 22 bits of the K-th largest lower bound; T (those
+    // bits, the rest zero) is at most that bound, which is all the filter needs
+    const Boundary bd = radix_boundary(sm, N, K, false, 2);
     const uint32_t T = bd.P;
     // 2. candidates whose upper bound reaches T, in id order: each thread
     //    takes its segment's upper bounds into registers, the scan orders the
@@ -353,65 +405,72 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     __syncthreads();
   }
   // 4. exact best K of the survivors
-  select_sorted(sm, M, K, sm.ids, 0);
   if (mode == 0) {
+    select_sorted(sm, M, K, sel_from, id_base);
     write_final(sm, K, unit, sel_ids, sel_scores);
     return;
   }
-  // chunk list out; the unit's last block to arrive merges all of them
+  // chunk list out: its best K, sorted, zero-padded to 512; the unit's last
+  // block to arrive merges all of them
+  select_sorted(sm, M, K, sel_from, id_base);
   unsigned long long* dst = partial + (unit * nchunks + c) * TK;
   for (int i = tid; i < TK; i += TK_THREADS) dst[i] = sm.out[i];
   __shared__ int sh_last;
-  __syncthreads();  // every thread's list stores have completed
-  if (tid == 0) {
-    __threadfence();  // release: the block's stores become visible device-wide
-    sh_last = atomicAdd(&arrivals[unit], 1u) == (unsigned)(nchunks - 1);
-    if (sh_last) __threadfence();  // acquire: drop stale copies before reading the lists
-  }
-  __syncthreads();
-  if (!sh_last) return;
-  const int Kall = ncand < TK ? (int)ncand : TK;
-  merge_lists(partial + unit * (int64_t)nchunks * TK, nchunks, Kall, unit, smem, sel_ids,
+  if (!block_arrive_last(&arrivals[unit], (unsigned)nchunks, &sh_last)) return;
+  merge_lists(partial + unit * (int64_t)nchunks * TK, nchunks, ncand, unit, smem, sel_ids,
               sel_scores);
 }
 
-// Merge of the chunk lists of one (row, group): each list is sorted best
-// first and composites are distinct, so an element's rank in the union is its
-// index in its own list plus, for every other list, the number of elements
-// above it there (a binary search). Elements ranked below K go to their rank:
-// the output is sorted. smem holds (nchunks + 1) * TK composites.
-__device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int K,
+// Merge of the chunk lists of one (row, group): each list holds its chunk's
+// exact best (at most 512) composites sorted best first, zero-padded, and
+// composites are distinct. The best 512 of two such lists A, B are
+// max(A[i], B[511 - i]), i < 512, a bitonic sequence, which the last nine
+// bitonic stages sort. Lists are merged in pairs (two pairs at a time, one
+// per half of the block) until one is left.
+__device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int64_t ncand,
                             int64_t unit, unsigned char* smem, int32_t* __restrict__ sel_ids,
                             float* __restrict__ sel_scores) {
-  unsigned long long* lists = reinterpret_cast<unsigned long long*>(smem);  // [nchunks][TK]
-  unsigned long long* outl = lists + (int64_t)nchunks * TK;                 // [TK]
-  const int N = nchunks * TK;
-  for (int i = threadIdx.x; i < N; i += TK_THREADS) lists[i] = src[i];
-  for (int i = threadIdx.x; i < TK; i += TK_THREADS) outl[i] = 0ull;
+  unsigned long long* lists = reinterpret_cast<unsigned long long*>(smem);  // [nchunks][512]
+  unsigned long long* xb = lists + (int64_t)nchunks * TK;                   // [2 groups][2][512]
+  const int tid = threadIdx.x;
+  const int grp = tid >> 9, i = tid & (TK - 1);
+  for (int t = tid; t < nchunks * TK; t += TK_THREADS) lists[t] = src[t];
   __syncthreads();
-  for (int i = threadIdx.x; i < N; i += TK_THREADS) {
-    const unsigned long long x = lists[i];
-    if (x == 0ull) continue;  // padding
-    const int c = i / TK;
-    int rank = i - c * TK;
-    for (int o = 0; o < nchunks && rank < K; ++o) {
-      if (o == c) continue;
-      const unsigned long long* L = lists + (int64_t)o * TK;
-      int lo = 0, hi = TK;  // count of L[j] > x: L is descending
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (L[mid] > x) lo = mid + 1; else hi = mid;
+  int nl = nchunks;
+  BitonicCtx bc;
+  bc.i = i;
+  bc.lane = tid & 63;
+  bc.xb = xb + grp * 2 * TK;
+  bc.flip = 0;
+  while (nl > 1) {
+    const int npairs = nl >> 1;
+    for (int p0 = 0; p0 < npairs; p0 += 2) {
+      const int pr = p0 + grp;
+      bc.active = pr < npairs;
+      unsigned long long v = 0ull;
+      if (bc.active) {
+        const unsigned long long a = lists[(2 * pr) * TK + i];
+        const unsigned long long b = lists[(2 * pr + 1) * TK + (TK - 1 - i)];
+        v = a > b ? a : b;
       }
-      rank += lo;
+      v = BitonicMerge<TK, TK / 2>::run(v, bc);
+      __syncthreads();
+      if (bc.active) lists[pr * TK + i] = v;
+      __syncthreads();
     }
-    if (rank < K) outl[rank] = x;
+    if (nl & 1) {
+      // the odd list moves down to slot npairs (its old list is merged already)
+      for (int t = tid; t < TK; t += TK_THREADS) lists[npairs * TK + t] = lists[(nl - 1) * TK + t];
+      __syncthreads();
+    }
+    nl = npairs + (nl & 1);
   }
-  __syncthreads();
-  for (int i = threadIdx.x; i < TK; i += TK_THREADS) {
-    const unsigned long long c = outl[i];
-    const bool have = i < K;
-    sel_ids[unit * TK + i] = have ? (int32_t)(~(uint32_t)c) : -1;
-    if (sel_scores) sel_scores[unit * TK + i] = have ? key_score((uint32_t)(c >> 32)) : 0.0f;
+  const int K = ncand < TK ? (int)ncand : TK;
+  for (int t = tid; t < TK; t += TK_THREADS) {
+    const unsigned long long c = lists[t];
+    const bool have = t < K;
+    sel_ids[unit * TK + t] = have ? (int32_t)(~(uint32_t)c) : -1;
+    if (sel_scores) sel_scores[unit * TK + t] = have ? key_score((uint32_t)(c >> 32)) : 0.0f;
   }
 }
 
@@ -447,14 +506,14 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const TopkPlan p = topk_plan(a.rows, a.R_cap);
   const unsigned units = (unsigned)a.rows * 4u;
   size_t sm = tk_smem_bytes((int)p.chunk);
-  const size_t sm_merge = (size_t)(p.nchunks + 1) * TK * sizeof(unsigned long long);
+  const size_t sm_merge = (size_t)(p.nchunks + 4) * TK * sizeof(unsigned long long);
   if (p.nchunks > 1 && sm_merge > sm) sm = sm_merge;
   hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const int mode = p.nchunks == 1 ? 0 : 1;
   hipLaunchKernelGGL(topk_chunk_kernel, dim3(units, (unsigned)p.nchunks), dim3(TK_THREADS), sm,
-                     stream, mode, a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit,
+                     stream, mode, a.exact ? 1 : 0, a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit,
                      a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks,
                      a.partial, a.arrivals, a.sel_ids, a.sel_scores);
   return hipGetLastError();

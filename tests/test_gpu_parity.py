@@ -113,6 +113,19 @@ def test_select_all_below_512_decode8_ctx3000(seed):
             assert np.all(got[r, g, 374:] == -1)
 
 
+def test_select_72_decode_rows_matrix_core_path():
+    """More than 64 rows take the matrix-core intervals and exact rescoring;
+    72 decode rows of 72 sequences (6,000 tokens: 750 candidates each) use its
+    per-row tiling."""
+    d = _case("decode8_ctx3000", 29, DEV, rows=72, batch=72, cache_tokens=6000, with_kv=False)
+    S = P.gpu_summary(d)
+    rows = [0, 1, 35, 70, 71]
+    O = np.concatenate([P.oracle_summary({**d, "k_idx": d["k_idx"][b:b + 1],
+                                          "z_idx": d["z_idx"][b:b + 1]}) for b in rows])
+    assert np.array_equal(S[rows].cpu().numpy(), O)
+    _select_check(d, S, O, rows, seq_map={b: i for i, b in enumerate(rows)})
+
+
 def test_select_prefill2048_ctx32k_sampled():
     d = _case("prefill2048_ctx32k", 17, DEV, with_kv=False)
     S = P.gpu_summary(d)
@@ -168,32 +181,41 @@ def test_fp8_products_exhaustive_through_scores():
             assert np.array_equal(got, prod), (hex(codes[a]), g)
 
 
-def _bounds_view(ws, rows, R_cap):
-    """The score intervals inside step5_index_score_topk's workspace (white-box:
-    e4m3 q [rows*1024 B], fp64 q [rows*8192 B], then float2 [rows, 4, R_cap],
-    each part 256-byte aligned)."""
+def _scores_view(ws, rows, R_cap, exact):
+    """The candidate scores inside step5_index_score_topk's workspace
+    (white-box: e4m3 q [rows*1024 B], fp64 q [rows*8192 B], then per (row,
+    group, candidate) the exact score as float, with up to 64 rows, or else an
+    interval as float2; each part 256-byte aligned)."""
     up = lambda x: (x + 255) // 256 * 256
     off = up(up(rows * 1024) + rows * 8192)
-    n = rows * 4 * R_cap * 2
-    return ws[off:off + n * 4].view(torch.float32).view(rows, 4, R_cap, 2)
+    k = 1 if exact else 2
+    n = rows * 4 * R_cap * k
+    return ws[off:off + n * 4].view(torch.float32).view(rows, 4, R_cap, k)
 
 
-@pytest.mark.parametrize("name,rows", [("decode16_ctx128k", [0, 5, 10]),
-                                       ("prefill2048_ctx32k", [0, 1, 1000, 2047])])
-def test_score_intervals_hold_exact_scores(name, rows):
-    """The matrix-core scores come with intervals derived from an error bound
-    of fp32 accumulation; every interval must hold the exact score."""
+@pytest.mark.parametrize("name,rows,kw", [
+    ("decode16_ctx128k", [0, 5, 10], {}),
+    ("decode8_ctx3000", [0, 33, 71], dict(rows=72, batch=72)),
+    ("prefill2048_ctx32k", [0, 1, 1000, 2047], {})])
+def test_scores_exact_or_bracketed(name, rows, kw):
+    """Up to 64 rows are scored exactly: the scores must equal the oracle's
+    bit for bit. More rows get matrix-core scores with intervals derived from
+    an error bound of fp32 accumulation: every interval must hold the exact
+    score (72 decode rows of different sequences, and a prefill chunk of one
+    sequence, cover both tilings)."""
     import long_context_sparse_indexer_amd as s5
-    d = _case(name, 23, DEV, with_kv=False)
+    d = _case(name, 23, DEV, with_kv=False, **kw)
     S = P.gpu_summary(d)
     R_cap = S.shape[1]
-    nb = s5.step5_index_score_topk_workspace(d["rows"], R_cap)
+    nrows = d["rows"]
+    exact = nrows <= 64
+    nb = s5.step5_index_score_topk_workspace(nrows, R_cap)
     ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
-    ids = torch.empty((d["rows"], 4, 512), dtype=torch.int32, device=DEV)
+    ids = torch.empty((nrows, 4, 512), dtype=torch.int32, device=DEV)
     s5.step5_index_score_topk(d["q_idx"], d["w_head"], d["row_seq"], d["row_pos"], S, ids,
                               q_norm_w=d["q_norm_w"], q_eps=P.EPS, rope=d["rope"], workspace=ws)
     torch.cuda.synchronize()
-    bnd = _bounds_view(ws, d["rows"], R_cap).cpu().numpy()[rows]
+    got = _scores_view(ws, nrows, R_cap, exact).cpu().numpy()[rows]
     seqs = sorted({int(d["row_seq"][r]) for r in rows})
     O = np.concatenate([P.oracle_summary({**d, "k_idx": d["k_idx"][s:s + 1],
                                           "z_idx": d["z_idx"][s:s + 1]}) for s in seqs])
@@ -201,13 +223,18 @@ def test_score_intervals_hold_exact_scores(name, rows):
     worst = 0.0
     for i, r in enumerate(rows):
         nc = int(d["row_pos"][r]) // 8
-        lo, hi, ex = bnd[i, :, :nc, 0], bnd[i, :, :nc, 1], osc[i, :, :nc]
+        ex = osc[i, :, :nc]
+        if exact:
+            assert np.array_equal(got[i, :, :nc, 0], ex), (name, r)
+            continue
+        lo, hi = got[i, :, :nc, 0], got[i, :, :nc, 1]
         assert np.all(lo <= ex) and np.all(ex <= hi), (name, r)
         half = (hi - lo) / 2
         mid = (hi + lo) / 2
         ok = half > 0
         worst = max(worst, float(np.max(np.abs(mid[ok] - ex[ok]) / half[ok])))
-    P.say(f"  largest |approx - exact| / half-width = {worst:.4f}")
+    if not exact:
+        P.say(f"  largest |approx - exact| / half-width = {worst:.4f}")
 
 
 # ---- edge rows ------------------------------------------------------------

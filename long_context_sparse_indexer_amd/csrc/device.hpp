@@ -66,6 +66,24 @@ __host__ __device__ inline uint32_t e4m3_from_bf16(uint32_t h) {
   return sign | v;                  // v == 8 is the smallest normal, as it should be
 }
 
+// The same two roundings by gfx950's conversion instructions, two values at a
+// time (a to the low half or byte, b to the next). bf16: nearest-even, as
+// bf16_bits for every finite input (fp32 denormals are kept, the default
+// mode). e4m3 of a bf16 value given as fp32: the clamp to +-448 first makes
+// the hardware's nearest-even conversion saturate like e4m3_from_bf16. Both
+// are checked against the software forms on the GPU, over every input.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t bf16x2_hw(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+template <bool HIGH_WORD>
+__device__ inline uint32_t e4m3x2_hw(float a, float b, uint32_t old) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HIGH_WORD);
+}
+
 // ---------------------------------------------------------------------------
 // The path's exp: Cody & Waite's (1980) argument reduction x = n*ln2 + r,
 // |r| <= ln2/2, with ln2 split in a 15-bit head and an fp32 tail; e^r from

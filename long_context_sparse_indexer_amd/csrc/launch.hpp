@@ -50,7 +50,9 @@ struct ScoreArgs {
   int64_t B, R_cap, ssb;
   int64_t pos_limit;      // rows at p >= pos_limit are invalid (no rope row)
   const double* q64;      // from launch_qprep, exact query [rows, 4 groups, 64 dims, 4 heads]
-  bool exact;             // exact scores (score_exact_mode) instead of intervals
+  bool exact;             // exact scores (score_exact_mode) instead of intervals; the q prep
+                          // is then done in the score kernel from `prep` (no launch_qprep)
+  QPrepArgs prep;
   float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score, or (exact)
                           // the exact scores as float [rows, 4, R_cap]
 };

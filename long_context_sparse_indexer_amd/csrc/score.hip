@@ -60,9 +60,57 @@ __device__ inline double e4m3_f64(uint32_t c) {
 }
 
 // ---------------------------------------------------------------------------
-// q prep: one 8-lane group per (row, head); lane c holds dims 8c..8c+7.
-// mode 0: bf16 input, full prep; mode 1: the input is already e4m3.
+// q prep of one (row r, head h) by an 8-lane group: lane c gets the e4m3
+// codes of dims 8c..8c+7 (all 8 lanes of the group must be active).
+// mode 0: bf16 input, RMSNorm with scale (1 + w), rotation, bf16, e4m3;
+// mode 1: the input is already e4m3.
 // ---------------------------------------------------------------------------
+__device__ inline void qprep_lane(int mode, const void* __restrict__ qin, int64_t qs, int64_t r,
+                                  int h, int c, int lane, const float* __restrict__ w, float eps,
+                                  const uint16_t* __restrict__ rope, int64_t rope_rows,
+                                  const int64_t* __restrict__ row_pos, uint32_t (&code)[8]) {
+  if (mode == 1) {
+    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(qin) + r * qs + h * 64 + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      code[i] = (raw.x >> (8 * i)) & 0xffu;
+      code[4 + i] = (raw.y >> (8 * i)) & 0xffu;
+    }
+    return;
+  }
+  const uint16_t* q = static_cast<const uint16_t*>(qin);
+  int64_t p = row_pos[r];
+  if (p < 0 || p >= rope_rows) p = 0;  // such a row selects nothing later; keep reads in range
+  float x[8], sq[8], y[8];
+  unpack_bf16x8(ldg16(q + r * qs + h * 64 + c * 8), x);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sq[i] = x[i] * x[i];
+  const float ms = sum8_lanes(pair8(sq), lane) / 64.0f;
+  const float rr = 1.0f / sqrtf(ms + eps);
+  const float4 w0 = reinterpret_cast<const float4*>(w)[2 * c];
+  const float4 w1 = reinterpret_cast<const float4*>(w)[2 * c + 1];
+  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float scale = 1.0f + wv[i];
+    y[i] = (x[i] * rr) * scale;
+  }
+  const bool rotated = c < 4, first_half = c < 2;
+  const int fi = (c & 1) * 8;
+  float cf[8], sf[8];
+  unpack_bf16x8(ldg16(rope + p * 32 + fi), cf);
+  unpack_bf16x8(ldg16(rope + p * 32 + 16 + fi), sf);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float other = dpp<DPP_QUAD_XOR2>(y[i]);
+    const float own_c = y[i] * cf[i];
+    const float oth_s = other * sf[i];
+    const float rot = first_half ? (own_c - oth_s) : (own_c + oth_s);
+    code[i] = e4m3_from_bf16(bf16_bits(rotated ? rot : y[i]));
+  }
+}
+
+// q prep kernel: one 8-lane group per (row, head)
 __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __restrict__ qin,
                                                     int64_t qs, int32_t rows,
                                                     const float* __restrict__ w, float eps,
@@ -84,45 +132,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
   const int64_t r = vec >> 4;
   const int h = (int)(vec & 15);
   uint32_t code[8];
-  if (mode == 1) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(qin) + r * qs + h * 64 + c * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      code[i] = (raw.x >> (8 * i)) & 0xffu;
-      code[4 + i] = (raw.y >> (8 * i)) & 0xffu;
-    }
-  } else {
-    const uint16_t* q = static_cast<const uint16_t*>(qin);
-    int64_t p = row_pos[r];
-    if (p < 0 || p >= rope_rows) p = 0;  // such a row selects nothing later; keep reads in range
-    float x[8], sq[8], y[8];
-    unpack_bf16x8(ldg16(q + r * qs + h * 64 + c * 8), x);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) sq[i] = x[i] * x[i];
-    const float ms = sum8_lanes(pair8(sq), lane) / 64.0f;
-    const float rr = 1.0f / sqrtf(ms + eps);
-    const float4 w0 = reinterpret_cast<const float4*>(w)[2 * c];
-    const float4 w1 = reinterpret_cast<const float4*>(w)[2 * c + 1];
-    const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float scale = 1.0f + wv[i];
-      y[i] = (x[i] * rr) * scale;
-    }
-    const bool rotated = c < 4, first_half = c < 2;
-    const int fi = (c & 1) * 8;
-    float cf[8], sf[8];
-    unpack_bf16x8(ldg16(rope + p * 32 + fi), cf);
-    unpack_bf16x8(ldg16(rope + p * 32 + 16 + fi), sf);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float other = dpp<DPP_QUAD_XOR2>(y[i]);
-      const float own_c = y[i] * cf[i];
-      const float oth_s = other * sf[i];
-      const float rot = first_half ? (own_c - oth_s) : (own_c + oth_s);
-      code[i] = e4m3_from_bf16(bf16_bits(rotated ? rot : y[i]));
-    }
-  }
+  qprep_lane(mode, qin, qs, r, h, c, lane, w, eps, rope, rope_rows, row_pos, code);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -294,10 +304,10 @@ __global__ __launch_bounds__(256) void score_kernel(
 
 // ---------------------------------------------------------------------------
 // exact scores: one block per (row, 64 * SX_NB candidates); wave g takes KV
-// group g, so the row's query for the group (exact fp64) is the same in every
-// lane and sits in scalar registers; each lane scores one candidate per
-// 64-candidate batch with fp64 fused multiply-adds, exact at every step
-// (exact.hpp). The block loads its candidates' 256-byte rows with contiguous
+// group g: it preps the row's query for the group's 4 heads (the same steps
+// as qprep_kernel) into LDS as exact fp64, a value every lane reads alike;
+// each lane scores one candidate per 64-candidate batch with fp64 fused
+// multiply-adds, exact at every step (exact.hpp). The block loads its candidates' 256-byte rows with contiguous
 // 16-byte loads (all batches in flight at once) and hands each wave its
 // group's 64 bytes per candidate through LDS (rows padded to 272 bytes, so
 // the per-lane reads do not collide in the banks).
@@ -306,15 +316,19 @@ constexpr int SX_NB = 4;       // 64-candidate batches per block
 constexpr int SX_ROW = 272;    // LDS bytes per candidate row
 
 __global__ __launch_bounds__(256) void score_exact_kernel(
-    const double* __restrict__ q64, const float* __restrict__ w_head, int64_t w_stride,
-    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
+    int qmode, const void* __restrict__ qin, int64_t qs, const float* __restrict__ qw, float eps,
+    const uint16_t* __restrict__ rope, int64_t rope_rows, const float* __restrict__ w_head,
+    int64_t w_stride, const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
     const uint8_t* __restrict__ S, int64_t B, int64_t R_cap, int64_t ssb, int64_t pos_limit,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, unsigned* __restrict__ arrivals) {
   __shared__ __align__(16) uint8_t rows_lds[64 * SX_ROW];
+  __shared__ __align__(16) double q_lds[4][256];  // per group: [64 dims][4 heads], exact
   const int tid = threadIdx.x;
   const int g = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
   const int lane = tid & 63;
   const int64_t row = blockIdx.y;
+  // the selection pass of this call counts chunk arrivals per (row, group)
+  if (blockIdx.x == 0 && lane == 0) arrivals[row * 4 + g] = 0u;
   const int32_t seq = row_seq[row];
   const int64_t p = row_pos[row];
   if (!(seq >= 0 && seq < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap)) return;
@@ -322,10 +336,20 @@ __global__ __launch_bounds__(256) void score_exact_kernel(
   const int64_t j0 = (int64_t)blockIdx.x * (64 * SX_NB);
   if (j0 >= nc) return;
   const uint8_t* Sb = S + (int64_t)seq * ssb;
-  const double* qg = q64 + (row * 4 + g) * 256;
   float w4[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
+  {
+    // q prep of the group's 4 heads (lanes 32..63 repeat lanes 0..31)
+    const int hh = (lane >> 3) & 3, c = lane & 7;
+    uint32_t code[8];
+    qprep_lane(qmode, qin, qs, row, 4 * g + hh, c, lane, qw, eps, rope, rope_rows, row_pos, code);
+    if (lane < 32) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q_lds[g][(8 * c + i) * 4 + hh] = e4m3_f64(code[i]);
+    }
+  }
+  const double* qg = q_lds[g];
 
   // thread t loads part t%16 of candidates t/16 + 16i of every batch;
   // candidates past the row's last are loaded as its last one (not stored)
@@ -352,11 +376,11 @@ __global__ __launch_bounds__(256) void score_exact_kernel(
       raw[b][u] = *reinterpret_cast<const uint4*>(rows_lds + lane * SX_ROW + g * 64 + 16 * u);
   }
 
-  // dims outer, batches inner: each query value is loaded once (scalar) and
+  // dims outer, batches inner: each query value is loaded once and
   // used for the lane's SX_NB candidates; the fp64 sums are exact in any
   // order. Empty asm statements that take the accumulators and clobber memory
   // between 4-dim chunks keep the compiler to this order (it would otherwise
-  // run one batch over all dims first and keep the whole 2 KB query in scalar
+  // run one batch over all dims first and keep the whole 2 KB query in
   // registers, which spills).
   double acc[SX_NB][4];
 #pragma unroll
@@ -415,9 +439,11 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.rows == 0 || a.R_cap == 0) return hipSuccess;
   if (a.exact) {
     const dim3 grid((unsigned)((a.R_cap + 64 * SX_NB - 1) / (64 * SX_NB)), (unsigned)a.rows);
-    hipLaunchKernelGGL(score_exact_kernel, grid, dim3(256), 0, stream, a.q64, a.w_head,
-                       a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                       a.pos_limit, reinterpret_cast<float*>(a.bounds));
+    hipLaunchKernelGGL(score_exact_kernel, grid, dim3(256), 0, stream, a.prep.prepared ? 1 : 0,
+                       a.prep.q, a.prep.q_stride_row, a.prep.w, a.prep.eps,
+                       (const uint16_t*)a.prep.rope, a.prep.rope_rows, a.w_head, a.w_stride_row,
+                       a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb, a.pos_limit,
+                       reinterpret_cast<float*>(a.bounds), a.prep.arrivals);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));

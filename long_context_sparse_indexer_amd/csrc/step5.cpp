@@ -185,9 +185,11 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   qa.q8 = q8;
   qa.q64 = q64;
   qa.arrivals = reinterpret_cast<unsigned*>(ws + w.arrivals);
-  int st = from_hip(s5::launch_qprep(qa, stream));
+  const bool exact = s5::score_exact_mode(rows);
+  int st = exact ? STEP5_OK : from_hip(s5::launch_qprep(qa, stream));
   if (st) return st;
   s5::ScoreArgs sa;
+  sa.prep = qa;
   sa.q8 = q8;
   sa.q8_stride_row = (int64_t)kIdxHeads * kIdxDim;
   sa.rows = rows;
@@ -201,7 +203,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   sa.ssb = s_stride_b;
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
   sa.q64 = q64;
-  sa.exact = s5::score_exact_mode(rows);
+  sa.exact = exact;
   sa.bounds = reinterpret_cast<float2*>(ws + w.bounds);
   st = from_hip(s5::launch_score(sa, stream));
   if (st) return st;

@@ -13,6 +13,8 @@
 //   summary, per (region, group, dim):  m = max_t z_t, e_t = exp_fixed(z_t - m),
 //     den and num summed in token order (num of the rounded products e_t*k_t),
 //     s = num/den, code = e4m3(bf16(s)).
+// The bf16 and e4m3 roundings use gfx950's conversion instructions
+// (bf16x2_hw, e4m3x2_hw), which give the same bits as the software forms.
 //
 // Mapping: a region is 4 KB of k and 4 KB of z (8 tokens x 4 groups x 64
 // bf16, contiguous). 32 lanes own it: lane (g, c) holds dims 8c..8c+7 of group
@@ -48,6 +50,7 @@ __global__ __launch_bounds__(256) void summarize_kernel(
   const bool rotated = c < 4;        // dims 0..31
   const bool first_half = c < 2;     // dims 0..15 hold the pair's first element
   const int fi = (c & 1) * 8;        // frequency index of this lane's first dim
+  const uint32_t sflip = first_half ? 0x80000000u : 0u;
   const int64_t j0 = t0 >> 3;
 
   for (int64_t u = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); u < total;
@@ -93,18 +96,27 @@ __global__ __launch_bounds__(256) void summarize_kernel(
         const float tt = (d[i] * r) * gw[i];
         y[i] = tt + gb[i];
       }
-      // NEOX rotation: lanes c and c^2 (c < 4) hold the two halves of the pairs
+      // NEOX rotation: lanes c and c^2 (c < 4) hold the two halves of the
+      // pairs; a*c - b*s on the first half is computed as a*c + b*(-s)
+      // (negation is exact)
       float cf[8], sf[8];
       unpack_bf16x8(ldg16(cs + t * 32 + fi), cf);
       unpack_bf16x8(ldg16(cs + t * 32 + 16 + fi), sf);
-      float kv[8];
+      float rv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float other = dpp<DPP_QUAD_XOR2>(y[i]);
+        const float sfs = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sf[i]) ^ sflip);
         const float own_c = y[i] * cf[i];
-        const float oth_s = other * sf[i];
-        const float rot = first_half ? (own_c - oth_s) : (own_c + oth_s);
-        kv[i] = bf16_round(rotated ? rot : y[i]);
+        const float oth_s = dpp<DPP_QUAD_XOR2>(y[i]) * sfs;
+        const float rot = own_c + oth_s;
+        rv[i] = rotated ? rot : y[i];
+      }
+      float kv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t pk = bf16x2_hw(rv[2 * i], rv[2 * i + 1]);
+        kv[2 * i] = bf_lo(pk);
+        kv[2 * i + 1] = bf_hi(pk);
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -119,14 +131,17 @@ __global__ __launch_bounds__(256) void summarize_kernel(
         }
       }
     }
-    uint32_t lo = 0, hi = 0;
+    float sb[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = num[i] / den[i];
-      const uint32_t code = e4m3_from_bf16(bf16_bits(s));
-      if (i < 4) lo |= code << (8 * i);
-      else hi |= code << (8 * (i - 4));
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pk = bf16x2_hw(num[2 * i] / den[2 * i], num[2 * i + 1] / den[2 * i + 1]);
+      sb[2 * i] = bf_lo(pk);
+      sb[2 * i + 1] = bf_hi(pk);
     }
+    uint32_t lo = e4m3x2_hw<false>(sb[0], sb[1], 0u);
+    lo = e4m3x2_hw<true>(sb[2], sb[3], lo);
+    uint32_t hi = e4m3x2_hw<false>(sb[4], sb[5], 0u);
+    hi = e4m3x2_hw<true>(sb[6], sb[7], hi);
     uint2* dst = reinterpret_cast<uint2*>(S + b * ssb + (j0 + jr) * 256 + g * 64 + c * 8);
     *dst = make_uint2(lo, hi);
   }

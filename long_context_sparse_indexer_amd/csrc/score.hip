@@ -387,18 +387,11 @@ __global__ __launch_bounds__(256) void score_exact_kernel(
   for (int b = 0; b < SX_NB; ++b)
 #pragma unroll
     for (int h = 0; h < 4; ++h) acc[b][h] = 0.0;
-  double qc[16], qn[16];  // query values of dims 4w..4w+3 (x 4 heads), and the next four
-#pragma unroll
-  for (int i = 0; i < 16; ++i) qc[i] = qg[i];
 #pragma unroll
   for (int w = 0; w < 16; ++w) {  // 4-byte word w holds dims 4w..4w+3
 #pragma unroll
     for (int b = 0; b < SX_NB; ++b)
       asm volatile("" : "+v"(acc[b][0]), "+v"(acc[b][1]), "+v"(acc[b][2]), "+v"(acc[b][3])::"memory");
-    if (w < 15) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qn[i] = qg[16 * (w + 1) + i];
-    }
     double sv[SX_NB][4];
 #pragma unroll
     for (int b = 0; b < SX_NB; ++b) {
@@ -412,14 +405,14 @@ __global__ __launch_bounds__(256) void score_exact_kernel(
       sv[b][3] = (double)hi[1];
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
+      const int d = 4 * w + e;
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
+      for (int h = 0; h < 4; ++h) {
+        const double qv = qg[4 * d + h];
 #pragma unroll
-        for (int b = 0; b < SX_NB; ++b) acc[b][h] = fma(qc[4 * e + h], sv[b][e], acc[b][h]);
-    if (w < 15) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) qc[i] = qn[i];
+        for (int b = 0; b < SX_NB; ++b) acc[b][h] = fma(qv, sv[b][e], acc[b][h]);
+      }
     }
   }
   asm volatile("" ::: "memory");

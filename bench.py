@@ -32,6 +32,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per step5_sparse_attn call (attn_kernel + attn_merge_kernel) on
+# decode16_ctx128k, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE;
+# profiles/sparse_attn_hbm_counters_decode16_ctx128k.md), each scaled by what
+# the counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
+# Valid only for the attention source the counters were taken on.
+ATTN_TRAFFIC = {"source_sha256": "df915b3bb38687258d3dff1aee2239e2f34331461d47be83dfa82194f0b9d93e",
+                "bytes_per_launch": 136095687}
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"
@@ -268,6 +275,18 @@ def run_workload(name, args, torch, s5, W):
     return res, d, S
 
 
+def attn_traffic(workload):
+    """Measured HBM bytes per attention call, or None when the workload or the
+    attention source differs from the one the counters were taken on."""
+    import hashlib
+    if workload != HEADLINE:
+        return None
+    path = os.path.join(ROOT, "long_context_sparse_indexer_amd", "csrc", "attn.hip")
+    with open(path, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["source_sha256"] else None
+
+
 def copy_ceiling(torch):
     """A plain device-to-device copy of 1 GiB: the HBM rate a streaming kernel
     reaches on this GPU (read + write bytes per second)."""
@@ -329,9 +348,10 @@ def main():
         "config": {"workload": wl.name, "rows": head["rows"], "context_tokens": head["context_tokens"],
                    "sequences": head["sequences"], "topk": 512, "region": 8, "idx_heads": 16,
                    "kv_groups": 4, "q_heads": 16, "head_dim": 128, "inputs": wl.dist},
-        "roofline": {"bound": "hbm", "kernel": "step5_sparse_attn (attn_kernel)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "step5_sparse_attn (attn_kernel + attn_merge_kernel)",
                      "achieved": sa["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": sa["frac_hbm"], "traffic": None,
+                     "frac": sa["frac_hbm"], "traffic": attn_traffic(args.workload),
                      "algorithmic_bytes_per_launch": sa["algorithmic_bytes"]},
         "phases": {"graph_replay": not args.eager, **{k: v for k, v in head.items()
                                                       if k not in ("workload",)}},

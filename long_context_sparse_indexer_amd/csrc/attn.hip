@@ -179,6 +179,34 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int wb = e0 + 4 * wave;
   const int niter = wb < e1 ? (e1 - wb + 15) >> 4 : 0;
   const int32_t* sl = sel + unit * 512;
+  __shared__ uint32_t ids_lds[512];
+  if (nsplit == 1) {
+    // one workgroup per unit (many rows: prefill): visit the selected regions
+    // in id order, so the units resident on a chip die sweep the context
+    // together and share its cached K/V lines; ids sort as unsigned (-1 last)
+    for (int i = threadIdx.x; i < 512; i += 256) ids_lds[i] = (uint32_t)sl[i];
+    __syncthreads();
+#pragma unroll 1
+    for (int kk = 2; kk <= 512; kk <<= 1)
+#pragma unroll 1
+      for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int i = threadIdx.x + 256 * h;
+          const int pi = i ^ jj;
+          if (pi > i) {
+            const uint32_t a = ids_lds[i], b = ids_lds[pi];
+            const bool up = (i & kk) == 0;
+            if ((a > b) == up) {
+              ids_lds[i] = b;
+              ids_lds[pi] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    sl = reinterpret_cast<const int32_t*>(ids_lds);
+  }
   int64_t lj;
   int lcnt;
   auto load_table = [&](int ibase) {

@@ -46,43 +46,31 @@
 
 namespace s5 {
 
-// exact value of an e4m3 code (finite codes)
-__device__ inline double e4m3_f64(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  double v;
-  if (e == 0) {
-    v = (double)m * 0x1p-9;
-  } else {
-    const unsigned long long bits = ((unsigned long long)(e + 1016u) << 52) | ((unsigned long long)m << 49);
-    v = __builtin_bit_cast(double, bits);
-  }
-  return (c & 0x80u) ? -v : v;
-}
-
 // ---------------------------------------------------------------------------
 // q prep of one (row r, head h) by an 8-lane group: lane c gets the e4m3
-// codes of dims 8c..8c+7 (all 8 lanes of the group must be active).
+// codes of dims 8c..8c+7, packed (byte i = dim 8c + i; all 8 lanes of the
+// group must be active).
 // mode 0: bf16 input, RMSNorm with scale (1 + w), rotation, bf16, e4m3;
 // mode 1: the input is already e4m3.
+// The bf16 and e4m3 roundings use gfx950's conversion instructions
+// (bf16x2_hw, e4m3x2_hw), which give the same bits as the software forms.
 // ---------------------------------------------------------------------------
-__device__ inline void qprep_lane(int mode, const void* __restrict__ qin, int64_t qs, int64_t r,
-                                  int h, int c, int lane, const float* __restrict__ w, float eps,
-                                  const uint16_t* __restrict__ rope, int64_t rope_rows,
-                                  const int64_t* __restrict__ row_pos, uint32_t (&code)[8]) {
-  if (mode == 1) {
-    const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(qin) + r * qs + h * 64 + c * 8);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      code[i] = (raw.x >> (8 * i)) & 0xffu;
-      code[4 + i] = (raw.y >> (8 * i)) & 0xffu;
-    }
-    return;
-  }
+__device__ inline uint2 qprep8(int mode, const void* __restrict__ qin, int64_t qs, int64_t r,
+                               int h, int c, int lane, const float* __restrict__ w, float eps,
+                               const uint16_t* __restrict__ rope, int64_t rope_rows,
+                               const int64_t* __restrict__ row_pos) {
+  if (mode == 1)
+    return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(qin) + r * qs + h * 64 + c * 8);
   const uint16_t* q = static_cast<const uint16_t*>(qin);
   int64_t p = row_pos[r];
   if (p < 0 || p >= rope_rows) p = 0;  // such a row selects nothing later; keep reads in range
+  const bool rotated = c < 4, first_half = c < 2;
+  const int fi = (c & 1) * 8;
+  const uint4 qraw = ldg16(q + r * qs + h * 64 + c * 8);
+  const uint4 craw = ldg16(rope + p * 32 + fi);
+  const uint4 sraw = ldg16(rope + p * 32 + 16 + fi);
   float x[8], sq[8], y[8];
-  unpack_bf16x8(ldg16(q + r * qs + h * 64 + c * 8), x);
+  unpack_bf16x8(qraw, x);
 #pragma unroll
   for (int i = 0; i < 8; ++i) sq[i] = x[i] * x[i];
   const float ms = sum8_lanes(pair8(sq), lane) / 64.0f;
@@ -95,19 +83,40 @@ __device__ inline void qprep_lane(int mode, const void* __restrict__ qin, int64_
     const float scale = 1.0f + wv[i];
     y[i] = (x[i] * rr) * scale;
   }
-  const bool rotated = c < 4, first_half = c < 2;
-  const int fi = (c & 1) * 8;
-  float cf[8], sf[8];
-  unpack_bf16x8(ldg16(rope + p * 32 + fi), cf);
-  unpack_bf16x8(ldg16(rope + p * 32 + 16 + fi), sf);
+  float cf[8], sf[8], v[8];
+  unpack_bf16x8(craw, cf);
+  unpack_bf16x8(sraw, sf);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float other = dpp<DPP_QUAD_XOR2>(y[i]);
     const float own_c = y[i] * cf[i];
     const float oth_s = other * sf[i];
     const float rot = first_half ? (own_c - oth_s) : (own_c + oth_s);
-    code[i] = e4m3_from_bf16(bf16_bits(rotated ? rot : y[i]));
+    v[i] = rotated ? rot : y[i];
   }
+  float bf[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t pk = bf16x2_hw(v[2 * i], v[2 * i + 1]);
+    bf[2 * i] = bf_lo(pk);
+    bf[2 * i + 1] = bf_hi(pk);
+  }
+  uint32_t lo = e4m3x2_hw<false>(bf[0], bf[1], 0u);
+  lo = e4m3x2_hw<true>(bf[2], bf[3], lo);
+  uint32_t hi = e4m3x2_hw<false>(bf[4], bf[5], 0u);
+  hi = e4m3x2_hw<true>(bf[6], bf[7], hi);
+  return make_uint2(lo, hi);
+}
+
+// exact values of 8 packed e4m3 codes (every e4m3 value is an fp32 value)
+__device__ inline void e4m3x8_f64(uint2 pk, double (&out)[8]) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.x, false);
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.x, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.y, false);
+  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.y, true);
+  const float f[8] = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (double)f[i];
 }
 
 // q prep kernel: one 8-lane group per (row, head)
@@ -131,18 +140,13 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
   if (vec >= (int64_t)rows * 16) return;  // whole 8-lane groups leave together
   const int64_t r = vec >> 4;
   const int h = (int)(vec & 15);
-  uint32_t code[8];
-  qprep_lane(mode, qin, qs, r, h, c, lane, w, eps, rope, rope_rows, row_pos, code);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo |= code[i] << (8 * i);
-    hi |= code[4 + i] << (8 * i);
-  }
-  *reinterpret_cast<uint2*>(q8 + vec * 64 + c * 8) = make_uint2(lo, hi);
+  const uint2 pk = qprep8(mode, qin, qs, r, h, c, lane, w, eps, rope, rope_rows, row_pos);
+  *reinterpret_cast<uint2*>(q8 + vec * 64 + c * 8) = pk;
+  double vals[8];
+  e4m3x8_f64(pk, vals);
   double* dst = q64 + ((r * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i * 4] = e4m3_f64(code[i]);
+  for (int i = 0; i < 8; ++i) dst[i * 4] = vals[i];
 }
 
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream) {
@@ -163,16 +167,12 @@ constexpr int SC_CB = 64;  // candidates per block (decode: one per wave-row; pr
 struct Bf16x16 {
   uint4 lo, hi;
 };
+// bytes 2*UPPER, 2*UPPER + 1 of w as two bf16 (the first in the low half):
+// gfx950's scaled fp8 -> bf16 conversion with scale 1, exact since every
+// e4m3 value is a bf16 value
 template <bool UPPER>
 __device__ inline uint32_t widen2(uint32_t w) {
-  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, UPPER);
-  // the high halves of the two fp32 values are their exact bf16 values;
-  // element 2k goes to the low half. The elements are copied to scalars
-  // before the bit casts: clang compiles a bit cast of a member access on an
-  // ext_vector_type value (f.y) as a cast of the vector's first element.
-  const float fx = f[0], fy = f[1];
-  const uint32_t a = __builtin_bit_cast(uint32_t, fx), b = __builtin_bit_cast(uint32_t, fy);
-  return (a >> 16) | (b & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, UPPER));
 }
 __device__ inline Bf16x16 widen16(uint4 v) {
   Bf16x16 r;
@@ -203,11 +203,41 @@ __device__ inline float2 score_interval(f32x4 d, f32x4 a, const float* w4) {
   return make_float2(s - delta, s + delta);
 }
 
+// prep of the block's query rows into LDS (fused_prep, few rows): wave w
+// preps row r0 + w (16 heads, two passes of eight 8-lane groups) into
+// q_lds[w] as e4m3; the block of the first candidate range also writes the
+// row's exact query for the rescoring pass and zeroes its top-k arrival
+// counters (no early exit comes before this).
+__device__ inline void score_fused_prep(const QPrepArgs& pa, int r0, int nr, const int32_t* seq,
+                                        bool first_block, uint8_t (*q_lds)[16 * 64]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (wave >= nr) return;
+  const int64_t r = r0 + wave;
+  if (first_block && lane < 4) pa.arrivals[r * 4 + lane] = 0u;
+  if (seq[wave] < 0) return;
+  const int c = lane & 7;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int h = 8 * pass + (lane >> 3);
+    const uint2 pk = qprep8(pa.prepared ? 1 : 0, pa.q, pa.q_stride_row, r, h, c, lane, pa.w, pa.eps,
+                           static_cast<const uint16_t*>(pa.rope), pa.rope_rows, pa.row_pos);
+    *reinterpret_cast<uint2*>(&q_lds[wave][h * 64 + c * 8]) = pk;
+    if (first_block) {
+      double vals[8];
+      e4m3x8_f64(pk, vals);
+      double* dst = pa.q64 + ((r * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i * 4] = vals[i];
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void score_kernel(
     const uint8_t* __restrict__ q8, int64_t qs8, int32_t rows, const float* __restrict__ w_head,
     int64_t w_stride, const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
     const uint8_t* __restrict__ S, int64_t B, int64_t R_cap, int64_t ssb, int64_t pos_limit,
-    float2* __restrict__ bounds) {
+    float2* __restrict__ bounds, int fused_prep, QPrepArgs prep) {
+  __shared__ __align__(16) uint8_t q_lds[4][16 * 64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
   const int r0 = blockIdx.y * 4;
@@ -231,7 +261,6 @@ __global__ __launch_bounds__(256) void score_kernel(
       maxc = ncand[i] > maxc ? ncand[i] : maxc;
     }
   }
-  if (cb0 >= maxc) return;
   int32_t s0 = -1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -240,6 +269,30 @@ __global__ __launch_bounds__(256) void score_kernel(
       else if (seq[i] != s0) shared = false;
     }
   }
+  // rows of different sequences: wave w scores row r0 + w over candidates
+  // cb0..jend-1; its 64 candidates' loads (16 per lane) are issued first, so
+  // they are in flight during the query prep. In iteration u, column n of
+  // the MFMA's B operand is candidate cb0 + 4u + n/4 of group
+  // ((n & 3) + u) & 3 (the 1 KB of four candidates, the groups rotated by u)
+  const bool dec_live = !shared && wave < nr && seq[wave] >= 0 && cb0 < ncand[wave];
+  const int64_t jend = dec_live ? ((cb0 + SC_CB < ncand[wave]) ? cb0 + SC_CB : ncand[wave]) : 0;
+  uint4 bq[SC_CB / 4];
+  if (dec_live) {
+    const uint8_t* Sb = S + (int64_t)seq[wave] * ssb;
+#pragma unroll
+    for (int u = 0; u < SC_CB / 4; ++u) {
+      // candidates past jend load candidate jend - 1 again (not stored)
+      const int64_t j = cb0 + u * 4 + (n >> 2);
+      const int64_t jl = j < jend ? j : jend - 1;
+      bq[u] = ldg16(Sb + jl * 256 + (((n & 3) + u) & 3) * 64 + 16 * qd);
+    }
+  }
+  if (fused_prep) {
+    if (blockIdx.x != 0 && cb0 >= maxc) return;  // block-uniform
+    score_fused_prep(prep, r0, nr, seq, blockIdx.x == 0, q_lds);
+    __syncthreads();
+  }
+  if (cb0 >= maxc) return;
 
   if (shared) {
     // ---- one sequence: A = (4 rows x 4 heads of group g), B = 16 candidates of g
@@ -249,7 +302,9 @@ __global__ __launch_bounds__(256) void score_kernel(
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       uint4 raw = make_uint4(0, 0, 0, 0);
-      if (rr < nr && seq[rr] >= 0) raw = ldg16(q8 + (int64_t)(r0 + rr) * qs8 + (4 * g + hh) * 64 + 16 * qd);
+      if (rr < nr && seq[rr] >= 0)
+        raw = fused_prep ? *reinterpret_cast<const uint4*>(&q_lds[rr][(4 * g + hh) * 64 + 16 * qd])
+                         : ldg16(q8 + (int64_t)(r0 + rr) * qs8 + (4 * g + hh) * 64 + 16 * qd);
       aq[g] = widen16(raw);
     }
     const int orow = r0 + qd;
@@ -273,31 +328,111 @@ __global__ __launch_bounds__(256) void score_kernel(
       if (j < onc) bounds[((int64_t)orow * 4 + g) * R_cap + j] = score_interval(d, a, w4[g]);
     }
   } else {
-    // ---- rows of different sequences: wave w scores row r0 + w
-    if (wave >= nr || seq[wave] < 0) return;
+    // ---- rows of different sequences (loads issued above)
+    if (!dec_live) return;
     const int row = r0 + wave;
-    const int64_t nc = ncand[wave];
-    if (cb0 >= nc) return;
-    const uint8_t* Sb = S + (int64_t)seq[wave] * ssb;
-    const Bf16x16 aq = widen16(ldg16(q8 + (int64_t)row * qs8 + n * 64 + 16 * qd));
+    const Bf16x16 aq = widen16(fused_prep ? *reinterpret_cast<const uint4*>(&q_lds[wave][n * 64 + 16 * qd])
+                                          : ldg16(q8 + (int64_t)row * qs8 + n * 64 + 16 * qd));
     float w4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w4[i] = w_head[(int64_t)row * w_stride + 4 * qd + i];
-    const bool keep = qd == (n & 3);
-    const int64_t jend = (cb0 + SC_CB < nc) ? cb0 + SC_CB : nc;
-    // all 64 candidates' loads in flight at once (16 per lane)
-    uint4 bq[SC_CB / 4];
+    // output lane (n, qd) holds heads 4qd..4qd+3 of column n: the result is
+    // one of the row's (group qd) in the iteration u with ((n & 3) + u) & 3
+    // == qd, once in every four; those are kept and scored four at a time
+    const int mu = (qd - (n & 3)) & 3;
+    f32x4 dk = {0.f, 0.f, 0.f, 0.f}, ak = dk;
 #pragma unroll
     for (int u = 0; u < SC_CB / 4; ++u) {
-      const int64_t j = cb0 + u * 4 + (n >> 2);
-      bq[u] = (j < jend) ? ldg16(Sb + (cb0 + u * 4) * 256 + n * 64 + 16 * qd) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < SC_CB / 4; ++u) {
-      const int64_t j = cb0 + u * 4 + (n >> 2);
       f32x4 d, a;
       dot64(aq, widen16(bq[u]), d, a);
-      if (keep && j < jend) bounds[((int64_t)row * 4 + qd) * R_cap + j] = score_interval(d, a, w4);
+      const bool mine = (u & 3) == mu;
+      dk = mine ? d : dk;
+      ak = mine ? a : ak;
+      if ((u & 3) == 3) {
+        const int64_t j = cb0 + (u - 3 + mu) * 4 + (n >> 2);
+        const float2 iv = score_interval(dk, ak, w4);
+        if (j < jend) bounds[((int64_t)row * 4 + qd) * R_cap + j] = iv;
+      }
+    }
+  }
+}
+
+// Few rows (the query prep fused): one block per (row, 256 candidates); wave
+// w scores candidates cb0 + 64w .. cb0 + 64w + 63 of the row with A = the
+// row's 16 heads and B = 4 candidates x 4 groups per iteration (1 KB
+// contiguous), the groups rotated by the iteration u so that every output
+// lane holds one of the row's results (its own group) in one iteration of
+// every four. Waves 0 and 1 prep the row's 16 heads into LDS once per block;
+// the first candidate block also writes the exact query for the rescoring
+// pass and zeroes the row's top-k arrival counters. Each wave's 64
+// candidates are loaded (16 per lane) before the prep, so they are in flight
+// during it.
+constexpr int SR_CB = 256;  // candidates per block
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_rows_kernel(
+    const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
+    const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
+    int64_t ssb, int64_t pos_limit, float2* __restrict__ bounds, QPrepArgs prep) {
+  __shared__ __align__(16) uint8_t q_lds[16 * 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, qd = lane >> 4;
+  const int64_t row = blockIdx.y;
+  const int32_t s = row_seq[row];
+  const int64_t p = row_pos[row];
+  const bool ok = s >= 0 && s < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap;
+  const int64_t nc = ok ? (p >> 3) : 0;
+  if (blockIdx.x == 0 && threadIdx.x < 4) prep.arrivals[row * 4 + threadIdx.x] = 0u;
+  if ((int64_t)blockIdx.x * SR_CB >= nc) return;  // block-uniform
+  const int64_t cb0 = (int64_t)blockIdx.x * SR_CB + 64 * wave;
+  const bool live = cb0 < nc;
+  const int64_t jend = live ? (cb0 + 64 < nc ? cb0 + 64 : nc) : 0;
+  uint4 bq[16];
+  if (live) {
+    // wave-uniform base, 32-bit lane offsets; candidates past jend load
+    // candidate jend - 1 again (not stored)
+    const uint8_t* Sw = S + (int64_t)s * ssb + cb0 * 256;
+    const uint32_t jlast = (uint32_t)(jend - cb0 - 1);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const uint32_t jo = min((uint32_t)(u * 4 + (n >> 2)), jlast);
+      bq[u] = ldg16(Sw + (jo * 256u + (uint32_t)((((n & 3) + u) & 3) * 64 + 16 * qd)));
+    }
+  }
+  if (wave < 2) {
+    const int h = 8 * wave + (lane >> 3), c = lane & 7;
+    const uint2 pk = qprep8(prep.prepared ? 1 : 0, prep.q, prep.q_stride_row, row, h, c, lane,
+                            prep.w, prep.eps, static_cast<const uint16_t*>(prep.rope),
+                            prep.rope_rows, prep.row_pos);
+    *reinterpret_cast<uint2*>(&q_lds[h * 64 + c * 8]) = pk;
+    if (blockIdx.x == 0) {
+      double vals[8];
+      e4m3x8_f64(pk, vals);
+      double* dst = prep.q64 + ((row * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i * 4] = vals[i];
+    }
+  }
+  __syncthreads();
+  if (!live) return;
+  const Bf16x16 aq = widen16(*reinterpret_cast<const uint4*>(&q_lds[n * 64 + 16 * qd]));
+  float w4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * qd + i];
+  // output lane (n, qd) holds heads 4qd..4qd+3 of column n: the row's result
+  // for group qd in the iteration u with ((n & 3) + u) & 3 == qd
+  const int mu = (qd - (n & 3)) & 3;
+  f32x4 dk = {0.f, 0.f, 0.f, 0.f}, ak = dk;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    f32x4 d, a;
+    dot64(aq, widen16(bq[u]), d, a);
+    const bool mine = (u & 3) == mu;
+    dk = mine ? d : dk;
+    ak = mine ? a : ak;
+    if ((u & 3) == 3) {
+      const int64_t j = cb0 + (u - 3 + mu) * 4 + (n >> 2);
+      const float2 iv = score_interval(dk, ak, w4);
+      if (j < jend) bounds[(row * 4 + qd) * R_cap + j] = iv;
     }
   }
 }
@@ -342,11 +477,13 @@ __global__ __launch_bounds__(256) void score_exact_kernel(
   {
     // q prep of the group's 4 heads (lanes 32..63 repeat lanes 0..31)
     const int hh = (lane >> 3) & 3, c = lane & 7;
-    uint32_t code[8];
-    qprep_lane(qmode, qin, qs, row, 4 * g + hh, c, lane, qw, eps, rope, rope_rows, row_pos, code);
+    const uint2 pk = qprep8(qmode, qin, qs, row, 4 * g + hh, c, lane, qw, eps, rope, rope_rows,
+                            row_pos);
     if (lane < 32) {
+      double vals[8];
+      e4m3x8_f64(pk, vals);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q_lds[g][(8 * c + i) * 4 + hh] = e4m3_f64(code[i]);
+      for (int i = 0; i < 8; ++i) q_lds[g][(8 * c + i) * 4 + hh] = vals[i];
     }
   }
   const double* qg = q_lds[g];
@@ -439,10 +576,17 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
                        reinterpret_cast<float*>(a.bounds), a.prep.arrivals);
     return hipGetLastError();
   }
+  if (a.fused_prep) {
+    const dim3 grid((unsigned)((a.R_cap + SR_CB - 1) / SR_CB), (unsigned)a.rows);
+    hipLaunchKernelGGL(score_rows_kernel, grid, dim3(256), 0, stream, a.w_head, a.w_stride_row,
+                       a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb, a.pos_limit,
+                       a.bounds, a.prep);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));
   hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, a.q8, a.q8_stride_row, a.rows,
                      a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap,
-                     a.ssb, a.pos_limit, a.bounds);
+                     a.ssb, a.pos_limit, a.bounds, a.fused_prep ? 1 : 0, a.prep);
   return hipGetLastError();
 }
 

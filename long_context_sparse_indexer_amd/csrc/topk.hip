@@ -4,30 +4,38 @@
 // keep the top 512 regions by (-score, id), ascending: best score first,
 // equal scores by the smaller region id. Fewer than 512 candidates keep all.
 //
-// Input: the score kernel's exact score per candidate (few rows), which is
-// selected from directly, or its interval [lo, hi] holding the exact score. Per (row, group) and chunk of candidates (one 1024-thread
-// workgroup, everything in LDS; gfx950 gives a workgroup up to 160 KB), from
-// intervals:
-//   1. T = the top 22 bits of the K-th largest lower bound, the rest zero
-//      (K = min(512, candidates)), so T <= that bound;
-//   2. C = the candidates whose upper bound reaches T, kept in id order.
-//      C holds every candidate of the exact top K: each of those has
-//      hi >= exact score >= K-th largest exact score >= K-th largest lo >= T;
-//   3. every member of C is rescored exactly (exact.hpp);
-//   4. the best K of C by (-exact score, id) are selected and sorted.
-// Candidate ranges past 16,384, and batches too small to fill the GPU, are
-// cut into chunks: each chunk keeps its exact best 512, sorted; the last
-// chunk of a (row, group) to finish (an arrival counter per unit, zeroed by
-// the query prep of the same call) merges the chunk lists pairwise.
+// Input: per candidate either the score kernel's exact score (few rows) or an
+// interval [lo, hi] holding the exact score (many rows). One 1024-thread
+// workgroup takes a chunk of up to 16,384 candidates of one (row, group);
+// thread t holds the keys of candidates t, t + 1024, ... in registers
+// (scores mapped to 32-bit keys that order like the scores, -0 taken as +0;
+// absent candidates get key 0, below every real key).
+//   1. threshold: each wave finds, by a bitwise search over ballots, the 32nd
+//      largest of its 64 lanes' largest lower keys; tau = the least of the 16
+//      waves' values. At least 32 lanes of every wave, 512 in all, hold a
+//      lower key >= tau, so at least K = min(512, candidates) lower bounds
+//      reach tau and the K-th largest lower bound is >= tau;
+//   2. survivors C = the candidates whose upper key reaches tau. C holds the
+//      exact top K: each of those has hi >= exact score >= K-th largest exact
+//      score >= K-th largest lo >= tau. Typically |C| is 600..1,000;
+//   3. (intervals) the lower keys >= tau include the K largest, so a radix
+//      select over just those gives T = the top 22 bits of the K-th largest
+//      lower key (T <= that key); C is cut to the candidates whose upper key
+//      reaches T (the same argument holds for T), typically K plus a few, and
+//      every member of C is rescored exactly (exact.hpp);
+//   4. the best K of C by (-exact score, id): a bitonic sort of the
+//      composites (key << 32 | ~id), 512 or 1,024 wide, or, for a larger C
+//      (heavy ties), a radix select followed by a bitonic sort of 512.
+// Candidate ranges past 16,384 are cut into chunks: each chunk keeps its
+// exact best 512, sorted; the last chunk of a (row, group) to finish (an
+// arrival counter per unit, zeroed by the query prep of the same call)
+// merges the chunk lists pairwise.
 //
-// Selecting the best K of N exact keys (scores mapped to 32-bit keys that
-// order like the scores, -0 taken as +0; ties broken by id):
-//   radix select in 3 passes (11, 11, 10 bits) finds the boundary: a key
-//   prefix P under a mask, such that keys above P are all taken and `need`
-//   keys with prefix P are taken in list order (list order is id order); the
-//   passes stop early when the boundary bin is taken whole. The bins are
-//   scanned by all threads at once (two bins each, a block-wide scan). The
-//   selected elements are then sorted by a bitonic network.
+// The radix select (step 4 for a large C) finds the boundary in 3 passes
+// (11, 11, 10 bits): a key prefix P under a mask, such that keys above P are
+// all taken and `need` keys with prefix P are taken in list order; the
+// passes stop early when the boundary bin is taken whole. The bins are
+// scanned by all threads at once (two bins each, a block-wide scan).
 #include "device.hpp"
 #include "exact.hpp"
 #include "launch.hpp"
@@ -38,13 +46,14 @@ constexpr int TK = 512;
 constexpr int TK_THREADS = 1024;
 constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int64_t TK_MAX_N = 16384;
-constexpr int TK_MAX_CHUNKS = 32;
 constexpr int TK_BINS = 2048;
+constexpr int TK_PER = (int)(TK_MAX_N / TK_THREADS);  // keys per thread in registers
+constexpr int TK_SORT = 1024;                           // survivors sorted directly up to this
 
+// 32-bit key ordered like the float (-0 first turned into +0 by adding +0)
 __device__ inline uint32_t ord_key(float s) {
-  uint32_t u = __builtin_bit_cast(uint32_t, s);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __builtin_bit_cast(uint32_t, s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ inline float key_score(uint32_t k) {
   const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
@@ -60,20 +69,44 @@ struct TkShared {
   uint32_t* hist;           // [TK_BINS]
   uint32_t* misc;           // [64]
   unsigned long long* out;  // [TK]
+  unsigned long long* xb;   // [2 * TK_SORT] bitonic exchange
 };
 
 __host__ __device__ inline size_t tk_smem_bytes(int nmax) {
-  return (size_t)TK * 8 + (size_t)(TK_BINS + 64) * 4 + (size_t)nmax * 8;
+  return (size_t)TK * 8 + (size_t)2 * TK_SORT * 8 + (size_t)(TK_BINS + 64) * 4 +
+         (size_t)nmax * 8;
 }
 
 __device__ inline TkShared carve(unsigned char* base, int nmax) {
   TkShared s;
   s.out = reinterpret_cast<unsigned long long*>(base);
-  s.hist = reinterpret_cast<uint32_t*>(base + TK * 8);
+  s.xb = s.out + TK;
+  s.hist = reinterpret_cast<uint32_t*>(s.xb + 2 * TK_SORT);
   s.misc = s.hist + TK_BINS;
   s.keys = s.misc + 64;
   s.ids = reinterpret_cast<int32_t*>(s.keys + nmax);
   return s;
+}
+
+// The k-th largest of the wave's 64 values (1 <= k <= 64), the same in every
+// lane: the largest r with at least k lanes holding a value >= r, built bit
+// by bit from the top.
+__device__ inline uint32_t wave_kth_largest(uint32_t v, int k) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = r | (1u << b);
+    if (__popcll(__ballot(v >= c)) >= k) r = c;
+  }
+  return r;
+}
+
+__device__ inline uint32_t lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+// this lane's bit of a wave-uniform lane mask, without vector instructions
+__device__ inline bool lane_in(unsigned long long m) {
+  return __builtin_amdgcn_inverse_ballot_w64(m);
 }
 
 // exclusive scan of v over the 1024 threads (scratch: misc[0..47]); *total gets the sum
@@ -111,9 +144,9 @@ struct Boundary {
 
 // Radix select over keys[0..N), 1 <= K <= N: keys with (k & mask) > P are
 // the K - need best; `need` more come from the keys with (k & mask) == P.
-// With early = false and passes = 3 all 32 bits are resolved (P is then the
-// K-th best key); fewer passes leave P = the K-th best key's top bits.
-__device__ Boundary radix_boundary(const TkShared& sm, int N, int K, bool early, int passes = 3) {
+// With fewer than 3 passes P holds the K-th best key's top bits only (and
+// the passes do not stop early).
+__device__ Boundary radix_boundary(const TkShared& sm, int N, int K, int passes = 3) {
   const int tid = threadIdx.x;
   uint32_t P = 0, mask = 0, need = (uint32_t)K;
   const int shifts[3] = {21, 10, 0};
@@ -155,7 +188,7 @@ __device__ Boundary radix_boundary(const TkShared& sm, int N, int K, bool early,
     mask |= (nb - 1) << shift;
     need = nneed;
     __syncthreads();
-    if (early && need == cnt) break;
+    if (passes == 3 && need == cnt) break;
   }
   Boundary bd;
   bd.P = P;
@@ -164,89 +197,105 @@ __device__ Boundary radix_boundary(const TkShared& sm, int N, int K, bool early,
   return bd;
 }
 
-__device__ void collect_best(const TkShared& sm, int N, int K, const int32_t* ids, int32_t id_base);
-__device__ void rank_sort(const TkShared& sm, int K);
-
-// Best K of keys[0..N) (ids[i], or id_base + i when ids is null) as sorted
-// composites: sm.out[rank] for rank < K; sm.out[K..TK) = 0. Requires N >= K.
-__device__ void select_sorted(const TkShared& sm, int N, int K, const int32_t* ids,
-                              int32_t id_base) {
+// keys/ids[0..N) -> sm.out[0..K): the best K (any order), N > K >= 1
+__device__ void collect_best(const TkShared& sm, int N, int K) {
   const int tid = threadIdx.x;
-  if (N == K) {
-    // everything is taken
-    for (int i = tid; i < K; i += TK_THREADS) sm.out[i] = compose(sm.keys[i], ids ? ids[i] : id_base + i);
-    __syncthreads();
-  } else {
-    collect_best(sm, N, K, ids, id_base);
-  }
-  rank_sort(sm, K);
-}
-
-// keys[0..N) -> sm.out[0..K): the best K (any order), N > K >= 1 or K == 0
-__device__ void collect_best(const TkShared& sm, int N, int K, const int32_t* ids,
-                             int32_t id_base) {
-  const int tid = threadIdx.x;
-  Boundary bd = {0u, 0u, 0u};
-  if (K > 0) bd = radix_boundary(sm, N, K, true);
+  const Boundary bd = radix_boundary(sm, N, K);
   const int seg = (N + TK_THREADS - 1) / TK_THREADS;
   const int i0 = min(N, tid * seg), i1 = min(N, i0 + seg);
   uint32_t ngt = 0, neq = 0;
-  if (K > 0)
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t m = sm.keys[i] & bd.mask;
-      ngt += m > bd.P;
-      neq += m == bd.P;
-    }
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t m = sm.keys[i] & bd.mask;
+    ngt += m > bd.P;
+    neq += m == bd.P;
+  }
   uint32_t tot;
   uint32_t gt_off = block_excl_scan(ngt, sm.misc, &tot);
   uint32_t eq_off = block_excl_scan(neq, sm.misc, &tot);
   const uint32_t eq_base = (uint32_t)K - bd.need;
-  if (K > 0)
-    for (int i = i0; i < i1; ++i) {
-      const uint32_t k = sm.keys[i];
-      const uint32_t m = k & bd.mask;
-      if (m < bd.P) continue;
-      const int32_t id = ids ? ids[i] : id_base + i;
-      if (m > bd.P) {
-        sm.out[gt_off++] = compose(k, id);
-      } else {
-        if (eq_off < bd.need) sm.out[eq_base + eq_off] = compose(k, id);
-        ++eq_off;
-      }
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t k = sm.keys[i];
+    const uint32_t m = k & bd.mask;
+    if (m < bd.P) continue;
+    if (m > bd.P) {
+      sm.out[gt_off++] = compose(k, sm.ids[i]);
+    } else {
+      if (eq_off < bd.need) sm.out[eq_base + eq_off] = compose(k, sm.ids[i]);
+      ++eq_off;
     }
+  }
   __syncthreads();
 }
 
-// Bitonic network on 512 composites held one per thread by a group of 512
-// threads (i = index in the group; groups are whole waves). Stage (k, j):
-// compare with element i ^ j, keep the larger where the k-block runs
-// descending and i is the lower index of the pair (or neither), else the
-// smaller. Partners closer than 64 are in the wave (DPP or a lane permute);
-// farther ones go through xb (the group's 2 x 512 slots, alternated so one
-// barrier per stage suffices). Every thread of the block runs the stages
-// (the barriers); inactive ones exchange nothing.
+// ---------------------------------------------------------------------------
+// Bitonic network, one composite per thread; the thread's index i in the
+// sorted group is its thread index within the group (groups are whole
+// waves). Stage (K, J): compare with element i ^ J and keep the larger where
+// the K-block runs descending and i is the lower index of the pair (or
+// neither), else the smaller. Which lanes keep the larger is a lane mask
+// known at compile time (or per wave once K >= 64), so a stage is a 64-bit
+// compare into a lane mask, a scalar xor, and two selects. Partners closer
+// than 64 are in the wave: DPP for 1, 2, 8, a swizzle for 4, 16, a lane
+// permute for 32; farther ones go through xb (2 x stride slots, alternated
+// so one barrier per stage suffices). Every thread of the block runs the
+// stages (the barriers); inactive waves exchange nothing.
+// ---------------------------------------------------------------------------
 struct BitonicCtx {
-  int i, lane;
-  unsigned long long* xb;
+  int i;                   // index in the group
+  int iw;                  // index of the wave's lane 0 in the group (wave-uniform)
+  unsigned long long* xb;  // 2 x stride slots
+  int stride;
   bool active;
   int flip;
 };
 
+__host__ __device__ constexpr unsigned long long lanes_agree(int J, int K) {
+  unsigned long long m = 0;
+  for (int l = 0; l < 64; ++l)
+    if (((l & J) == 0) == ((l & K) == 0)) m |= 1ull << l;
+  return m;
+}
+__host__ __device__ constexpr unsigned long long lanes_clear(int J) {
+  unsigned long long m = 0;
+  for (int l = 0; l < 64; ++l)
+    if ((l & J) == 0) m |= 1ull << l;
+  return m;
+}
+
+template <int J>
+__device__ inline uint32_t lane_xor(uint32_t v) {
+  if constexpr (J == 1) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (J == 2) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (J == 4) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (4 << 10));    // xor 4
+  } else if constexpr (J == 8) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true); // row_ror:8
+  } else if constexpr (J == 16) {
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (16 << 10));   // xor 16
+  } else {
+    static_assert(J == 32, "lane_xor: J must be a power of two below 64");
+    return (uint32_t)__shfl_xor((int)v, 32, 64);
+  }
+}
+
 template <int K, int J>
 __device__ inline unsigned long long bitonic_stage(unsigned long long v, BitonicCtx& c) {
-  unsigned long long p;
+  unsigned long long p, tm;  // partner, lanes that keep the larger
   if constexpr (J >= 64) {
-    unsigned long long* b = c.xb + 512 * c.flip;
+    unsigned long long* b = c.xb + c.stride * c.flip;
     c.flip ^= 1;
     if (c.active) b[c.i] = v;
     __syncthreads();
     p = c.active ? b[c.i ^ J] : 0ull;
+    tm = (((c.iw & J) == 0) == ((c.iw & K) == 0)) ? ~0ull : 0ull;
   } else {
-    p = lane_xor64<J>(v, c.lane);
+    p = ((unsigned long long)lane_xor<J>((uint32_t)(v >> 32)) << 32) | lane_xor<J>((uint32_t)v);
+    if constexpr (K < 64) tm = lanes_agree(J, K);
+    else tm = ((c.iw & K) == 0) ? lanes_clear(J) : ~lanes_clear(J);
   }
-  const bool desc = (c.i & K) == 0;
-  const bool lower = (c.i & J) == 0;
-  return (desc == lower) ? (v > p ? v : p) : (v < p ? v : p);
+  return lane_in(~(__ballot(v > p) ^ tm)) ? v : p;
 }
 
 // stages J, J/2, ..., 1 of merge size K
@@ -274,22 +323,26 @@ struct BitonicSort<1> {
   __device__ static inline unsigned long long run(unsigned long long v, BitonicCtx&) { return v; }
 };
 
-// sm.out[0..K) (distinct composites, any order) -> sorted best first;
-// sm.out[K..TK) = 0. Threads 0..511 sort, with the histogram as exchange space.
-__device__ void rank_sort(const TkShared& sm, int K) {
-  const int tid = threadIdx.x;
+__device__ inline BitonicCtx bitonic_ctx(int i, unsigned long long* xb, int stride, bool active) {
   BitonicCtx c;
-  c.i = tid & (TK - 1);
-  c.lane = tid & 63;
-  c.active = tid < TK;
-  c.xb = reinterpret_cast<unsigned long long*>(sm.hist);  // 2 x 512 slots
+  c.i = i;
+  c.iw = __builtin_amdgcn_readfirstlane(i & ~63);
+  c.xb = xb;
+  c.stride = stride;
+  c.active = active;
   c.flip = 0;
-  unsigned long long v = (c.active && c.i < K) ? sm.out[c.i] : 0ull;
-  v = BitonicSort<TK>::run(v, c);
-  __syncthreads();
-  if (c.active) sm.out[c.i] = v;
-  __syncthreads();
+  return c;
 }
+
+// Composites v (one per thread of the first NS threads, 0 elsewhere) sorted
+// best first: thread t < NS returns rank t.
+template <int NS>
+__device__ inline unsigned long long sort_desc(unsigned long long v, const TkShared& sm) {
+  BitonicCtx c = bitonic_ctx((int)threadIdx.x, sm.xb, NS, (int)threadIdx.x < NS);
+  return BitonicSort<NS>::run(v, c);
+}
+
+// ---------------------------------------------------------------------------
 
 __device__ void merge_lists(const unsigned long long* __restrict__ src, int nchunks, int64_t ncand,
                             int64_t unit, unsigned char* smem, int32_t* __restrict__ sel_ids,
@@ -305,29 +358,63 @@ __device__ inline void unit_row(const int32_t* row_seq, const int64_t* row_pos, 
   *ncand = ok ? (p >> 3) : 0;
 }
 
-__device__ inline void write_final(const TkShared& sm, int K, int64_t unit, int32_t* sel_ids,
-                                   float* sel_scores) {
-  for (int i = threadIdx.x; i < TK; i += TK_THREADS) {
-    const unsigned long long c = sm.out[i];
-    const bool have = i < K;
-    sel_ids[unit * TK + i] = have ? (int32_t)(~(uint32_t)c) : -1;
-    if (sel_scores) sel_scores[unit * TK + i] = have ? key_score((uint32_t)(c >> 32)) : 0.0f;
-  }
+// thread t < 512 holds the rank-t composite v (rank < K), written as id and score
+__device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int32_t* sel_ids,
+                                  float* sel_scores) {
+  const int t = threadIdx.x;
+  if (t >= TK) return;
+  const bool have = t < K;
+  sel_ids[unit * TK + t] = have ? (int32_t)(~(uint32_t)v) : -1;
+  if (sel_scores) sel_scores[unit * TK + t] = have ? key_score((uint32_t)(v >> 32)) : 0.0f;
 }
 
-// One chunk of a (row, group)'s candidates: interval filter, exact rescoring,
-// exact selection. mode 0: the whole range, final output; mode 1: partial list.
+// Appends the candidates tid + 1024 k whose key reaches t to sm.ids (and,
+// with keys, the key to sm.keys), per wave in ballot order; misc[56] holds
+// the count, zero on entry. Returns the total (a barrier comes first).
+__device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_PER], uint32_t t,
+                                   int64_t j0, bool keys) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  unsigned long long msk[TK_PER];
+  uint32_t wt = 0;
+#pragma unroll
+  for (int k = 0; k < TK_PER; ++k) {
+    msk[k] = __ballot(key[k] >= t);
+    wt += (uint32_t)__popcll(msk[k]);
+  }
+  uint32_t base = 0;
+  if (lane == 0 && wt) base = atomicAdd(&sm.misc[56], wt);
+  base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+  for (int k = 0; k < TK_PER; ++k) {
+    if (msk[k]) {
+      if (lane_in(msk[k])) {
+        const uint32_t pos = base + lanes_below(msk[k]);
+        sm.ids[pos] = (int32_t)(j0 + tid + TK_THREADS * k);
+        if (keys) sm.keys[pos] = key[k];
+      }
+      base += (uint32_t)__popcll(msk[k]);
+    }
+  }
+  __syncthreads();
+  return (int)sm.misc[56];
+}
+
+// One chunk of a (row, group)'s candidates: threshold, survivors, exact
+// rescoring (intervals), exact selection. mode 0: the whole range, final
+// output; mode 1: partial list, merged by the unit's last block.
+template <bool EXACT>
 __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
-    int mode, int exact, const float2* __restrict__ bounds, int64_t R_cap, const int32_t* __restrict__ row_seq,
-    const int64_t* __restrict__ row_pos, int64_t B, int64_t pos_limit,
-    const double* __restrict__ q64, const float* __restrict__ w_head, int64_t w_stride,
-    const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
+    int mode, const float2* __restrict__ bounds, int64_t R_cap,
+    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int64_t B,
+    int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
+    int64_t w_stride, const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
     unsigned long long* __restrict__ partial, unsigned* __restrict__ arrivals,
     int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t unit = blockIdx.x;
   const int c = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TkShared sm = carve(smem, (int)chunk);
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
@@ -338,56 +425,81 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   int N = 0;
   if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
   const int K = N < TK ? N : TK;
-  const float2* bsrc = bounds + unit * R_cap + j0;
-  int M = 0;
-  const int32_t* sel_from = sm.ids;  // ids of keys[0..M), or j0 + index when exact
-  int32_t id_base = 0;
-  if (exact) {
-    // exact scores: select straight from them
-    const float* ssrc = reinterpret_cast<const float*>(bounds) + unit * R_cap + j0;
-    for (int i = tid; i < N; i += TK_THREADS) sm.keys[i] = ord_key(ssrc[i]);
-    __syncthreads();
-    M = N;
-    sel_from = nullptr;
-    id_base = (int32_t)j0;
-  } else if (K > 0) {
-    // 1. K-th largest lower bound (upper bounds parked in ids[] meanwhile)
-    for (int i = tid; i < N; i += TK_THREADS) {
-      const float2 b = bsrc[i];
-      sm.keys[i] = ord_key(b.x);
-      sm.ids[i] = (int32_t)ord_key(b.y);
-    }
-    __syncthreads();
-    // two passes fix the top 22 bits of the K-th largest lower bound; T (those
-    // bits, the rest zero) is at most that bound, which is all the filter needs
-    const Boundary bd = radix_boundary(sm, N, K, false, 2);
-    const uint32_t T = bd.P;
-    // 2. candidates whose upper bound reaches T, in id order: each thread
-    //    takes its segment's upper bounds into registers, the scan orders the
-    //    writes (its barriers separate every read from every write)
-    const int seg = (N + TK_THREADS - 1) / TK_THREADS;  // <= TK_MAX_N / TK_THREADS
-    const int i0 = min(N, tid * seg), i1 = min(N, i0 + seg);
-    uint32_t flags = 0, cnt = 0;
+  double qv = 0.0;  // (intervals) this thread's value of the exact query, loaded early
+  if constexpr (!EXACT) {
+    if (tid < 256) qv = q64[(row * 4 + g) * 256 + tid];
+  }
+
+  // keys of candidates tid + 1024 k in registers, and the largest lower key
+  // of the thread. All loads are issued before any is used (a lane past the
+  // end loads the last candidate again).
+  float2 raw[TK_PER];
 #pragma unroll
-    for (int k = 0; k < (int)(TK_MAX_N / TK_THREADS); ++k) {
-      const int i = i0 + k;
-      if (i < i1 && (uint32_t)sm.ids[i] >= T) {
-        flags |= 1u << k;
-        ++cnt;
+  for (int k = 0; k < TK_PER; ++k) {
+    raw[k] = make_float2(0.f, 0.f);
+    if (TK_THREADS * k < N) {
+      const int i = min(tid + TK_THREADS * k, N - 1);
+      if constexpr (EXACT) {
+        const float s = reinterpret_cast<const float*>(bounds)[unit * R_cap + j0 + i];
+        raw[k] = make_float2(s, s);
+      } else {
+        raw[k] = bounds[unit * R_cap + j0 + i];
       }
     }
-    uint32_t total;
-    uint32_t off = block_excl_scan(cnt, sm.misc, &total);
+  }
+  uint32_t kh[TK_PER];
+  uint32_t mx = 0;
 #pragma unroll
-    for (int k = 0; k < (int)(TK_MAX_N / TK_THREADS); ++k)
-      if ((flags >> k) & 1u) sm.ids[off++] = (int32_t)(j0 + i0 + k);
-    M = (int)total;
+  for (int k = 0; k < TK_PER; ++k) {
+    const bool have = tid + TK_THREADS * k < N;
+    const uint32_t lo = have ? ord_key(raw[k].x) : 0u;
+    kh[k] = EXACT ? lo : (have ? ord_key(raw[k].y) : 0u);
+    mx = lo > mx ? lo : mx;
+  }
+  // 1. tau = least over the waves of the wave's 32nd largest thread maximum
+  //    (at least 1: absent candidates, key 0, never survive)
+  const uint32_t tw = wave_kth_largest(mx, TK / TK_WAVES);
+  if (lane == 0) sm.misc[wave] = tw;
+  if (tid == 0) sm.misc[56] = 0u;
+  __syncthreads();
+  uint32_t tau = 1u;
+  {
+    uint32_t t = sm.misc[0];
+#pragma unroll
+    for (int w = 1; w < TK_WAVES; ++w) t = min(t, sm.misc[w]);
+    tau = t > 1u ? t : 1u;
+  }
+  // 2. survivors: upper key >= tau (intervals: first the lower keys >= tau,
+  //    see 3.), appended per wave (their order is free: the selection sorts
+  //    by (key, id))
+  uint32_t kl[TK_PER];
+  if constexpr (!EXACT) {
+#pragma unroll
+    for (int k = 0; k < TK_PER; ++k) {
+      const bool have = tid + TK_THREADS * k < N;
+      kl[k] = have ? ord_key(raw[k].x) : 0u;
+    }
+  }
+  int M;
+  if constexpr (EXACT) {
+    M = compact_keys(sm, kh, tau, j0, true);
+  } else {
+    M = compact_keys(sm, kl, tau, j0, true);
+    // 3. T from the lower keys >= tau, then the survivors by upper key >= T
+    uint32_t T = 1u;
+    if (K > 0) {
+      const Boundary bd = radix_boundary(sm, M, K, 2);
+      T = bd.P > 1u ? bd.P : 1u;
+    }
+    if (tid == 0) sm.misc[56] = 0u;
     __syncthreads();
+    M = compact_keys(sm, kh, T, j0, false);
+  }
+  if constexpr (!EXACT) {
     // 3. exact scores of the survivors: two threads per candidate (dims
     //    0..31 and 32..63); partial fp64 sums are exact, so is their sum
-    double* q_lds = reinterpret_cast<double*>(sm.hist);  // 256 doubles (the histogram is free now)
-    const double* qg = q64 + (row * 4 + g) * 256;
-    for (int i = tid; i < 256; i += TK_THREADS) q_lds[i] = qg[i];
+    double* q_lds = reinterpret_cast<double*>(sm.hist);  // 256 doubles
+    if (tid < 256) q_lds[tid] = qv;
     __syncthreads();
     const uint8_t* Sg = S + (int64_t)seq * ssb + g * 64;
     float w4[4];
@@ -400,21 +512,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
       if (m < M) exact_half_dots(Sg + (int64_t)sm.ids[m] * 256 + 32 * half, q_lds + 128 * half, a);
 #pragma unroll
       for (int h = 0; h < 4; ++h) a[h] += __shfl_xor(a[h], 1, 64);
-      if (m < M && half == 0) sm.keys[m] = ord_key(group_score4((float)a[0], (float)a[1], (float)a[2], (float)a[3], w4));
+      if (m < M && half == 0)
+        sm.keys[m] = ord_key(group_score4((float)a[0], (float)a[1], (float)a[2], (float)a[3], w4));
     }
     __syncthreads();
   }
-  // 4. exact best K of the survivors
+  // 4. exact best K of the survivors (M >= K), sorted: thread t < 512 gets rank t
+  unsigned long long v;
+  if (M <= TK) {
+    v = sort_desc<TK>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
+  } else if (M <= TK_SORT) {
+    v = sort_desc<TK_SORT>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
+  } else {
+    collect_best(sm, M, K);
+    v = sort_desc<TK>(tid < K ? sm.out[tid] : 0ull, sm);
+  }
   if (mode == 0) {
-    select_sorted(sm, M, K, sel_from, id_base);
-    write_final(sm, K, unit, sel_ids, sel_scores);
+    write_rank(v, K, unit, sel_ids, sel_scores);
     return;
   }
   // chunk list out: its best K, sorted, zero-padded to 512; the unit's last
   // block to arrive merges all of them
-  select_sorted(sm, M, K, sel_from, id_base);
   unsigned long long* dst = partial + (unit * nchunks + c) * TK;
-  for (int i = tid; i < TK; i += TK_THREADS) dst[i] = sm.out[i];
+  if (tid < TK) dst[tid] = tid < K ? v : 0ull;
   __shared__ int sh_last;
   if (!block_arrive_last(&arrivals[unit], (unsigned)nchunks, &sh_last)) return;
   merge_lists(partial + unit * (int64_t)nchunks * TK, nchunks, ncand, unit, smem, sel_ids,
@@ -437,11 +557,7 @@ __device__ void merge_lists(const unsigned long long* __restrict__ src, int nchu
   for (int t = tid; t < nchunks * TK; t += TK_THREADS) lists[t] = src[t];
   __syncthreads();
   int nl = nchunks;
-  BitonicCtx bc;
-  bc.i = i;
-  bc.lane = tid & 63;
-  bc.xb = xb + grp * 2 * TK;
-  bc.flip = 0;
+  BitonicCtx bc = bitonic_ctx(i, xb + grp * 2 * TK, TK, true);
   while (nl > 1) {
     const int npairs = nl >> 1;
     for (int p0 = 0; p0 < npairs; p0 += 2) {
@@ -466,21 +582,23 @@ __device__ void merge_lists(const unsigned long long* __restrict__ src, int nchu
     nl = npairs + (nl & 1);
   }
   const int K = ncand < TK ? (int)ncand : TK;
-  for (int t = tid; t < TK; t += TK_THREADS) {
-    const unsigned long long c = lists[t];
-    const bool have = t < K;
-    sel_ids[unit * TK + t] = have ? (int32_t)(~(uint32_t)c) : -1;
-    if (sel_scores) sel_scores[unit * TK + t] = have ? key_score((uint32_t)(c >> 32)) : 0.0f;
-  }
+  if (tid < TK) write_rank(lists[tid], K, unit, sel_ids, sel_scores);
 }
+
+// chunks of at least this many candidates when a batch is cut further to
+// fill the GPU
+#ifndef S5_TOPK_MIN_CHUNK
+#define S5_TOPK_MIN_CHUNK 16384
+#endif
 
 TopkPlan topk_plan(int32_t rows, int64_t R_cap) {
   // at most 16,384 candidates per chunk; a batch too small to fill the GPU
-  // (rows * 4 units) is cut further, into chunks of at least 2,048, up to 16
+  // (rows * 4 units) is cut further, into chunks of at least
+  // S5_TOPK_MIN_CHUNK, up to 16
   const int64_t units = (int64_t)rows * 4;
   const int64_t nmin = (R_cap + TK_MAX_N - 1) / TK_MAX_N;
   int64_t want = units > 0 ? (256 + units - 1) / units : 1;
-  const int64_t by_size = (R_cap + 2047) / 2048;
+  const int64_t by_size = (R_cap + S5_TOPK_MIN_CHUNK - 1) / S5_TOPK_MIN_CHUNK;
   if (want > by_size) want = by_size;
   if (want > 16) want = 16;
   int64_t n = want > nmin ? want : nmin;
@@ -508,14 +626,21 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   size_t sm = tk_smem_bytes((int)p.chunk);
   const size_t sm_merge = (size_t)(p.nchunks + 4) * TK * sizeof(unsigned long long);
   if (p.nchunks > 1 && sm_merge > sm) sm = sm_merge;
-  hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+  const void* fn = a.exact ? (const void*)topk_chunk_kernel<true> : (const void*)topk_chunk_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const int mode = p.nchunks == 1 ? 0 : 1;
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3(units, (unsigned)p.nchunks), dim3(TK_THREADS), sm,
-                     stream, mode, a.exact ? 1 : 0, a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit,
-                     a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks,
-                     a.partial, a.arrivals, a.sel_ids, a.sel_scores);
+  const dim3 grid(units, (unsigned)p.nchunks);
+  if (a.exact)
+    hipLaunchKernelGGL(topk_chunk_kernel<true>, grid, dim3(TK_THREADS), sm, stream, mode,
+                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit, a.q64,
+                       a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks, a.partial,
+                       a.arrivals, a.sel_ids, a.sel_scores);
+  else
+    hipLaunchKernelGGL(topk_chunk_kernel<false>, grid, dim3(TK_THREADS), sm, stream, mode,
+                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit, a.q64,
+                       a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks, a.partial,
+                       a.arrivals, a.sel_ids, a.sel_scores);
   return hipGetLastError();
 }
 

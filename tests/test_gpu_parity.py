@@ -184,8 +184,8 @@ def test_fp8_products_exhaustive_through_scores():
 def _scores_view(ws, rows, R_cap, exact):
     """The candidate scores inside step5_index_score_topk's workspace
     (white-box: e4m3 q [rows*1024 B], fp64 q [rows*8192 B], then per (row,
-    group, candidate) the exact score as float, with up to 64 rows, or else an
-    interval as float2; each part 256-byte aligned)."""
+    group, candidate) the exact score as float, or an interval as float2;
+    each part 256-byte aligned)."""
     up = lambda x: (x + 255) // 256 * 256
     off = up(up(rows * 1024) + rows * 8192)
     k = 1 if exact else 2
@@ -198,28 +198,36 @@ def _scores_view(ws, rows, R_cap, exact):
     ("decode8_ctx3000", [0, 33, 71], dict(rows=72, batch=72)),
     ("prefill2048_ctx32k", [0, 1, 1000, 2047], {})])
 def test_scores_exact_or_bracketed(name, rows, kw):
-    """Up to 64 rows are scored exactly: the scores must equal the oracle's
-    bit for bit. More rows get matrix-core scores with intervals derived from
-    an error bound of fp32 accumulation: every interval must hold the exact
-    score (72 decode rows of different sequences, and a prefill chunk of one
-    sequence, cover both tilings)."""
+    """The scores the selection pass starts from: either exact, which must
+    equal the oracle's bit for bit, or matrix-core scores with intervals
+    derived from an error bound of fp32 accumulation, every one of which must
+    hold the exact score. Which of the two a call uses is the library's choice
+    for small batches (16 decode rows); more than 64 rows always get intervals
+    (72 decode rows of different sequences, and a prefill chunk of one
+    sequence, cover both matrix-core tilings)."""
     import long_context_sparse_indexer_amd as s5
     d = _case(name, 23, DEV, with_kv=False, **kw)
     S = P.gpu_summary(d)
     R_cap = S.shape[1]
     nrows = d["rows"]
-    exact = nrows <= 64
     nb = s5.step5_index_score_topk_workspace(nrows, R_cap)
     ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
     ids = torch.empty((nrows, 4, 512), dtype=torch.int32, device=DEV)
     s5.step5_index_score_topk(d["q_idx"], d["w_head"], d["row_seq"], d["row_pos"], S, ids,
                               q_norm_w=d["q_norm_w"], q_eps=P.EPS, rope=d["rope"], workspace=ws)
     torch.cuda.synchronize()
-    got = _scores_view(ws, nrows, R_cap, exact).cpu().numpy()[rows]
     seqs = sorted({int(d["row_seq"][r]) for r in rows})
     O = np.concatenate([P.oracle_summary({**d, "k_idx": d["k_idx"][s:s + 1],
                                           "z_idx": d["z_idx"][s:s + 1]}) for s in seqs])
     osc = P.oracle_scores(d, O, rows, {s: i for i, s in enumerate(seqs)})
+    as_exact = _scores_view(ws, nrows, R_cap, True).cpu().numpy()[rows]
+    nc0 = int(d["row_pos"][rows[0]]) // 8
+    # an interval workspace read as plain floats cannot equal the exact scores
+    exact = np.array_equal(as_exact[0, :, :nc0, 0], osc[0, :, :nc0])
+    P.say(f"  scores in the workspace: {'exact' if exact else 'intervals'}")
+    if nrows > 64:
+        assert not exact
+    got = as_exact if exact else _scores_view(ws, nrows, R_cap, False).cpu().numpy()[rows]
     worst = 0.0
     for i, r in enumerate(rows):
         nc = int(d["row_pos"][r]) // 8

@@ -10,22 +10,26 @@
 // thread t holds the keys of candidates t, t + 1024, ... in registers
 // (scores mapped to 32-bit keys that order like the scores, -0 taken as +0;
 // absent candidates get key 0, below every real key).
-//   1. threshold: each wave finds, by a bitwise search over ballots, the 32nd
-//      largest of its 64 lanes' largest lower keys; tau = the least of the 16
-//      waves' values. At least 32 lanes of every wave, 512 in all, hold a
-//      lower key >= tau, so at least K = min(512, candidates) lower bounds
-//      reach tau and the K-th largest lower bound is >= tau;
+//   1. threshold: a thread's keys form 4 groups (keys k, k + 4, k + 8,
+//      k + 12); each wave finds, by a bitwise search over ballots, a lower
+//      bound of the 32nd largest of its 256 group maxima of the lower keys
+//      (its top 16 bits); tau = the least of the 16 waves' values. At least
+//      32 groups of every wave, 512 in all, hold a lower key >= tau, so at
+//      least K = min(512, candidates) lower bounds reach tau and the K-th
+//      largest lower bound is >= tau;
 //   2. survivors C = the candidates whose upper key reaches tau. C holds the
 //      exact top K: each of those has hi >= exact score >= K-th largest exact
 //      score >= K-th largest lo >= tau. Typically |C| is 600..1,000;
-//   3. (intervals) the lower keys >= tau include the K largest, so a radix
-//      select over just those gives T = the top 22 bits of the K-th largest
-//      lower key (T <= that key); C is cut to the candidates whose upper key
-//      reaches T (the same argument holds for T), typically K plus a few, and
-//      every member of C is rescored exactly (exact.hpp);
+//   3. (intervals) every member of C is rescored exactly (exact.hpp), one
+//      thread per candidate, the query read through scalar loads (the same
+//      value in every lane);
 //   4. the best K of C by (-exact score, id): a bitonic sort of the
 //      composites (key << 32 | ~id), 512 or 1,024 wide, or, for a larger C
 //      (heavy ties), a radix select followed by a bitonic sort of 512.
+// A C too large to sort directly (heavy ties) is first cut: the lower keys
+// >= tau include the K largest, so a radix select over just those gives T =
+// the top 22 bits of the K-th largest lower key (T <= that key), and C is
+// cut to the candidates whose upper key reaches T (the same argument holds).
 // Candidate ranges past 16,384 are cut into chunks: each chunk keeps its
 // exact best 512, sorted; the last chunk of a (row, group) to finish (an
 // arrival counter per unit, zeroed by the query prep of the same call)
@@ -88,15 +92,17 @@ __device__ inline TkShared carve(unsigned char* base, int nmax) {
   return s;
 }
 
-// The k-th largest of the wave's 64 values (1 <= k <= 64), the same in every
-// lane: the largest r with at least k lanes holding a value >= r, built bit
-// by bit from the top.
-__device__ inline uint32_t wave_kth_largest(uint32_t v, int k) {
+// A lower bound of the k-th largest of the wave's 4 x 64 values (1 <= k <=
+// 256), the same in every lane: the largest r with at least k values >= r,
+// built bit by bit from the top over the 16 high bits (the low 16 stay 0).
+__device__ inline uint32_t wave_kth_largest4(const uint32_t (&v)[4], int k) {
   uint32_t r = 0;
 #pragma unroll
-  for (int b = 31; b >= 0; --b) {
+  for (int b = 31; b >= 16; --b) {
     const uint32_t c = r | (1u << b);
-    if (__popcll(__ballot(v >= c)) >= k) r = c;
+    const int cnt = __popcll(__ballot(v[0] >= c)) + __popcll(__ballot(v[1] >= c)) +
+                    __popcll(__ballot(v[2] >= c)) + __popcll(__ballot(v[3] >= c));
+    if (cnt >= k) r = c;
   }
   return r;
 }
@@ -425,10 +431,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   int N = 0;
   if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
   const int K = N < TK ? N : TK;
-  double qv = 0.0;  // (intervals) this thread's value of the exact query, loaded early
-  if constexpr (!EXACT) {
-    if (tid < 256) qv = q64[(row * 4 + g) * 256 + tid];
-  }
 
   // keys of candidates tid + 1024 k in registers, and the largest lower key
   // of the thread. All loads are issued before any is used (a lane past the
@@ -448,17 +450,17 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     }
   }
   uint32_t kh[TK_PER];
-  uint32_t mx = 0;
+  uint32_t mx[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int k = 0; k < TK_PER; ++k) {
     const bool have = tid + TK_THREADS * k < N;
     const uint32_t lo = have ? ord_key(raw[k].x) : 0u;
     kh[k] = EXACT ? lo : (have ? ord_key(raw[k].y) : 0u);
-    mx = lo > mx ? lo : mx;
+    mx[k & 3] = lo > mx[k & 3] ? lo : mx[k & 3];
   }
-  // 1. tau = least over the waves of the wave's 32nd largest thread maximum
+  // 1. tau = least over the waves of the wave's 32nd largest group maximum
   //    (at least 1: absent candidates, key 0, never survive)
-  const uint32_t tw = wave_kth_largest(mx, TK / TK_WAVES);
+  const uint32_t tw = wave_kth_largest4(mx, TK / TK_WAVES);
   if (lane == 0) sm.misc[wave] = tw;
   if (tid == 0) sm.misc[56] = 0u;
   __syncthreads();
@@ -469,51 +471,38 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     for (int w = 1; w < TK_WAVES; ++w) t = min(t, sm.misc[w]);
     tau = t > 1u ? t : 1u;
   }
-  // 2. survivors: upper key >= tau (intervals: first the lower keys >= tau,
-  //    see 3.), appended per wave (their order is free: the selection sorts
-  //    by (key, id))
-  uint32_t kl[TK_PER];
+  // 2. survivors: upper key >= tau, appended per wave (their order is free:
+  //    the selection sorts by (key, id))
+  int M = compact_keys(sm, kh, tau, j0, EXACT);
   if constexpr (!EXACT) {
+    if (M > TK_SORT) {
+      // too many to sort directly: cut by T from the lower keys >= tau
+      uint32_t kl[TK_PER];
 #pragma unroll
-    for (int k = 0; k < TK_PER; ++k) {
-      const bool have = tid + TK_THREADS * k < N;
-      kl[k] = have ? ord_key(raw[k].x) : 0u;
-    }
-  }
-  int M;
-  if constexpr (EXACT) {
-    M = compact_keys(sm, kh, tau, j0, true);
-  } else {
-    M = compact_keys(sm, kl, tau, j0, true);
-    // 3. T from the lower keys >= tau, then the survivors by upper key >= T
-    uint32_t T = 1u;
-    if (K > 0) {
+      for (int k = 0; k < TK_PER; ++k) {
+        const bool have = tid + TK_THREADS * k < N;
+        kl[k] = have ? ord_key(raw[k].x) : 0u;
+      }
+      if (tid == 0) sm.misc[56] = 0u;
+      __syncthreads();
+      M = compact_keys(sm, kl, tau, j0, true);
       const Boundary bd = radix_boundary(sm, M, K, 2);
-      T = bd.P > 1u ? bd.P : 1u;
+      const uint32_t T = bd.P > 1u ? bd.P : 1u;
+      if (tid == 0) sm.misc[56] = 0u;
+      __syncthreads();
+      M = compact_keys(sm, kh, T, j0, false);
     }
-    if (tid == 0) sm.misc[56] = 0u;
-    __syncthreads();
-    M = compact_keys(sm, kh, T, j0, false);
-  }
-  if constexpr (!EXACT) {
-    // 3. exact scores of the survivors: two threads per candidate (dims
-    //    0..31 and 32..63); partial fp64 sums are exact, so is their sum
-    double* q_lds = reinterpret_cast<double*>(sm.hist);  // 256 doubles
-    if (tid < 256) q_lds[tid] = qv;
-    __syncthreads();
+    // 3. exact scores of the survivors, one thread per candidate; the query
+    //    for (row, group), [64 dims][4 heads], is the same in every lane
+    const double* qg = q64 + (row * 4 + g) * 256;
     const uint8_t* Sg = S + (int64_t)seq * ssb + g * 64;
     float w4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
-    const int half = tid & 1;
-    for (int m0 = 0; m0 < M; m0 += TK_THREADS / 2) {
-      const int m = m0 + (tid >> 1);
-      double a[4] = {0.0, 0.0, 0.0, 0.0};
-      if (m < M) exact_half_dots(Sg + (int64_t)sm.ids[m] * 256 + 32 * half, q_lds + 128 * half, a);
-#pragma unroll
-      for (int h = 0; h < 4; ++h) a[h] += __shfl_xor(a[h], 1, 64);
-      if (m < M && half == 0)
-        sm.keys[m] = ord_key(group_score4((float)a[0], (float)a[1], (float)a[2], (float)a[3], w4));
+    for (int m = tid; m < M; m += TK_THREADS) {
+      const uint8_t* sv = Sg + (int64_t)sm.ids[m] * 256;
+      const uint4 raw[4] = {ldg16(sv), ldg16(sv + 16), ldg16(sv + 32), ldg16(sv + 48)};
+      sm.keys[m] = ord_key(exact_group_score_sq(raw, qg, w4));
     }
     __syncthreads();
   }

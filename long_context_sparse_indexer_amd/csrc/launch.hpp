@@ -57,8 +57,8 @@ struct ScoreArgs {
   float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score, or (exact)
                           // the exact scores as float [rows, 4, R_cap]
 };
-// Rows up to S5_EXACT_MAX_ROWS are scored exactly, each candidate by one
-// lane; more rows get intervals from the matrix cores and exact rescoring of
+// Rows up to S5_EXACT_MAX_ROWS are scored exactly on the fp64 matrix cores;
+// more rows get intervals from the matrix cores and exact rescoring of
 // the few candidates near each selection boundary. Up to S5_FUSED_PREP_ROWS
 // rows the query prep runs inside the score kernel (no separate launch).
 #ifndef S5_EXACT_MAX_ROWS

@@ -27,6 +27,10 @@
 // intervals to find which candidates can reach the top 512 and rescores only
 // those exactly (exact.hpp), so exactness never rests on the accumulator.
 //
+// With few rows (decode) the intervals cost more than they save: there every
+// candidate is scored exactly on the fp64 matrix cores instead
+// (score_exact_mfma_kernel) and the selection pass reads plain scores.
+//
 // Operand lanes: lane l = 16q + n holds row/column n and the 16 contiguous
 // e4m3 bytes 16q..16q+15 of the 64-byte vector, widened to 16 bf16; the first
 // MFMA takes elements 0..7 of each lane's slice and the second 8..15,
@@ -438,142 +442,126 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 }
 
 // ---------------------------------------------------------------------------
-// exact scores: one block per (row, 64 * SX_NB candidates); wave g takes KV
-// group g: it preps the row's query for the group's 4 heads (the same steps
-// as qprep_kernel) into LDS as exact fp64, a value every lane reads alike;
-// each lane scores one candidate per 64-candidate batch with fp64 fused
-// multiply-adds, exact at every step (exact.hpp). The block loads its candidates' 256-byte rows with contiguous
-// 16-byte loads (all batches in flight at once) and hands each wave its
-// group's 64 bytes per candidate through LDS (rows padded to 272 bytes, so
-// the per-lane reads do not collide in the banks).
+// exact scores on the fp64 matrix cores (few rows): one block per (row, 256
+// candidates), wave w scoring candidates cb0 + 64w .. cb0 + 64w + 63 in 16
+// quads. v_mfma_f64_4x4x4f64 runs 4 independent 4x4x4 blocks; block b is KV
+// group g = b, with A[i][k] = the query of head 4g + i and B[k][j] = the
+// summary of candidate j of the quad, group g. Lane 16k + 4g + i holds A and
+// lane 16k + 4g + j holds B; step t of 16 covers dims 16k + t, so each lane
+// loads its 16 contiguous summary bytes (dims 16k..16k+15 of one candidate
+// and group) and its 16 query values once. D[i][j] lands in lane
+// 16i + 4g + j. All products are exact in fp64, and so is every partial sum
+// (a multiple of 2^-18 below 2^24), so the dots are exact in any order; the
+// score is then rounded as the oracle rounds it (exact.hpp). Waves 0 and 1
+// prep the row's 16 heads into LDS once per block (the same steps as
+// qprep_kernel); the first candidate block zeroes the row's top-k arrival
+// counters. Each wave's summary loads are issued before the prep.
 // ---------------------------------------------------------------------------
-constexpr int SX_NB = 4;       // 64-candidate batches per block
-constexpr int SX_ROW = 272;    // LDS bytes per candidate row
+constexpr int SM_CB = 256;  // candidates per block
 
-__global__ __launch_bounds__(256) void score_exact_kernel(
-    int qmode, const void* __restrict__ qin, int64_t qs, const float* __restrict__ qw, float eps,
-    const uint16_t* __restrict__ rope, int64_t rope_rows, const float* __restrict__ w_head,
-    int64_t w_stride, const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
-    const uint8_t* __restrict__ S, int64_t B, int64_t R_cap, int64_t ssb, int64_t pos_limit,
-    float* __restrict__ scores, unsigned* __restrict__ arrivals) {
-  __shared__ __align__(16) uint8_t rows_lds[64 * SX_ROW];
-  __shared__ __align__(16) double q_lds[4][256];  // per group: [64 dims][4 heads], exact
-  const int tid = threadIdx.x;
-  const int g = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
-  const int lane = tid & 63;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_exact_mfma_kernel(
+    const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
+    const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
+    int64_t ssb, int64_t pos_limit, float* __restrict__ scores, QPrepArgs prep) {
+  __shared__ __align__(16) uint8_t q_lds[16 * 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = lane >> 4, g = (lane >> 2) & 3, ij = lane & 3;  // ij: head i (A) or candidate j (B)
   const int64_t row = blockIdx.y;
-  // the selection pass of this call counts chunk arrivals per (row, group)
-  if (blockIdx.x == 0 && lane == 0) arrivals[row * 4 + g] = 0u;
-  const int32_t seq = row_seq[row];
+  const int32_t s = row_seq[row];
   const int64_t p = row_pos[row];
-  if (!(seq >= 0 && seq < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap)) return;
-  const int64_t nc = p >> 3;
-  const int64_t j0 = (int64_t)blockIdx.x * (64 * SX_NB);
-  if (j0 >= nc) return;
-  const uint8_t* Sb = S + (int64_t)seq * ssb;
-  float w4[4];
+  const bool ok = s >= 0 && s < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap;
+  const int64_t nc = ok ? (p >> 3) : 0;
+  if (blockIdx.x == 0 && threadIdx.x < 4) prep.arrivals[row * 4 + threadIdx.x] = 0u;
+  if ((int64_t)blockIdx.x * SM_CB >= nc) return;  // block-uniform
+  const int64_t cb0 = (int64_t)blockIdx.x * SM_CB + 64 * wave;
+  const bool live = cb0 < nc;
+  const int64_t jend = live ? (cb0 + 64 < nc ? cb0 + 64 : nc) : 0;
+  // this lane's 16 summary bytes of quad u: candidate cb0 + 4u + ij, group
+  // g, dims 16k..16k+15 (candidates past jend load jend - 1 again). Quads
+  // are loaded four at a time, two groups ahead of the one computed.
+  const uint8_t* Sw = S + (int64_t)s * ssb + cb0 * 256;
+  const uint32_t jlast = live ? (uint32_t)(jend - cb0 - 1) : 0u;
+  auto load4 = [&](int u0, uint4 (&dst)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
-  {
-    // q prep of the group's 4 heads (lanes 32..63 repeat lanes 0..31)
-    const int hh = (lane >> 3) & 3, c = lane & 7;
-    const uint2 pk = qprep8(qmode, qin, qs, row, 4 * g + hh, c, lane, qw, eps, rope, rope_rows,
-                            row_pos);
-    if (lane < 32) {
-      double vals[8];
-      e4m3x8_f64(pk, vals);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q_lds[g][(8 * c + i) * 4 + hh] = vals[i];
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t jo = min((uint32_t)(4 * (u0 + q) + ij), jlast);
+      dst[q] = ldg16(Sw + (jo * 256u + (uint32_t)(g * 64 + 16 * k)));
     }
+  };
+  uint4 bA[4], bB[4], bC[4];
+  if (live) {
+    load4(0, bA);
+    load4(4, bB);
   }
-  const double* qg = q_lds[g];
-
-  // thread t loads part t%16 of candidates t/16 + 16i of every batch;
-  // candidates past the row's last are loaded as its last one (not stored)
-  uint4 ld[SX_NB][4];
-  const int part = tid & 15;
-#pragma unroll
-  for (int b = 0; b < SX_NB; ++b)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t j = j0 + 64 * b + (tid >> 4) + 16 * i;
-      const int64_t jl = j < nc ? j : nc - 1;
-      ld[b][i] = ldg16(Sb + jl * 256 + 16 * part);
-    }
-  uint4 raw[SX_NB][4];  // this lane's candidate, group g, per batch
-#pragma unroll
-  for (int b = 0; b < SX_NB; ++b) {
-    if (b > 0) __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(rows_lds + ((tid >> 4) + 16 * i) * SX_ROW + 16 * part) = ld[b][i];
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      raw[b][u] = *reinterpret_cast<const uint4*>(rows_lds + lane * SX_ROW + g * 64 + 16 * u);
+  if (wave < 2) {
+    const int h = 8 * wave + (lane >> 3), c = lane & 7;
+    const uint2 pk = qprep8(prep.prepared ? 1 : 0, prep.q, prep.q_stride_row, row, h, c, lane,
+                            prep.w, prep.eps, static_cast<const uint16_t*>(prep.rope),
+                            prep.rope_rows, prep.row_pos);
+    *reinterpret_cast<uint2*>(&q_lds[h * 64 + c * 8]) = pk;
   }
-
-  // dims outer, batches inner: each query value is loaded once and
-  // used for the lane's SX_NB candidates; the fp64 sums are exact in any
-  // order. Empty asm statements that take the accumulators and clobber memory
-  // between 4-dim chunks keep the compiler to this order (it would otherwise
-  // run one batch over all dims first and keep the whole 2 KB query in
-  // registers, which spills).
-  double acc[SX_NB][4];
+  __syncthreads();
+  if (!live) return;
+  // A operand: head 4g + ij, dims 16k..16k+15 as packed e4m3, converted per use
+  const uint4 qraw = *reinterpret_cast<const uint4*>(&q_lds[(4 * g + ij) * 64 + 16 * k]);
+  const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
+  // this lane's weight for the epilogue: head 4g + i with i = lane >> 4 (the D row)
+  const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
+  float* out_g = scores + (row * 4 + g) * R_cap;
+  auto quads4 = [&](int u0, const uint4 (&bq)[4]) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int b = 0; b < SX_NB; ++b)
+    for (int m = 0; m < 4; ++m) {  // dword m of the 16 bytes: steps 4m .. 4m+3
+      const f32x2 ql = __builtin_amdgcn_cvt_pk_f32_fp8((int)qw[m], false);
+      const f32x2 qh = __builtin_amdgcn_cvt_pk_f32_fp8((int)qw[m], true);
+      const double qa[4] = {(double)ql[0], (double)ql[1], (double)qh[0], (double)qh[1]};
+      double sv[4][4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) acc[b][h] = 0.0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {  // 4-byte word w holds dims 4w..4w+3
-#pragma unroll
-    for (int b = 0; b < SX_NB; ++b)
-      asm volatile("" : "+v"(acc[b][0]), "+v"(acc[b][1]), "+v"(acc[b][2]), "+v"(acc[b][3])::"memory");
-    double sv[SX_NB][4];
-#pragma unroll
-    for (int b = 0; b < SX_NB; ++b) {
-      const uint4 r4 = raw[b][w >> 2];
-      const uint32_t word = (w & 3) == 0 ? r4.x : (w & 3) == 1 ? r4.y : (w & 3) == 2 ? r4.z : r4.w;
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
-      sv[b][0] = (double)lo[0];
-      sv[b][1] = (double)lo[1];
-      sv[b][2] = (double)hi[0];
-      sv[b][3] = (double)hi[1];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d = 4 * w + e;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const double qv = qg[4 * d + h];
-#pragma unroll
-        for (int b = 0; b < SX_NB; ++b) acc[b][h] = fma(qv, sv[b][e], acc[b][h]);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 r4 = bq[q];
+        const uint32_t wd = m == 0 ? r4.x : m == 1 ? r4.y : m == 2 ? r4.z : r4.w;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd, true);
+        sv[q][0] = (double)lo[0];
+        sv[q][1] = (double)lo[1];
+        sv[q][2] = (double)hi[0];
+        sv[q][3] = (double)hi[1];
       }
-    }
-  }
-  asm volatile("" ::: "memory");
-  float* out = scores + (row * 4 + g) * R_cap;
 #pragma unroll
-  for (int b = 0; b < SX_NB; ++b) {
-    const int64_t j = j0 + 64 * b + lane;
-    float sc = group_score4((float)acc[b][0], (float)acc[b][1], (float)acc[b][2],
-                            (float)acc[b][3], w4);
-    // computed in every lane (an opaque use), not sunk into the guarded store
-    asm volatile("" : "+v"(sc));
-    if (j < nc) out[j] = sc;
-  }
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[q] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[e], sv[q][e], acc[q], 0, 0, 0);
+    }
+    // D lane 16i + 4g + j: dot of head 4g + i with candidate j. The score
+    // sums the heads' weighted relu terms in head order, gathered into the
+    // lanes of head 0 (16 apart).
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float t = relu0((float)acc[q]) * wl;
+      const float t1 = __shfl_down(t, 16, 64), t2 = __shfl_down(t, 32, 64), t3 = __shfl_down(t, 48, 64);
+      float sc = t + t1;
+      sc = sc + t2;
+      sc = sc + t3;
+      const int64_t j = cb0 + 4 * (u0 + q) + ij;
+      if (lane < 16 && j < jend) out_g[j] = sc;
+    }
+  };
+  load4(8, bC);
+  quads4(0, bA);
+  load4(12, bA);
+  quads4(4, bB);
+  quads4(8, bC);
+  quads4(12, bA);
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.rows == 0 || a.R_cap == 0) return hipSuccess;
   if (a.exact) {
-    const dim3 grid((unsigned)((a.R_cap + 64 * SX_NB - 1) / (64 * SX_NB)), (unsigned)a.rows);
-    hipLaunchKernelGGL(score_exact_kernel, grid, dim3(256), 0, stream, a.prep.prepared ? 1 : 0,
-                       a.prep.q, a.prep.q_stride_row, a.prep.w, a.prep.eps,
-                       (const uint16_t*)a.prep.rope, a.prep.rope_rows, a.w_head, a.w_stride_row,
-                       a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb, a.pos_limit,
-                       reinterpret_cast<float*>(a.bounds), a.prep.arrivals);
+    const dim3 grid((unsigned)((a.R_cap + SM_CB - 1) / SM_CB), (unsigned)a.rows);
+    hipLaunchKernelGGL(score_exact_mfma_kernel, grid, dim3(256), 0, stream, a.w_head,
+                       a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
+                       a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
     return hipGetLastError();
   }
   if (a.fused_prep) {

@@ -24,8 +24,9 @@
 //      thread per candidate, the query read through scalar loads (the same
 //      value in every lane);
 //   4. the best K of C by (-exact score, id): a bitonic sort of the
-//      composites (key << 32 | ~id), 512 or 1,024 wide, or, for a larger C
-//      (heavy ties), a radix select followed by a bitonic sort of 512.
+//      composites (key << 32 | ~id), one per thread, 512 or 1,024 wide, or,
+//      for a larger C (heavy ties), a radix select followed by a bitonic sort
+//      of 512.
 // A C too large to sort directly (heavy ties) is first cut: the lower keys
 // >= tau include the K largest, so a radix select over just those gives T =
 // the top 22 bits of the K-th largest lower key (T <= that key), and C is
@@ -364,14 +365,17 @@ __device__ inline void unit_row(const int32_t* row_seq, const int64_t* row_pos, 
   *ncand = ok ? (p >> 3) : 0;
 }
 
-// thread t < 512 holds the rank-t composite v (rank < K), written as id and score
-__device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int32_t* sel_ids,
-                                  float* sel_scores) {
-  const int t = threadIdx.x;
-  if (t >= TK) return;
+// the rank-t composite v (rank t < K), written as id and score
+__device__ inline void write_rank_at(unsigned long long v, int t, int K, int64_t unit,
+                                     int32_t* sel_ids, float* sel_scores) {
   const bool have = t < K;
   sel_ids[unit * TK + t] = have ? (int32_t)(~(uint32_t)v) : -1;
   if (sel_scores) sel_scores[unit * TK + t] = have ? key_score((uint32_t)(v >> 32)) : 0.0f;
+}
+// thread t < 512 holds the rank-t composite v
+__device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int32_t* sel_ids,
+                                  float* sel_scores) {
+  if ((int)threadIdx.x < TK) write_rank_at(v, threadIdx.x, K, unit, sel_ids, sel_scores);
 }
 
 // Appends the candidates tid + 1024 k whose key reaches t to sm.ids (and,
@@ -424,23 +428,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
   const TkShared sm = carve(smem, (int)chunk);
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
-  int32_t seq;
-  int64_t ncand;
-  unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
   const int64_t j0 = (int64_t)c * chunk;
-  int N = 0;
-  if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
-  const int K = N < TK ? N : TK;
-
-  // keys of candidates tid + 1024 k in registers, and the largest lower key
-  // of the thread. All loads are issued before any is used (a lane past the
-  // end loads the last candidate again).
+  // keys of candidates tid + 1024 k in registers. The chunk's slots of the
+  // score buffer are read before the row's candidate count is known (it only
+  // masks them), all loads in flight at once; a lane past the chunk's end
+  // reads its last slot again.
+  const int nslot = (int)((R_cap - j0 < chunk) ? R_cap - j0 : chunk);
   float2 raw[TK_PER];
 #pragma unroll
   for (int k = 0; k < TK_PER; ++k) {
     raw[k] = make_float2(0.f, 0.f);
-    if (TK_THREADS * k < N) {
-      const int i = min(tid + TK_THREADS * k, N - 1);
+    if (TK_THREADS * k < nslot) {
+      const int i = min(tid + TK_THREADS * k, nslot - 1);
       if constexpr (EXACT) {
         const float s = reinterpret_cast<const float*>(bounds)[unit * R_cap + j0 + i];
         raw[k] = make_float2(s, s);
@@ -449,6 +448,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
       }
     }
   }
+  int32_t seq;
+  int64_t ncand;
+  unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
+  int N = 0;
+  if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
+  const int K = N < TK ? N : TK;
+  // the thread's keys (absent candidates 0) and its 4 group maxima
   uint32_t kh[TK_PER];
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -516,14 +522,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
     collect_best(sm, M, K);
     v = sort_desc<TK>(tid < K ? sm.out[tid] : 0ull, sm);
   }
-  if (mode == 0) {
-    write_rank(v, K, unit, sel_ids, sel_scores);
-    return;
-  }
-  // chunk list out: its best K, sorted, zero-padded to 512; the unit's last
-  // block to arrive merges all of them
-  unsigned long long* dst = partial + (unit * nchunks + c) * TK;
-  if (tid < TK) dst[tid] = tid < K ? v : 0ull;
+  if (mode == 0) write_rank(v, K, unit, sel_ids, sel_scores);
+  else if (tid < TK) partial[(unit * nchunks + c) * TK + tid] = tid < K ? v : 0ull;
+  if (mode == 0) return;
+  // the unit's last block to arrive merges all chunk lists
   __shared__ int sh_last;
   if (!block_arrive_last(&arrivals[unit], (unsigned)nchunks, &sh_last)) return;
   merge_lists(partial + unit * (int64_t)nchunks * TK, nchunks, ncand, unit, smem, sel_ids,

@@ -20,9 +20,8 @@
 //   2. survivors C = the candidates whose upper key reaches tau. C holds the
 //      exact top K: each of those has hi >= exact score >= K-th largest exact
 //      score >= K-th largest lo >= tau. Typically |C| is 600..1,000;
-//   3. (intervals) every member of C is rescored exactly (exact.hpp), one
-//      thread per candidate, the query read through scalar loads (the same
-//      value in every lane);
+//   3. (intervals) every member of C is rescored exactly on the fp64
+//      matrix cores, 16 survivors per instruction chain (rescore_survivors);
 //   4. the best K of C by (-exact score, id): a bitonic sort of the
 //      composites (key << 32 | ~id), one per thread, 512 or 1,024 wide, or,
 //      for a larger C (heavy ties), a radix select followed by a bitonic sort
@@ -409,11 +408,81 @@ __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_
   return (int)sm.misc[56];
 }
 
+// Exact scores of the survivors ids[0..M) of one (row, group) into keys[],
+// on the fp64 matrix cores. qg: the row's query for the group as exact fp64
+// [64 dims][4 heads]; Sg: the group's 64 bytes of candidate 0 (stride 256);
+// wl: the weight of head 4g + (lane >> 4). A wave scores 16 survivors per
+// chain of v_mfma_f64_4x4x4f64: the instruction's 4 blocks hold 4 survivors
+// each and share the query, A[i][kk] = head i and B[kk][j] = survivor
+// 16u + 4b + j (lane 16kk + 4b + i resp. j), step t of 16 taking dim
+// 16kk + t, so each lane loads 16 contiguous bytes of one survivor. Every
+// product and partial sum is exact in fp64; D[i][j] (lane 16i + 4b + j) then
+// goes through group_score4's fp32 epilogue, heads summed in order. Waves
+// take RS_Q groups of 16 at a time, groups wave, wave + 16, ... (3 fit the
+// 64-register cap without spills). xb holds the query meanwhile (it is free
+// until the sort).
+constexpr int RS_Q = 3;
+__device__ inline void rescore_survivors(const TkShared& sm, int M, const double* __restrict__ qg,
+                                         const uint8_t* __restrict__ Sg, float wl, int tid) {
+  double* qs = reinterpret_cast<double*>(sm.xb);
+  if (tid < 256) qs[tid] = qg[tid];
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int kk = lane >> 4, c16 = lane & 15, i = lane & 3;
+  const int ngrp = (M + 15) >> 4;
+  for (int u0 = wave; u0 < ngrp; u0 += RS_Q * TK_WAVES) {
+    const int nq = min(RS_Q, (ngrp - u0 + TK_WAVES - 1) / TK_WAVES);  // groups u0 + 16q < ngrp
+    uint4 bq[RS_Q];
+#pragma unroll
+    for (int q = 0; q < RS_Q; ++q) {
+      const int m = min(16 * (u0 + TK_WAVES * q) + c16, M - 1);
+      bq[q] = ldg16(Sg + (int64_t)sm.ids[m] * 256 + 16 * kk);
+    }
+    double acc[RS_Q];
+#pragma unroll
+    for (int q = 0; q < RS_Q; ++q) acc[q] = 0.0;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {  // dword t4 of the 16 bytes: steps 4 t4 .. 4 t4 + 3
+      double qa[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qa[e] = qs[(16 * kk + 4 * t4 + e) * 4 + i];
+#pragma unroll
+      for (int q = 0; q < RS_Q; ++q) {
+        if (q >= nq) break;
+        const uint32_t wd = t4 == 0 ? bq[q].x : t4 == 1 ? bq[q].y : t4 == 2 ? bq[q].z : bq[q].w;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd, false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd, true);
+        acc[q] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[0], (double)lo[0], acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[1], (double)lo[1], acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[2], (double)hi[0], acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[3], (double)hi[1], acc[q], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < RS_Q; ++q) {
+      if (q >= nq) break;
+      const float t = relu0((float)acc[q]) * wl;
+      const float t1 = __shfl_down(t, 16, 64), t2 = __shfl_down(t, 32, 64),
+                  t3 = __shfl_down(t, 48, 64);
+      float sc = t + t1;
+      sc = sc + t2;
+      sc = sc + t3;
+      const int m = 16 * (u0 + TK_WAVES * q) + lane;
+      if (lane < 16 && m < M) sm.keys[m] = ord_key(sc);
+    }
+  }
+  __syncthreads();
+}
+
 // One chunk of a (row, group)'s candidates: threshold, survivors, exact
 // rescoring (intervals), exact selection. mode 0: the whole range, final
 // output; mode 1: partial list, merged by the unit's last block.
+// Registers are capped for 8 waves per SIMD, so that two 1024-thread blocks
+// share a CU when the chunk's LDS allows it (prefill-sized chunks of 4,096
+// candidates): uncapped, the interval variant's scalar registers held it to
+// one block per CU and 1.6x the time.
 template <bool EXACT>
-__global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_chunk_kernel(
     int mode, const float2* __restrict__ bounds, int64_t R_cap,
     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int64_t B,
     int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
@@ -498,19 +567,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(
       __syncthreads();
       M = compact_keys(sm, kh, T, j0, false);
     }
-    // 3. exact scores of the survivors, one thread per candidate; the query
-    //    for (row, group), [64 dims][4 heads], is the same in every lane
-    const double* qg = q64 + (row * 4 + g) * 256;
-    const uint8_t* Sg = S + (int64_t)seq * ssb + g * 64;
-    float w4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
-    for (int m = tid; m < M; m += TK_THREADS) {
-      const uint8_t* sv = Sg + (int64_t)sm.ids[m] * 256;
-      const uint4 raw[4] = {ldg16(sv), ldg16(sv + 16), ldg16(sv + 32), ldg16(sv + 48)};
-      sm.keys[m] = ord_key(exact_group_score_sq(raw, qg, w4));
-    }
-    __syncthreads();
+    // 3. exact scores of the survivors (matrix cores)
+    const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
+    rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)seq * ssb + g * 64, wl, tid);
   }
   // 4. exact best K of the survivors (M >= K), sorted: thread t < 512 gets rank t
   unsigned long long v;

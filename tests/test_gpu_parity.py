@@ -126,6 +126,18 @@ def test_select_72_decode_rows_matrix_core_path():
     _select_check(d, S, O, rows, seq_map={b: i for i, b in enumerate(rows)})
 
 
+def test_select_tie_heavy_72_rows_matrix_core_path():
+    """Tie-heavy scores (q and summaries from a few codes, ramp weights)
+    through the interval path: scores tie in large blocks, so many candidates
+    survive the threshold (the cut by the lower keys, and more than one round
+    of matrix-core rescoring per wave); ids must still match exactly."""
+    d = _case("decode1_ctx1m", 23, DEV, rows=72, batch=72, cache_tokens=16384, with_kv=False)
+    S = d["summary"]
+    rows = [0, 35, 71]
+    _, ex = _select_check(d, S, P.host8(S), rows, exact=True)
+    assert ex == 0
+
+
 def test_select_prefill2048_ctx32k_sampled():
     d = _case("prefill2048_ctx32k", 17, DEV, with_kv=False)
     S = P.gpu_summary(d)

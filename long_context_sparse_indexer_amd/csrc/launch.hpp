@@ -49,26 +49,20 @@ struct ScoreArgs {
   const uint8_t* summary;
   int64_t B, R_cap, ssb;
   int64_t pos_limit;      // rows at p >= pos_limit are invalid (no rope row)
-  const double* q64;      // from launch_qprep, exact query [rows, 4 groups, 64 dims, 4 heads]
-  bool exact;             // exact scores (score_exact_mode) instead of intervals
-  bool fused_prep;        // the q prep is done in the score kernel from `prep`, which then
-                          // also writes q64 and zeroes the arrival counters (no launch_qprep)
+  bool exact;             // exact scores (score_exact_mode) instead of intervals; the exact
+                          // kernel also does the q prep from `prep` (no launch_qprep)
   QPrepArgs prep;
   float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score, or (exact)
                           // the exact scores as float [rows, 4, R_cap]
 };
-// Rows up to S5_EXACT_MAX_ROWS are scored exactly on the fp64 matrix cores;
-// more rows get intervals from the matrix cores and exact rescoring of
-// the few candidates near each selection boundary. Up to S5_FUSED_PREP_ROWS
-// rows the query prep runs inside the score kernel (no separate launch).
+// Rows up to S5_EXACT_MAX_ROWS are scored exactly on the fp64 matrix cores,
+// the query prep fused in; more rows get their query prepped by its own
+// kernel, intervals from the bf16 matrix cores, and exact rescoring of the
+// candidates that can reach each row's top 512.
 #ifndef S5_EXACT_MAX_ROWS
 #define S5_EXACT_MAX_ROWS 64
 #endif
-#ifndef S5_FUSED_PREP_ROWS
-#define S5_FUSED_PREP_ROWS 64
-#endif
 inline bool score_exact_mode(int32_t rows) { return rows <= S5_EXACT_MAX_ROWS; }
-inline bool score_fused_prep(int32_t rows) { return rows <= S5_FUSED_PREP_ROWS; }
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 
 // Top-k selection plan: the candidates of a (row, group) are cut into

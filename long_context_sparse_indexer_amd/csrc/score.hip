@@ -207,41 +207,11 @@ __device__ inline float2 score_interval(f32x4 d, f32x4 a, const float* w4) {
   return make_float2(s - delta, s + delta);
 }
 
-// prep of the block's query rows into LDS (fused_prep, few rows): wave w
-// preps row r0 + w (16 heads, two passes of eight 8-lane groups) into
-// q_lds[w] as e4m3; the block of the first candidate range also writes the
-// row's exact query for the rescoring pass and zeroes its top-k arrival
-// counters (no early exit comes before this).
-__device__ inline void score_fused_prep(const QPrepArgs& pa, int r0, int nr, const int32_t* seq,
-                                        bool first_block, uint8_t (*q_lds)[16 * 64]) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (wave >= nr) return;
-  const int64_t r = r0 + wave;
-  if (first_block && lane < 4) pa.arrivals[r * 4 + lane] = 0u;
-  if (seq[wave] < 0) return;
-  const int c = lane & 7;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int h = 8 * pass + (lane >> 3);
-    const uint2 pk = qprep8(pa.prepared ? 1 : 0, pa.q, pa.q_stride_row, r, h, c, lane, pa.w, pa.eps,
-                           static_cast<const uint16_t*>(pa.rope), pa.rope_rows, pa.row_pos);
-    *reinterpret_cast<uint2*>(&q_lds[wave][h * 64 + c * 8]) = pk;
-    if (first_block) {
-      double vals[8];
-      e4m3x8_f64(pk, vals);
-      double* dst = pa.q64 + ((r * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i * 4] = vals[i];
-    }
-  }
-}
-
 __global__ __launch_bounds__(256) void score_kernel(
     const uint8_t* __restrict__ q8, int64_t qs8, int32_t rows, const float* __restrict__ w_head,
     int64_t w_stride, const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
     const uint8_t* __restrict__ S, int64_t B, int64_t R_cap, int64_t ssb, int64_t pos_limit,
-    float2* __restrict__ bounds, int fused_prep, QPrepArgs prep) {
-  __shared__ __align__(16) uint8_t q_lds[4][16 * 64];
+    float2* __restrict__ bounds) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
   const int r0 = blockIdx.y * 4;
@@ -274,8 +244,8 @@ __global__ __launch_bounds__(256) void score_kernel(
     }
   }
   // rows of different sequences: wave w scores row r0 + w over candidates
-  // cb0..jend-1; its 64 candidates' loads (16 per lane) are issued first, so
-  // they are in flight during the query prep. In iteration u, column n of
+  // cb0..jend-1; its 64 candidates' loads (16 per lane) are issued first.
+  // In iteration u, column n of
   // the MFMA's B operand is candidate cb0 + 4u + n/4 of group
   // ((n & 3) + u) & 3 (the 1 KB of four candidates, the groups rotated by u)
   const bool dec_live = !shared && wave < nr && seq[wave] >= 0 && cb0 < ncand[wave];
@@ -291,11 +261,6 @@ __global__ __launch_bounds__(256) void score_kernel(
       bq[u] = ldg16(Sb + jl * 256 + (((n & 3) + u) & 3) * 64 + 16 * qd);
     }
   }
-  if (fused_prep) {
-    if (blockIdx.x != 0 && cb0 >= maxc) return;  // block-uniform
-    score_fused_prep(prep, r0, nr, seq, blockIdx.x == 0, q_lds);
-    __syncthreads();
-  }
   if (cb0 >= maxc) return;
 
   if (shared) {
@@ -307,8 +272,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     for (int g = 0; g < 4; ++g) {
       uint4 raw = make_uint4(0, 0, 0, 0);
       if (rr < nr && seq[rr] >= 0)
-        raw = fused_prep ? *reinterpret_cast<const uint4*>(&q_lds[rr][(4 * g + hh) * 64 + 16 * qd])
-                         : ldg16(q8 + (int64_t)(r0 + rr) * qs8 + (4 * g + hh) * 64 + 16 * qd);
+        raw = ldg16(q8 + (int64_t)(r0 + rr) * qs8 + (4 * g + hh) * 64 + 16 * qd);
       aq[g] = widen16(raw);
     }
     const int orow = r0 + qd;
@@ -335,8 +299,7 @@ __global__ __launch_bounds__(256) void score_kernel(
     // ---- rows of different sequences (loads issued above)
     if (!dec_live) return;
     const int row = r0 + wave;
-    const Bf16x16 aq = widen16(fused_prep ? *reinterpret_cast<const uint4*>(&q_lds[wave][n * 64 + 16 * qd])
-                                          : ldg16(q8 + (int64_t)row * qs8 + n * 64 + 16 * qd));
+    const Bf16x16 aq = widen16(ldg16(q8 + (int64_t)row * qs8 + n * 64 + 16 * qd));
     float w4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w4[i] = w_head[(int64_t)row * w_stride + 4 * qd + i];
@@ -357,86 +320,6 @@ __global__ __launch_bounds__(256) void score_kernel(
         const float2 iv = score_interval(dk, ak, w4);
         if (j < jend) bounds[((int64_t)row * 4 + qd) * R_cap + j] = iv;
       }
-    }
-  }
-}
-
-// Few rows (the query prep fused): one block per (row, 256 candidates); wave
-// w scores candidates cb0 + 64w .. cb0 + 64w + 63 of the row with A = the
-// row's 16 heads and B = 4 candidates x 4 groups per iteration (1 KB
-// contiguous), the groups rotated by the iteration u so that every output
-// lane holds one of the row's results (its own group) in one iteration of
-// every four. Waves 0 and 1 prep the row's 16 heads into LDS once per block;
-// the first candidate block also writes the exact query for the rescoring
-// pass and zeroes the row's top-k arrival counters. Each wave's 64
-// candidates are loaded (16 per lane) before the prep, so they are in flight
-// during it.
-constexpr int SR_CB = 256;  // candidates per block
-
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_rows_kernel(
-    const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
-    const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
-    int64_t ssb, int64_t pos_limit, float2* __restrict__ bounds, QPrepArgs prep) {
-  __shared__ __align__(16) uint8_t q_lds[16 * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 15, qd = lane >> 4;
-  const int64_t row = blockIdx.y;
-  const int32_t s = row_seq[row];
-  const int64_t p = row_pos[row];
-  const bool ok = s >= 0 && s < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap;
-  const int64_t nc = ok ? (p >> 3) : 0;
-  if (blockIdx.x == 0 && threadIdx.x < 4) prep.arrivals[row * 4 + threadIdx.x] = 0u;
-  if ((int64_t)blockIdx.x * SR_CB >= nc) return;  // block-uniform
-  const int64_t cb0 = (int64_t)blockIdx.x * SR_CB + 64 * wave;
-  const bool live = cb0 < nc;
-  const int64_t jend = live ? (cb0 + 64 < nc ? cb0 + 64 : nc) : 0;
-  uint4 bq[16];
-  if (live) {
-    // wave-uniform base, 32-bit lane offsets; candidates past jend load
-    // candidate jend - 1 again (not stored)
-    const uint8_t* Sw = S + (int64_t)s * ssb + cb0 * 256;
-    const uint32_t jlast = (uint32_t)(jend - cb0 - 1);
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const uint32_t jo = min((uint32_t)(u * 4 + (n >> 2)), jlast);
-      bq[u] = ldg16(Sw + (jo * 256u + (uint32_t)((((n & 3) + u) & 3) * 64 + 16 * qd)));
-    }
-  }
-  if (wave < 2) {
-    const int h = 8 * wave + (lane >> 3), c = lane & 7;
-    const uint2 pk = qprep8(prep.prepared ? 1 : 0, prep.q, prep.q_stride_row, row, h, c, lane,
-                            prep.w, prep.eps, static_cast<const uint16_t*>(prep.rope),
-                            prep.rope_rows, prep.row_pos);
-    *reinterpret_cast<uint2*>(&q_lds[h * 64 + c * 8]) = pk;
-    if (blockIdx.x == 0) {
-      double vals[8];
-      e4m3x8_f64(pk, vals);
-      double* dst = prep.q64 + ((row * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i * 4] = vals[i];
-    }
-  }
-  __syncthreads();
-  if (!live) return;
-  const Bf16x16 aq = widen16(*reinterpret_cast<const uint4*>(&q_lds[n * 64 + 16 * qd]));
-  float w4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * qd + i];
-  // output lane (n, qd) holds heads 4qd..4qd+3 of column n: the row's result
-  // for group qd in the iteration u with ((n & 3) + u) & 3 == qd
-  const int mu = (qd - (n & 3)) & 3;
-  f32x4 dk = {0.f, 0.f, 0.f, 0.f}, ak = dk;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    f32x4 d, a;
-    dot64(aq, widen16(bq[u]), d, a);
-    const bool mine = (u & 3) == mu;
-    dk = mine ? d : dk;
-    ak = mine ? a : ak;
-    if ((u & 3) == 3) {
-      const int64_t j = cb0 + (u - 3 + mu) * 4 + (n >> 2);
-      const float2 iv = score_interval(dk, ak, w4);
-      if (j < jend) bounds[(row * 4 + qd) * R_cap + j] = iv;
     }
   }
 }
@@ -564,17 +447,10 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
                        a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
     return hipGetLastError();
   }
-  if (a.fused_prep) {
-    const dim3 grid((unsigned)((a.R_cap + SR_CB - 1) / SR_CB), (unsigned)a.rows);
-    hipLaunchKernelGGL(score_rows_kernel, grid, dim3(256), 0, stream, a.w_head, a.w_stride_row,
-                       a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb, a.pos_limit,
-                       a.bounds, a.prep);
-    return hipGetLastError();
-  }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));
   hipLaunchKernelGGL(score_kernel, grid, dim3(256), 0, stream, a.q8, a.q8_stride_row, a.rows,
                      a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap,
-                     a.ssb, a.pos_limit, a.bounds, a.fused_prep ? 1 : 0, a.prep);
+                     a.ssb, a.pos_limit, a.bounds);
   return hipGetLastError();
 }
 

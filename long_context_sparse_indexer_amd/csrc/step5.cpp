@@ -186,8 +186,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   qa.q64 = q64;
   qa.arrivals = reinterpret_cast<unsigned*>(ws + w.arrivals);
   const bool exact = s5::score_exact_mode(rows);
-  const bool fused = exact || s5::score_fused_prep(rows);
-  int st = fused ? STEP5_OK : from_hip(s5::launch_qprep(qa, stream));
+  int st = exact ? STEP5_OK : from_hip(s5::launch_qprep(qa, stream));
   if (st) return st;
   s5::ScoreArgs sa;
   sa.prep = qa;
@@ -203,9 +202,7 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   sa.R_cap = R_cap;
   sa.ssb = s_stride_b;
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
-  sa.q64 = q64;
   sa.exact = exact;
-  sa.fused_prep = fused;
   sa.bounds = reinterpret_cast<float2*>(ws + w.bounds);
   st = from_hip(s5::launch_score(sa, stream));
   if (st) return st;

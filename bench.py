@@ -4,7 +4,9 @@ A step is one pass of the whole path over a batch of rows, with every input
 resident in HBM (each call captured once as a HIP graph and replayed, so the
 step measures the GPU and not the Python launch path; the whole step is one
 graph, launched once per step):
-  1. step5_index_summarize   the regions the step completes (k prep + summary)
+  1. step5_index_append      decode: each row's new token into the k/z rings and
+                             the region it completes summarised (prefill:
+                             step5_index_summarize over the chunk)
   2. step5_index_score_topk  q prep, scores over all candidates, top 512 per
                              KV group
   3. step5_sparse_attn       attention over the picks plus the own region
@@ -43,6 +45,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"
 HEADLINE = "decode16_ctx128k"
+RING_SLOTS = 520  # indexer k/z ring per sequence: one 512-token prompt chunk plus a region
 
 
 def parse():
@@ -221,12 +224,15 @@ def run_workload(name, args, torch, s5, W):
         calls.append(("summarize", lambda: s5.step5_index_summarize(
             kc_, zc_, t0, d["ln_w"], d["ln_b"], eps, d["rope"], S)))
     elif not wl.tie_heavy:
-        own0 = (T - 1) // 8 * 8
-        if T - own0 == 8:
-            ko, zo = d["k_idx"][:, own0:own0 + 8], d["z_idx"][:, own0:own0 + 8]
-            summ_step_tokens = 8 * B
-            calls.append(("summarize", lambda: s5.step5_index_summarize(
-                ko, zo, own0, d["ln_w"], d["ln_b"], eps, d["rope"], S)))
+        # the rings hold the open regions' earlier tokens; each step appends
+        # the rows' own tokens (the last of their regions here)
+        k_ring, z_ring = ring_before_step(torch, d, RING_SLOTS)
+        rs, rp = d["row_seq"].long(), d["row_pos"]
+        one_per_seq = len(set(d["row_seq"].tolist())) == rows
+        k_new, z_new = d["k_idx"][rs, rp].contiguous(), d["z_idx"][rs, rp].contiguous()
+        calls.append(("append", lambda: s5.step5_index_append(
+            k_new, z_new, d["row_seq"], d["row_pos"], k_ring, z_ring, d["ln_w"], d["ln_b"], eps,
+            d["rope"], S, one_per_seq=one_per_seq)))
     if wl.tie_heavy:
         calls.append(("score_topk", lambda: s5.step5_index_score_topk(
             d["q8"], d["w_head"], d["row_seq"], d["row_pos"], S, ids, q_is_e4m3=True,
@@ -270,9 +276,30 @@ def run_workload(name, args, torch, s5, W):
         b = summ_step_tokens * 1024 + (summ_step_tokens // 8) * 256
         res["summarize_in_step"] = {"tokens": summ_step_tokens, "algorithmic_bytes": b,
                                     "GBs": round(b / per_call["summarize"] / 1e3, 1)}
+    if "append" in per_call:
+        # per row: its token's k and z read and written to the ring (2 KB); per
+        # completed region: 8 tokens' k and z read (8 KB) and 256 B written
+        done = sum(1 for p in pos if p % 8 == 7)
+        b = rows * 2048 + done * (8 * 1024 + 256)
+        res["append_in_step"] = {"rows": rows, "regions_completed": done, "algorithmic_bytes": b,
+                                 "ring_slots": RING_SLOTS,
+                                 "GBs": round(b / per_call["append"] / 1e3, 1)}
     if wl.prefill_chunk:
         res["prefill_tokens_per_s"] = round(wl.prefill_chunk * steps / elapsed, 1)
     return res, d, S
+
+
+def ring_before_step(torch, d, slots):
+    """k/z rings [B, slots, 4, 64] holding, for every row, the tokens of its
+    own region before the row's position (what earlier appends left there)."""
+    k, z = d["k_idx"], d["z_idx"]
+    k_ring = torch.zeros((k.shape[0], slots) + tuple(k.shape[2:]), dtype=k.dtype, device=k.device)
+    z_ring = torch.zeros_like(k_ring)
+    for s, p in zip(d["row_seq"].tolist(), d["row_pos"].tolist()):
+        for t in range(p - p % 8, p):
+            k_ring[s, t % slots] = k[s, t]
+            z_ring[s, t % slots] = z[s, t]
+    return k_ring, z_ring
 
 
 def attn_traffic(workload):
@@ -367,8 +394,9 @@ def cpu_baseline(d, wl, nrows, seconds, torch):
     """The oracle (unchanged) on a bounded sample of the same decode step: the
     first `nrows` rows, each over its own sequence, repeated until `seconds`
     have passed. The oracle builds its own summaries of those sequences first
-    (untimed, like the GPU's cache); the timed part is the step: own-region
-    summary, q prep, scores, top-512 selection and attention."""
+    (untimed, like the GPU's cache); the timed part is the step: the rows'
+    tokens appended (ring + the region each completes), q prep, scores,
+    top-512 selection and attention."""
     import numpy as np
     from oracle import oracle as orc
     import workloads as W
@@ -392,12 +420,21 @@ def cpu_baseline(d, wl, nrows, seconds, torch):
     seq = np.array([smap[int(d["row_seq"][r])] for r in rows], np.int32)
     w = d["w_head"].cpu().numpy()
     q = W.bits16(d["q"])[rows]
-    own0 = (T - 1) // 8 * 8
+    if not wl.tie_heavy:
+        # the rings as the GPU step starts them, the rows' new tokens
+        k_ring = np.zeros((len(seqs), RING_SLOTS, 4, 64), np.uint16)
+        z_ring = np.zeros_like(k_ring)
+        for r in rows:
+            s, p = smap[int(d["row_seq"][r])], int(pos[rows.index(r)])
+            for t in range(p - p % 8, p):
+                k_ring[s, t % RING_SLOTS] = k16[s, t]
+                z_ring[s, t % RING_SLOTS] = z16[s, t]
+        k_new = np.stack([k16[seq[i], pos[i]] for i in range(len(rows))])
+        z_new = np.stack([z16[seq[i], pos[i]] for i in range(len(rows))])
 
     def one_step():
         if not wl.tie_heavy:
-            orc.summarize(k16[:, own0:own0 + 8], z16[:, own0:own0 + 8], own0, lnw, lnb,
-                          W.NORM_EPS, rope, R_cap=Sh.shape[1], summary=Sh, nthreads=nth)
+            orc.append(k_new, z_new, seq, pos, k_ring, z_ring, lnw, lnb, W.NORM_EPS, rope, Sh)
             q8 = orc.q_prep(W.bits16(d["q_idx"])[rows], d["q_norm_w"].cpu().numpy(), W.NORM_EPS,
                             rope, pos, nthreads=nth)
         else:
@@ -417,7 +454,8 @@ def cpu_baseline(d, wl, nrows, seconds, torch):
     return {"value": round(len(rows) * reps / dt, 3), "unit": "rows/s", "cores": nth,
             "kind": "oracle",
             "sample": f"rows 0..{len(rows) - 1} of {wl.name} ({len(rows)} of {d['rows']} rows, "
-                      f"each its own {T}-token sequence): own-region summary, q prep, scores, "
+                      f"each its own {T}-token sequence): cache append (ring + own-region "
+                      f"summary), q prep, scores, "
                       f"top-512, attention; repeated {reps} times in {dt:.1f} s"}
 
 

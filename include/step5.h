@@ -87,6 +87,9 @@ enum {
  * skipped and q_norm_w, q_eps, rope_cs, rope_rows are ignored. */
 #define STEP5_Q_E4M3 1u
 
+/* Flag of step5_index_append: no two rows of the call share a sequence. */
+#define STEP5_APPEND_ONE_PER_SEQ 1u
+
 /* Human-readable name of a status code (static string). */
 const char* step5_status_str(int status);
 
@@ -118,6 +121,55 @@ int step5_index_summarize(const step5_geom* geom, const void* k, const void* z, 
                           const float* ln_w, const float* ln_b, float ln_eps,
                           const void* rope_cs, int64_t rope_rows, void* summary,
                           int64_t s_stride_b, int64_t R_cap, hipStream_t stream);
+
+/*
+ * Append one new token per row to the indexer's k/z rings and summarise the
+ * regions those tokens complete: the cache-side work of a decode step (or of
+ * a prompt chunk, one row per token).
+ * [TensorFold #903: prompt-path commit note (the indexer's k and z live in
+ * rings that hold one prompt chunk more than a chunk); indexer commit note
+ * (every completed region is summarised, as step5_index_summarize does)]
+ *
+ * k_new, z_new  bf16 [rows, groups, idx_dim]: the raw indexer k and z of each
+ *             row's new token; element stride new_stride_row between rows
+ *             (>= groups*idx_dim, a multiple of 8); 16-byte aligned.
+ * row_seq     int32 [rows] (device): the row's sequence, 0 .. B-1.
+ * row_pos     int64 [rows] (device): the absolute position of its token.
+ * k_ring, z_ring  bf16 [B, ring_slots, groups, idx_dim]: per sequence, the
+ *             token at position p lives in slot p mod ring_slots. Element
+ *             stride ring_stride_b between sequences (a multiple of 8,
+ *             >= ring_slots*groups*idx_dim when B > 1); 16-byte aligned.
+ *             ring_slots: a multiple of region, >= region.
+ * ln_w, ln_b, ln_eps, rope_cs, rope_rows  as for step5_index_summarize.
+ * summary, s_stride_b, R_cap  as for step5_index_summarize.
+ *
+ * Step 1: every valid row's k and z are written to ring slot
+ * row_pos mod ring_slots of sequence row_seq. Step 2 (after all of step 1):
+ * every valid row whose token ends a region (row_pos mod region == region-1)
+ * has that region, row_pos / region, summarised from the ring slots of its
+ * tokens: the same bits step5_index_summarize writes from contiguous k and
+ * z. Nothing else is written. A row is valid if 0 <= row_seq < B,
+ * 0 <= row_pos < rope_rows and row_pos / region < R_cap; other rows are
+ * skipped.
+ * Preconditions (device values, not checked): the rows of one call have
+ * distinct (sequence, position) pairs, and every region completed in the
+ * call has its other tokens in the ring, from this call or earlier ones:
+ * the positions a call brings for one sequence span at most
+ * ring_slots - region + 1 tokens (a ring one prompt chunk plus one region
+ * long takes chunks of that many).
+ * flags       0, or STEP5_APPEND_ONE_PER_SEQ: the caller guarantees that no
+ *             two rows of the call share a sequence (a decode step); the
+ *             call then runs as one launch, reading a completed region's
+ *             earlier tokens from the ring and the row's own from k_new/z_new.
+ *             Other bits are STEP5_E_INVALID.
+ * rows == 0 is a successful no-op.
+ */
+int step5_index_append(const step5_geom* geom, uint32_t flags, const void* k_new,
+                       const void* z_new, int64_t new_stride_row, const int32_t* row_seq, const int64_t* row_pos,
+                       int32_t rows, void* k_ring, void* z_ring, int64_t B, int64_t ring_slots,
+                       int64_t ring_stride_b, const float* ln_w, const float* ln_b, float ln_eps,
+                       const void* rope_cs, int64_t rope_rows, void* summary, int64_t s_stride_b,
+                       int64_t R_cap, hipStream_t stream);
 
 /*
  * Score every candidate region of each row and keep the best topk per group.

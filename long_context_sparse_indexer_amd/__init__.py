@@ -20,12 +20,13 @@ import torch
 
 __all__ = [
     "Step5Error", "GEOM", "lib", "step5_status_str", "step5_index_summarize",
-    "step5_index_score_topk", "step5_index_score_topk_workspace", "step5_sparse_attn",
-    "step5_sparse_attn_workspace", "STEP5_Q_E4M3",
+    "step5_index_append", "step5_index_score_topk", "step5_index_score_topk_workspace", "step5_sparse_attn",
+    "step5_sparse_attn_workspace", "STEP5_Q_E4M3", "STEP5_APPEND_ONE_PER_SEQ",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstep5.so")
 STEP5_Q_E4M3 = 1
+STEP5_APPEND_ONE_PER_SEQ = 1
 
 IDX_HEADS, GROUPS, IDX_DIM, ROPE_DIM, REGION, TOPK = 16, 4, 64, 32, 8, 512
 Q_HEADS, KV_HEADS, HEAD_DIM = 16, 4, 128
@@ -63,6 +64,9 @@ def lib():
         L.step5_index_summarize.restype = C.c_int
         L.step5_index_summarize.argtypes = [G, P, P, I64, I64, I64, I64, I64, P, P, F, P, I64, P,
                                             I64, I64, P]
+        L.step5_index_append.restype = C.c_int
+        L.step5_index_append.argtypes = [G, U32, P, P, I64, P, P, I32, P, P, I64, I64, I64, P, P, F, P,
+                                         I64, P, I64, I64, P]
         L.step5_index_score_topk.restype = C.c_int
         L.step5_index_score_topk.argtypes = [G, U32, P, I64, P, F, P, I64, P, I64, P, P, I32, P,
                                              I64, I64, I64, P, P, P, SZ, P]
@@ -129,6 +133,47 @@ def step5_index_summarize(k: torch.Tensor, z: torch.Tensor, t0: int, ln_w: torch
         _ptr(ln_b), float(ln_eps), _ptr(rope), rope.shape[0], _ptr(summary), summary.stride(0),
         summary.shape[1], _stream(stream))
     _check("step5_index_summarize", st)
+
+
+def step5_index_append(k_new: torch.Tensor, z_new: torch.Tensor, row_seq: torch.Tensor,
+                       row_pos: torch.Tensor, k_ring: torch.Tensor, z_ring: torch.Tensor,
+                       ln_w: torch.Tensor, ln_b: torch.Tensor, ln_eps: float, rope: torch.Tensor,
+                       summary: torch.Tensor, one_per_seq: bool = False, stream=None) -> None:
+    """Write each row's new token (k_new, z_new: bf16 [rows, 4, 64]) to slot
+    row_pos mod slots of its sequence's rings (k_ring, z_ring: bf16
+    [B, slots, 4, 64]) and summarise the regions those tokens complete into
+    summary (e4m3 as uint8 [B, R_cap, 4, 64]). one_per_seq: no two rows share a
+    sequence (a decode step), which lets the call run as one launch."""
+    _need(k_new.dtype == torch.bfloat16 and z_new.dtype == torch.bfloat16, "k_new, z_new must be bf16")
+    _need(k_new.dim() == 3 and k_new.shape == z_new.shape and
+          tuple(k_new.shape[1:]) == (GROUPS, IDX_DIM), "k_new, z_new must be [rows, 4, 64]")
+    _need(k_new.stride() == z_new.stride() and k_new.stride(2) == 1 and k_new.stride(1) == IDX_DIM,
+          "k_new, z_new need contiguous (group, dim) and equal strides")
+    _need(k_ring.dtype == torch.bfloat16 and z_ring.dtype == torch.bfloat16 and
+          k_ring.dim() == 4 and k_ring.shape == z_ring.shape and
+          tuple(k_ring.shape[2:]) == (GROUPS, IDX_DIM), "rings must be bf16 [B, slots, 4, 64]")
+    _need(k_ring.stride() == z_ring.stride() and k_ring.stride(3) == 1 and
+          k_ring.stride(2) == IDX_DIM and k_ring.stride(1) == GROUPS * IDX_DIM,
+          "ring slots must be contiguous, both rings alike")
+    summary = _u8(summary)
+    _need(summary.dtype == torch.uint8 and summary.dim() == 4 and
+          tuple(summary.shape[2:]) == (GROUPS, IDX_DIM) and summary.shape[0] == k_ring.shape[0],
+          "summary must be uint8 [B, R_cap, 4, 64]")
+    _need(summary.stride(3) == 1 and summary.stride(2) == IDX_DIM and
+          summary.stride(1) == GROUPS * IDX_DIM, "summary regions must be contiguous")
+    _need(rope.dtype == torch.bfloat16 and rope.dim() == 2 and rope.shape[1] == ROPE_DIM and
+          rope.is_contiguous(), "rope must be contiguous bf16 [rows, 32]")
+    _need(row_seq.dtype == torch.int32 and row_pos.dtype == torch.int64 and
+          row_seq.is_contiguous() and row_pos.is_contiguous() and
+          row_seq.numel() == k_new.shape[0] and row_pos.numel() == k_new.shape[0],
+          "row_seq int32 [rows], row_pos int64 [rows], contiguous")
+    st = lib().step5_index_append(
+        C.byref(GEOM), STEP5_APPEND_ONE_PER_SEQ if one_per_seq else 0, _ptr(k_new), _ptr(z_new),
+        k_new.stride(0), _ptr(row_seq), _ptr(row_pos),
+        k_new.shape[0], _ptr(k_ring), _ptr(z_ring), k_ring.shape[0], k_ring.shape[1],
+        k_ring.stride(0), _ptr(ln_w), _ptr(ln_b), float(ln_eps), _ptr(rope), rope.shape[0],
+        _ptr(summary), summary.stride(0), summary.shape[1], _stream(stream))
+    _check("step5_index_append", st)
 
 
 def step5_index_score_topk_workspace(rows: int, R_cap: int) -> int:

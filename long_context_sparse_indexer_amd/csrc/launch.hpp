@@ -22,6 +22,27 @@ struct SummarizeArgs {
 };
 hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream);
 
+struct AppendArgs {
+  const void* k_new;       // bf16 [rows, 4, 64], row stride new_stride_row (elements)
+  const void* z_new;
+  int64_t new_stride_row;
+  const int32_t* row_seq;
+  const int64_t* row_pos;
+  int32_t rows;
+  void* k_ring;            // bf16 [B, slots, 4, 64], sequence stride ring_stride_b (elements)
+  void* z_ring;
+  int64_t B, slots, ring_stride_b;
+  const float* ln_w;
+  const float* ln_b;
+  float eps;
+  const void* rope;
+  int64_t rope_rows;
+  void* summary;
+  int64_t ssb, R_cap;
+  bool one_per_seq;        // no two rows share a sequence: one fused launch
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
 struct QPrepArgs {
   bool prepared;          // q is already e4m3 (row stride in bytes); else bf16 (elements)
   const void* q;

@@ -122,6 +122,59 @@ STEP5_EXPORT int step5_index_summarize(const step5_geom* geom, const void* k, co
   return from_hip(s5::launch_summarize(a, stream));
 }
 
+STEP5_EXPORT int step5_index_append(const step5_geom* geom, uint32_t flags, const void* k_new,
+                                    const void* z_new,
+                                    int64_t new_stride_row, const int32_t* row_seq,
+                                    const int64_t* row_pos, int32_t rows, void* k_ring,
+                                    void* z_ring, int64_t B, int64_t ring_slots,
+                                    int64_t ring_stride_b, const float* ln_w, const float* ln_b,
+                                    float ln_eps, const void* rope_cs, int64_t rope_rows,
+                                    void* summary, int64_t s_stride_b, int64_t R_cap,
+                                    hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
+  if (rows < 0 || (flags & ~STEP5_APPEND_ONE_PER_SEQ) != 0) return STEP5_E_INVALID;
+  if (rows == 0) return STEP5_OK;
+  if (!k_new || !z_new || !row_seq || !row_pos || !k_ring || !z_ring || !ln_w || !ln_b ||
+      !rope_cs || !summary)
+    return STEP5_E_INVALID;
+  if (!aligned(k_new, 16) || !aligned(z_new, 16) || !aligned(k_ring, 16) || !aligned(z_ring, 16) ||
+      !aligned(ln_w, 16) || !aligned(ln_b, 16) || !aligned(rope_cs, 16) || !aligned(summary, 16) ||
+      !aligned(row_seq, 4) || !aligned(row_pos, 8))
+    return STEP5_E_INVALID;
+  const int64_t tok = (int64_t)kGroups * kIdxDim;  // elements of one token's k (or z)
+  if (new_stride_row < tok || (new_stride_row % 8) != 0) return STEP5_E_INVALID;
+  if (B < 1 || ring_slots < kRegion || (ring_slots % kRegion) != 0) return STEP5_E_INVALID;
+  if (ring_stride_b < 0 || (ring_stride_b % 8) != 0) return STEP5_E_INVALID;
+  if (B > 1 && ring_stride_b < ring_slots * tok) return STEP5_E_INVALID;
+  if (!finite_pos(ln_eps) || rope_rows < kRegion) return STEP5_E_INVALID;
+  if (R_cap < 1 || s_stride_b < 0 || (s_stride_b % 16) != 0) return STEP5_E_INVALID;
+  if (B > 1 && s_stride_b < R_cap * kRegionBytes) return STEP5_E_INVALID;
+
+  s5::AppendArgs a;
+  a.k_new = k_new;
+  a.z_new = z_new;
+  a.new_stride_row = new_stride_row;
+  a.row_seq = row_seq;
+  a.row_pos = row_pos;
+  a.rows = rows;
+  a.k_ring = k_ring;
+  a.z_ring = z_ring;
+  a.B = B;
+  a.slots = ring_slots;
+  a.ring_stride_b = ring_stride_b;
+  a.ln_w = ln_w;
+  a.ln_b = ln_b;
+  a.eps = ln_eps;
+  a.rope = rope_cs;
+  a.rope_rows = rope_rows;
+  a.summary = summary;
+  a.ssb = s_stride_b;
+  a.R_cap = R_cap;
+  a.one_per_seq = (flags & STEP5_APPEND_ONE_PER_SEQ) != 0;
+  return from_hip(s5::launch_append(a, stream));
+}
+
 STEP5_EXPORT size_t step5_index_score_topk_workspace(const step5_geom* geom, int32_t rows,
                                                      int64_t R_cap) {
   if (check_geom(geom) || rows < 0 || rows > kMaxScoreRows || R_cap < 1 || R_cap > kMaxRcap)

@@ -147,27 +147,27 @@ __global__ __launch_bounds__(256) void summarize_kernel(
   }
 }
 
-// Few regions (a decode step's own regions, a prefill chunk): one 256-thread
-// workgroup per region, lane (t, g, c) = token t, group g, dims 8c..8c+7, so
-// the 8 tokens run side by side. The same arithmetic in the same order: the
-// max over tokens (order-free), each token's k prep and e_t, e_t * k_t, then
-// den and num summed in token order by the lanes of token 0, from LDS.
-__global__ __launch_bounds__(256) void summarize_small_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ z, int64_t nreg,
-    int64_t t0, int64_t sb, int64_t st, const float* __restrict__ lnw,
-    const float* __restrict__ lnb, float eps, const uint16_t* __restrict__ rope,
-    uint8_t* __restrict__ S, int64_t ssb) {
+// One region by one 256-thread workgroup, lane (t, g, c) = token t, group g,
+// dims 8c..8c+7, so the 8 tokens run side by side. The same arithmetic in the
+// same order as summarize_kernel: the max over tokens (order-free), each
+// token's k prep and e_t, e_t * k_t, then den and num summed in token order by
+// the lanes of token 0, from LDS. kt, zt: this lane's 8 dims of its token;
+// cs: its token's rope row; dst: the region's 8 output bytes of this lane
+// (written by the lanes of token 0). Every thread of the block must call it.
+__device__ inline void summarize_region_block(const uint16_t* __restrict__ kt,
+                                              const uint16_t* __restrict__ zt,
+                                              const uint16_t* __restrict__ cs,
+                                              const float* __restrict__ lnw,
+                                              const float* __restrict__ lnb, float eps,
+                                              uint8_t* __restrict__ dst) {
   __shared__ uint4 z_lds[8][32];          // [token][lane of the token]: z, 8 bf16
   __shared__ float4 ep_lds[8][32][4];     // [token][lane]: e[0..7], e*k[0..7]
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int t = tid >> 5, sub = tid & 31;
-  const int g = sub >> 3, c = sub & 7;
-  const int64_t u = blockIdx.x;
-  const int64_t b = u / nreg, jr = u - b * nreg;
-  const int64_t off = b * sb + (jr * 8 + t) * st + g * 64 + c * 8;
-  const uint4 zraw = ldg16(z + off);
-  const uint4 kraw = ldg16(k + off);
+  const int c = sub & 7;
+  const uint4 zraw = ldg16(zt);
+  const uint4 kraw = ldg16(kt);
   z_lds[t][sub] = zraw;
   float gw[8], gb[8];
   {
@@ -201,7 +201,6 @@ __global__ __launch_bounds__(256) void summarize_small_kernel(
     const float tt = (d[i] * r) * gw[i];
     y[i] = tt + gb[i];
   }
-  const uint16_t* cs = rope + (t0 + jr * 8 + t) * 32;
   float cf[8], sf[8];
   unpack_bf16x8(ldg16(cs + fi), cf);
   unpack_bf16x8(ldg16(cs + 16 + fi), sf);
@@ -273,8 +272,73 @@ __global__ __launch_bounds__(256) void summarize_small_kernel(
   lo = e4m3x2_hw<true>(sbv[2], sbv[3], lo);
   uint32_t hi = e4m3x2_hw<false>(sbv[4], sbv[5], 0u);
   hi = e4m3x2_hw<true>(sbv[6], sbv[7], hi);
-  uint2* dst = reinterpret_cast<uint2*>(S + b * ssb + ((t0 >> 3) + jr) * 256 + g * 64 + c * 8);
-  *dst = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+}
+
+// Few regions (a decode step's own regions, a prefill chunk): one workgroup
+// per region of the span.
+__global__ __launch_bounds__(256) void summarize_small_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ z, int64_t nreg,
+    int64_t t0, int64_t sb, int64_t st, const float* __restrict__ lnw,
+    const float* __restrict__ lnb, float eps, const uint16_t* __restrict__ rope,
+    uint8_t* __restrict__ S, int64_t ssb) {
+  const int t = threadIdx.x >> 5, sub = threadIdx.x & 31;
+  const int g = sub >> 3, c = sub & 7;
+  const int64_t u = blockIdx.x;
+  const int64_t b = u / nreg, jr = u - b * nreg;
+  const int64_t off = b * sb + (jr * 8 + t) * st + g * 64 + c * 8;
+  summarize_region_block(k + off, z + off, rope + (t0 + jr * 8 + t) * 32, lnw, lnb, eps,
+                         S + b * ssb + ((t0 >> 3) + jr) * 256 + g * 64 + c * 8);
+}
+
+// ---------------------------------------------------------------------------
+// Incremental update of the k/z rings (TensorFold #903, prompt-path commit
+// note: the indexer keeps its k and z in rings; indexer commit note: every
+// completed region is summarised). Step 1 writes every row's token to slot
+// p mod slots of its sequence; step 2, a second launch so that it sees every
+// token of step 1, summarises the region each row's token completes, from
+// the ring (a region's 8 slots are contiguous: slots is a multiple of 8).
+// ---------------------------------------------------------------------------
+__device__ inline bool append_row_ok(int32_t s, int64_t p, int64_t B, int64_t rope_rows,
+                                     int64_t R_cap) {
+  return s >= 0 && s < B && p >= 0 && p < rope_rows && (p >> 3) < R_cap;
+}
+
+// one wave per row: lanes 0..31 copy the 512 B of k, lanes 32..63 those of z
+__global__ __launch_bounds__(256) void append_scatter_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ z_new, int64_t nsr,
+    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int32_t rows,
+    uint16_t* __restrict__ k_ring, uint16_t* __restrict__ z_ring, int64_t B, int64_t slots,
+    int64_t rsb, int64_t rope_rows, int64_t R_cap) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int32_t s = row_seq[r];
+  const int64_t p = row_pos[r];
+  if (!append_row_ok(s, p, B, rope_rows, R_cap)) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t e = (int64_t)(lane & 31) * 8;  // this lane's 8 bf16 of the token's 256
+  const int64_t dst = (int64_t)s * rsb + (p % slots) * 256 + e;
+  if (lane < 32) *reinterpret_cast<uint4*>(k_ring + dst) = ldg16(k_new + r * nsr + e);
+  else *reinterpret_cast<uint4*>(z_ring + dst) = ldg16(z_new + r * nsr + e);
+}
+
+// one workgroup per row; rows whose token does not end a region exit
+__global__ __launch_bounds__(256) void append_summarize_kernel(
+    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
+    const uint16_t* __restrict__ k_ring, const uint16_t* __restrict__ z_ring, int64_t B,
+    int64_t slots, int64_t rsb, const float* __restrict__ lnw, const float* __restrict__ lnb,
+    float eps, const uint16_t* __restrict__ rope, int64_t rope_rows, uint8_t* __restrict__ S,
+    int64_t ssb, int64_t R_cap) {
+  const int64_t r = blockIdx.x;
+  const int32_t s = row_seq[r];
+  const int64_t p = row_pos[r];
+  if (!append_row_ok(s, p, B, rope_rows, R_cap) || (p & 7) != 7) return;  // block-uniform
+  const int t = threadIdx.x >> 5, sub = threadIdx.x & 31;
+  const int g = sub >> 3, c = sub & 7;
+  const int64_t a = p - 7;  // the region's first token
+  const int64_t off = (int64_t)s * rsb + ((a % slots) + t) * 256 + g * 64 + c * 8;
+  summarize_region_block(k_ring + off, z_ring + off, rope + (a + t) * 32, lnw, lnb, eps,
+                         S + (int64_t)s * ssb + (p >> 3) * 256 + g * 64 + c * 8);
 }
 
 // spans of up to this many regions run token-parallel
@@ -298,6 +362,63 @@ hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(summarize_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const uint16_t*)a.k, (const uint16_t*)a.z, nreg, total, a.t0, a.sb, a.st,
                      a.ln_w, a.ln_b, a.eps, (const uint16_t*)a.rope, (uint8_t*)a.summary, a.ssb);
+  return hipGetLastError();
+}
+
+// One launch when no two rows share a sequence (a decode step): the block of
+// row r copies its token into the ring and, if the token ends a region,
+// summarises it with the region's other 7 tokens from the ring (earlier
+// calls wrote them; no block of this launch writes this sequence's ring) and
+// its own token straight from k_new/z_new.
+__global__ __launch_bounds__(256) void append_one_per_seq_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ z_new, int64_t nsr,
+    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
+    uint16_t* __restrict__ k_ring, uint16_t* __restrict__ z_ring, int64_t B, int64_t slots,
+    int64_t rsb, const float* __restrict__ lnw, const float* __restrict__ lnb, float eps,
+    const uint16_t* __restrict__ rope, int64_t rope_rows, uint8_t* __restrict__ S, int64_t ssb,
+    int64_t R_cap) {
+  const int64_t r = blockIdx.x;
+  const int32_t s = row_seq[r];
+  const int64_t p = row_pos[r];
+  if (!append_row_ok(s, p, B, rope_rows, R_cap)) return;  // block-uniform
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int64_t e = (int64_t)(tid & 31) * 8;
+    const int64_t dst = (int64_t)s * rsb + (p % slots) * 256 + e;
+    if (tid < 32) *reinterpret_cast<uint4*>(k_ring + dst) = ldg16(k_new + r * nsr + e);
+    else *reinterpret_cast<uint4*>(z_ring + dst) = ldg16(z_new + r * nsr + e);
+  }
+  if ((p & 7) != 7) return;  // block-uniform
+  const int t = tid >> 5, sub = tid & 31;
+  const int g = sub >> 3, c = sub & 7;
+  const int64_t a = p - 7;
+  const int64_t io = (int64_t)g * 64 + c * 8;
+  const uint16_t* kt = t == 7 ? k_new + r * nsr + io : k_ring + (int64_t)s * rsb + ((a % slots) + t) * 256 + io;
+  const uint16_t* zt = t == 7 ? z_new + r * nsr + io : z_ring + (int64_t)s * rsb + ((a % slots) + t) * 256 + io;
+  summarize_region_block(kt, zt, rope + (a + t) * 32, lnw, lnb, eps,
+                         S + (int64_t)s * ssb + (p >> 3) * 256 + io);
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.one_per_seq) {
+    hipLaunchKernelGGL(append_one_per_seq_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream,
+                       (const uint16_t*)a.k_new, (const uint16_t*)a.z_new, a.new_stride_row,
+                       a.row_seq, a.row_pos, (uint16_t*)a.k_ring, (uint16_t*)a.z_ring, a.B,
+                       a.slots, a.ring_stride_b, a.ln_w, a.ln_b, a.eps, (const uint16_t*)a.rope,
+                       a.rope_rows, (uint8_t*)a.summary, a.ssb, a.R_cap);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(append_scatter_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,
+                     stream, (const uint16_t*)a.k_new, (const uint16_t*)a.z_new, a.new_stride_row,
+                     a.row_seq, a.row_pos, a.rows, (uint16_t*)a.k_ring, (uint16_t*)a.z_ring, a.B,
+                     a.slots, a.ring_stride_b, a.rope_rows, a.R_cap);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(append_summarize_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream,
+                     a.row_seq, a.row_pos, (const uint16_t*)a.k_ring, (const uint16_t*)a.z_ring,
+                     a.B, a.slots, a.ring_stride_b, a.ln_w, a.ln_b, a.eps,
+                     (const uint16_t*)a.rope, a.rope_rows, (uint8_t*)a.summary, a.ssb, a.R_cap);
   return hipGetLastError();
 }
 

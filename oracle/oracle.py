@@ -168,6 +168,45 @@ def summarize(k16, z16, t0, ln_w, ln_b, eps, rope, R_cap=None, summary=None, sha
     return (summary, sh) if shadow else summary
 
 
+def append(k_new, z_new, row_seq, row_pos, k_ring, z_ring, ln_w, ln_b, eps, rope, summary):
+    """Indexer cache update for one new token per row, in place.
+
+    TensorFold #903 ("Step-5-Preview on one 256 GB Mac"): the prompt-path
+    commit note keeps the indexer's k and z in rings that hold one prompt
+    chunk more than it needs; the indexer commit note summarises every
+    completed 8-token region. Written out:
+      1. row r's raw k and z go to slot row_pos[r] mod slots of sequence
+         row_seq[r] (all rows first);
+      2. every row whose token ends a region (p mod 8 == 7) has that region,
+         p // 8, summarised from the ring slots of its tokens p-7 .. p, as the
+         batch summary does it from contiguous k and z.
+    k_new, z_new: uint16 [rows, G, 64]; k_ring, z_ring: uint16 [B, slots, G,
+    64]; summary: uint8 [B, R_cap, G, 64]. Rows whose sequence is outside
+    0..B-1, or whose position is negative, past the rope table or in a region
+    >= R_cap, are skipped.
+    """
+    B, slots = k_ring.shape[:2]
+    assert slots % REGION == 0 and slots >= REGION and z_ring.shape == k_ring.shape
+    assert k_ring.flags["C_CONTIGUOUS"] and z_ring.flags["C_CONTIGUOUS"]
+    R_cap = summary.shape[1]
+    done = []
+    for r in range(len(row_seq)):
+        s, p = int(row_seq[r]), int(row_pos[r])
+        if not (0 <= s < B and 0 <= p < rope.shape[0] and p // REGION < R_cap):
+            continue
+        k_ring[s, p % slots] = k_new[r]
+        z_ring[s, p % slots] = z_new[r]
+        done.append((s, p))
+    for s, p in done:
+        if p % REGION != REGION - 1:
+            continue
+        a = p - (REGION - 1)
+        sl = a % slots
+        summarize(k_ring[s:s + 1, sl:sl + REGION], z_ring[s:s + 1, sl:sl + REGION], a, ln_w,
+                  ln_b, eps, rope, R_cap=R_cap, summary=summary[s:s + 1])
+    return k_ring, z_ring, summary
+
+
 def score(q8, w_head, row_seq, row_pos, summary, nthreads=None) -> np.ndarray:
     """q8 [rows, H, 64] e4m3; w_head [H] or [rows, H]; summary [B, R_cap, G, 64].
 

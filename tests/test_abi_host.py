@@ -39,7 +39,7 @@ def geom(s5, **kw):
 def test_exports_every_declared_symbol(s5):
     text = open(HEADER).read()
     declared = set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(step5_\w+)\s*\(", text, re.M))
-    assert {"step5_index_summarize", "step5_index_score_topk", "step5_sparse_attn",
+    assert {"step5_index_summarize", "step5_index_append", "step5_index_score_topk", "step5_sparse_attn",
             "step5_index_score_topk_workspace", "step5_sparse_attn_workspace",
             "step5_status_str"} <= declared
     nm = subprocess.run(["nm", "-D", "--defined-only", s5.LIB_PATH], capture_output=True,
@@ -116,6 +116,54 @@ def _summ(s5, **over):
 ])
 def test_summarize_rejections(s5, over, code):
     assert _summ(s5, **over) == code
+
+
+def _append(s5, **over):
+    g = geom(s5)
+    a = dict(k=A, z=A, ns=256, seq=A, pos=A, rows=16, kr=A, zr=A, B=16, slots=520,
+             rsb=520 * 256, lnw=A, lnb=A, eps=1e-6, rope=A, rope_rows=131072, summary=A,
+             ssb=16384 * 256, R_cap=16384)
+    a.update(over)
+    return s5.lib().step5_index_append(
+        C.byref(g), a.get("flags", 0), a["k"], a["z"], a["ns"], a["seq"], a["pos"], a["rows"], a["kr"], a["zr"],
+        a["B"], a["slots"], a["rsb"], a["lnw"], a["lnb"], a["eps"], a["rope"], a["rope_rows"],
+        a["summary"], a["ssb"], a["R_cap"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"rows": 0}, OK),
+    ({"rows": 0, "k": None}, OK),    # an empty call touches nothing
+    ({"rows": -1}, E_INVALID),
+    ({"k": None}, E_INVALID),
+    ({"seq": None}, E_INVALID),
+    ({"zr": None}, E_INVALID),
+    ({"summary": None}, E_INVALID),
+    ({"z": A + 8}, E_INVALID),       # misaligned
+    ({"kr": A + 2}, E_INVALID),
+    ({"pos": A + 4}, E_INVALID),     # int64 array not 8-byte aligned
+    ({"ns": 255}, E_INVALID),
+    ({"ns": 260}, E_INVALID),        # not a multiple of 8
+    ({"B": 0}, E_INVALID),
+    ({"slots": 4}, E_INVALID),       # shorter than a region
+    ({"slots": 524}, E_INVALID),     # not a multiple of the region
+    ({"rsb": 520 * 256 - 8}, E_INVALID),
+    ({"eps": -1.0}, E_INVALID),
+    ({"rope_rows": 7}, E_INVALID),
+    ({"R_cap": 0}, E_INVALID),
+    ({"ssb": 16384 * 256 - 16}, E_INVALID),
+    ({"ssb": 16384 * 256 + 8}, E_INVALID),
+    ({"flags": 2}, E_INVALID),       # unknown flag bit
+    ({"flags": 1, "k": None}, E_INVALID),
+    ({"q_heads": 32}, E_UNSUPPORTED),
+])
+def test_append_rejections(s5, over, code):
+    if "q_heads" in over:
+        g = geom(s5, q_heads=over.pop("q_heads"))
+        assert s5.lib().step5_index_append(C.byref(g), 0, A, A, 256, A, A, 16, A, A, 16, 520,
+                                           520 * 256, A, A, 1e-6, A, 131072, A, 16384 * 256,
+                                           16384, None) == code
+        return
+    assert _append(s5, **over) == code
 
 
 def _score(s5, **over):

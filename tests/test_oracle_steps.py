@@ -252,6 +252,60 @@ def test_summary_only_writes_completed_regions(orc):
         orc.summarize(k16, z16, 12, ln_w, ln_b, EPS, rope, R_cap=8)     # t0 not a region start
 
 
+# ---- incremental cache update (k/z rings + summary on region completion) ----
+
+def _stream(orc, k16, z16, ln_w, ln_b, rope, slots, chunks, R_cap):
+    """Feed B sequences' tokens through orc.append in the given chunk sizes
+    (every sequence the same chunk at once); returns rings and summary."""
+    B, T = k16.shape[:2]
+    k_ring = np.zeros((B, slots, 4, 64), np.uint16)
+    z_ring = np.zeros((B, slots, 4, 64), np.uint16)
+    S = np.full((B, R_cap, 4, 64), 0x55, np.uint8)
+    t = 0
+    for n in chunks:
+        pos = np.repeat(np.arange(t, t + n)[None], B, 0).reshape(-1)
+        seq = np.repeat(np.arange(B, dtype=np.int32)[:, None], n, 1).reshape(-1)
+        orc.append(k16[:, t:t + n].reshape(-1, 4, 64), z16[:, t:t + n].reshape(-1, 4, 64), seq, pos,
+                   k_ring, z_ring, ln_w, ln_b, EPS, rope, S)
+        t += n
+    assert t == T
+    return k_ring, z_ring, S
+
+
+@pytest.mark.parametrize("chunks", [[1] * 61, [5, 11, 16, 1, 7, 13, 8], [3, 17, 17, 17, 7]])
+def test_append_equals_batch_summary(orc, chunks):
+    """Tokens appended one at a time or in chunks (each within the ring's
+    reach, slots - 7) leave exactly the summaries the batch summary writes
+    from the contiguous k and z, and nothing for the open region."""
+    k16, z16, ln_w, ln_b, rope = _summary_inputs(23, B=2, T=61)
+    R_cap = 9
+    _, _, S = _stream(orc, k16, z16, ln_w, ln_b, rope, slots=24, chunks=chunks, R_cap=R_cap)
+    want = orc.summarize(k16, z16, 0, ln_w, ln_b, EPS, rope, R_cap=R_cap,
+                         summary=np.full((2, R_cap, 4, 64), 0x55, np.uint8))
+    assert np.array_equal(S, want)
+    assert np.all(S[:, 7:] == 0x55)          # tokens 56..60 leave region 7 open
+
+
+def test_append_ring_holds_latest_token_per_slot(orc):
+    k16, z16, ln_w, ln_b, rope = _summary_inputs(5, B=1, T=40)
+    k_ring, z_ring, _ = _stream(orc, k16, z16, ln_w, ln_b, rope, slots=16, chunks=[9, 9, 9, 9, 4],
+                                R_cap=5)
+    for i in range(16):
+        last = max(p for p in range(40) if p % 16 == i)
+        assert np.array_equal(k_ring[0, i], k16[0, last]) and np.array_equal(z_ring[0, i], z16[0, last])
+
+
+def test_append_skips_invalid_rows(orc):
+    k16, z16, ln_w, ln_b, rope = _summary_inputs(7, B=2, T=8)
+    k_ring = np.zeros((2, 8, 4, 64), np.uint16)
+    z_ring = np.zeros((2, 8, 4, 64), np.uint16)
+    S = np.full((2, 1, 4, 64), 0x55, np.uint8)
+    # sequence 2 does not exist, -1 is no sequence, position 8 is region 1 >= R_cap
+    orc.append(k16[0, :3], z16[0, :3], np.array([2, -1, 0], np.int32), np.array([7, 7, 8]),
+               k_ring, z_ring, ln_w, ln_b, EPS, rope, S)
+    assert np.all(k_ring == 0) and np.all(z_ring == 0) and np.all(S == 0x55)
+
+
 # ---- scores ----------------------------------------------------------------
 
 def test_score_dyadic_closed_form(orc):

@@ -84,6 +84,15 @@ struct ScoreArgs {
 #define S5_EXACT_MAX_ROWS 64
 #endif
 inline bool score_exact_mode(int32_t rows) { return rows <= S5_EXACT_MAX_ROWS; }
+// Interval-mode batches whose units have at most 4,096 candidates (contexts
+// up to 32K tokens: a prefill chunk) skip the score pass: the selection
+// kernel computes each unit's intervals itself (no interval buffer).
+#ifndef S5_FUSED_SELECT_MAX_RCAP
+#define S5_FUSED_SELECT_MAX_RCAP 4096
+#endif
+inline bool select_fused(int32_t rows, int64_t R_cap) {
+  return !score_exact_mode(rows) && R_cap <= S5_FUSED_SELECT_MAX_RCAP;
+}
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream);
 
 // Top-k selection plan: the candidates of a (row, group) are cut into
@@ -100,6 +109,9 @@ size_t topk_partial_bytes(int32_t rows, int64_t R_cap);
 struct TopkArgs {
   const float2* bounds;  // [rows, 4, R_cap] from launch_score
   bool exact;            // bounds holds exact scores (see ScoreArgs)
+  bool fused;            // select_fused: no bounds; intervals computed from q8
+  const uint8_t* q8;     // from launch_qprep, [rows, 16, 64] (fused)
+  int64_t q8_stride_row; // bytes
   const double* q64;     // exact query, for rescoring
   const float* w_head;
   int64_t w_stride_row;

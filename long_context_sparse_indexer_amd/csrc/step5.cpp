@@ -56,8 +56,9 @@ ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   off = up(off + (size_t)rows * kIdxHeads * kIdxDim);
   w.q64 = off;  // its exact fp64 values, [rows, groups, idx_dim, heads per group]
   off = up(off + (size_t)rows * kIdxHeads * kIdxDim * sizeof(double));
-  w.bounds = off;  // score interval per (row, group, candidate)
-  off = up(off + (size_t)rows * kGroups * (size_t)R_cap * 2 * sizeof(float));
+  w.bounds = off;  // score interval per (row, group, candidate), unless fused
+  if (!s5::select_fused(rows, R_cap))
+    off = up(off + (size_t)rows * kGroups * (size_t)R_cap * 2 * sizeof(float));
   w.partial = off;
   off = up(off + s5::topk_partial_bytes(rows, R_cap));
   w.arrivals = off;  // chunk arrival counters per (row, group)
@@ -257,11 +258,17 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
   sa.exact = exact;
   sa.bounds = reinterpret_cast<float2*>(ws + w.bounds);
-  st = from_hip(s5::launch_score(sa, stream));
-  if (st) return st;
+  const bool fused = s5::select_fused(rows, R_cap);
+  if (!fused) {
+    st = from_hip(s5::launch_score(sa, stream));
+    if (st) return st;
+  }
   s5::TopkArgs ta;
   ta.bounds = sa.bounds;
   ta.exact = sa.exact;
+  ta.fused = fused;
+  ta.q8 = q8;
+  ta.q8_stride_row = sa.q8_stride_row;
   ta.q64 = q64;
   ta.w_head = w_head;
   ta.w_stride_row = w_stride_row;

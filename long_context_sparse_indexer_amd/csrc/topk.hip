@@ -42,6 +42,7 @@
 // scanned by all threads at once (two bins each, a block-wide scan).
 #include "device.hpp"
 #include "exact.hpp"
+#include "interval.hpp"
 #include "launch.hpp"
 
 namespace s5 {
@@ -377,9 +378,74 @@ __device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int
   if ((int)threadIdx.x < TK) write_rank_at(v, threadIdx.x, K, unit, sel_ids, sel_scores);
 }
 
-// Appends the candidates tid + 1024 k whose key reaches t to sm.ids (and,
-// with keys, the key to sm.keys), per wave in ballot order; misc[56] holds
-// the count, zero on entry. Returns the total (a barrier comes first).
+// ---------------------------------------------------------------------------
+// Fused intervals (prefill-sized units, up to FUSED_MAX_N candidates): the
+// workgroup of a (row, group) computes its candidates' score intervals on
+// the bf16 matrix cores instead of reading them from memory. A = the row's 4
+// query heads of the group (MFMA rows 0..3, the rest zero), B = 16
+// candidates; output lane n (of the first 16) then holds the 4 head dots of
+// column n, and its interval. Tile t of wave w covers candidates
+// 256 t + 16 w + n: the waves interleave, so that with at least 512
+// candidates every wave holds 32 groups (lane, t mod 4) with one, as the
+// threshold step needs. Keys stay in lanes 0..15, 16 per lane.
+// ---------------------------------------------------------------------------
+constexpr int FUSED_MAX_N = 16 * TK_WAVES * TK_PER;  // 4,096
+
+__device__ inline int32_t fused_id(int tid, int k) {
+  return 256 * k + 16 * (tid >> 6) + (tid & 15);
+}
+
+// The keys of candidate fused_id(tid, t): upper key in kh[t], lower key in
+// kl[fused_id] (LDS, for the rare cut by lower keys), absent ones 0; mx gets
+// the thread's 4 group maxima of lower keys. q8r: the row's prepared query
+// [16 heads][64]; Sg: the sequence's summary at group g (candidate stride
+// 256 B); N >= 1 candidates.
+__device__ inline void fused_keys(uint32_t (&kh)[TK_PER], uint32_t (&mx)[4], uint32_t* kl,
+                                  const uint8_t* __restrict__ q8r, const uint8_t* __restrict__ Sg,
+                                  int g, int N, const float* w4, int tid) {
+  const int lane = tid & 63, n = lane & 15, qd = lane >> 4;
+  const int wave = tid >> 6;
+  // the query stays packed (widened per tile) and tiles go two at a time,
+  // within the selection's 64-register cap
+  uint4 araw = n < 4 ? ldg16(q8r + (4 * g + n) * 64 + 16 * qd) : make_uint4(0, 0, 0, 0);
+  const uint32_t jmax = (uint32_t)(N - 1);
+#pragma unroll
+  for (int k = 0; k < TK_PER; ++k) kh[k] = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mx[i] = 0u;
+#pragma unroll
+  for (int b = 0; b < TK_PER / 2; ++b) {
+    if (2 * 256 * b >= N) break;  // block-uniform
+    // re-widened every pair of tiles, not hoisted out of the loop (16 more
+    // registers for the whole loop would spill)
+    asm volatile("" : "+v"(araw.x), "+v"(araw.y), "+v"(araw.z), "+v"(araw.w));
+    uint4 bq[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t j = min((uint32_t)(256 * (2 * b + u) + 16 * wave + n), jmax);
+      bq[u] = ldg16(Sg + j * 256u + 16 * qd);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = 2 * b + u;
+      f32x4 d, a;
+      dot64(widen16(araw), widen16(bq[u]), d, a);
+      const float2 iv = score_interval(d, a, w4);
+      const int j = 256 * t + 16 * wave + n;
+      const bool ok = qd == 0 && j < N;
+      const uint32_t lo = ok ? ord_key(iv.x) : 0u;
+      kh[t] = ok ? ord_key(iv.y) : 0u;
+      mx[t & 3] = lo > mx[t & 3] ? lo : mx[t & 3];
+      if (ok) kl[j] = lo;
+    }
+  }
+}
+
+// Appends the candidates whose key reaches t to sm.ids (and, with keys, the
+// key to sm.keys), per wave in ballot order; misc[56] holds the count, zero
+// on entry. Returns the total (a barrier comes first). Key k of thread tid is
+// candidate j0 + tid + 1024 k, or with FUSED the candidate fused_id gives.
+template <bool FUSED = false>
 __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_PER], uint32_t t,
                                    int64_t j0, bool keys) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -398,7 +464,7 @@ __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_
     if (msk[k]) {
       if (lane_in(msk[k])) {
         const uint32_t pos = base + lanes_below(msk[k]);
-        sm.ids[pos] = (int32_t)(j0 + tid + TK_THREADS * k);
+        sm.ids[pos] = FUSED ? fused_id(tid, k) : (int32_t)(j0 + tid + TK_THREADS * k);
         if (keys) sm.keys[pos] = key[k];
       }
       base += (uint32_t)__popcll(msk[k]);
@@ -477,18 +543,26 @@ __device__ inline void rescore_survivors(const TkShared& sm, int M, const double
 // One chunk of a (row, group)'s candidates: threshold, survivors, exact
 // rescoring (intervals), exact selection. mode 0: the whole range, final
 // output; mode 1: partial list, merged by the unit's last block.
+// KIND: TK_EXACT reads exact scores from `bounds` (as float), TK_INTERVAL
+// reads intervals, TK_FUSED computes the intervals itself (fused_intervals;
+// one chunk of at most FUSED_MAX_N candidates) from q8 (row stride qs8).
 // Registers are capped for 8 waves per SIMD, so that two 1024-thread blocks
 // share a CU when the chunk's LDS allows it (prefill-sized chunks of 4,096
 // candidates): uncapped, the interval variant's scalar registers held it to
 // one block per CU and 1.6x the time.
-template <bool EXACT>
+enum { TK_EXACT = 0, TK_INTERVAL = 1, TK_FUSED = 2 };
+
+template <int KIND>
 __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_chunk_kernel(
-    int mode, const float2* __restrict__ bounds, int64_t R_cap,
+    int mode, const float2* __restrict__ bounds, const uint8_t* __restrict__ q8, int64_t qs8,
+    int64_t R_cap,
     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int64_t B,
     int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
     int64_t w_stride, const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
     unsigned long long* __restrict__ partial, unsigned* __restrict__ arrivals,
     int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores) {
+  constexpr bool EXACT = KIND == TK_EXACT;
+  constexpr bool FUSED = KIND == TK_FUSED;
   extern __shared__ __align__(16) unsigned char smem[];
   const int64_t unit = blockIdx.x;
   const int c = blockIdx.y;
@@ -498,41 +572,54 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
   const int64_t j0 = (int64_t)c * chunk;
-  // keys of candidates tid + 1024 k in registers. The chunk's slots of the
-  // score buffer are read before the row's candidate count is known (it only
-  // masks them), all loads in flight at once; a lane past the chunk's end
-  // reads its last slot again.
-  const int nslot = (int)((R_cap - j0 < chunk) ? R_cap - j0 : chunk);
+  // keys of candidates tid + 1024 k (fused: fused_id) in registers. The
+  // chunk's slots of the score buffer are read before the row's candidate
+  // count is known (it only masks them), all loads in flight at once; a lane
+  // past the chunk's end reads its last slot again.
   float2 raw[TK_PER];
-#pragma unroll
-  for (int k = 0; k < TK_PER; ++k) {
-    raw[k] = make_float2(0.f, 0.f);
-    if (TK_THREADS * k < nslot) {
-      const int i = min(tid + TK_THREADS * k, nslot - 1);
-      if constexpr (EXACT) {
-        const float s = reinterpret_cast<const float*>(bounds)[unit * R_cap + j0 + i];
-        raw[k] = make_float2(s, s);
-      } else {
-        raw[k] = bounds[unit * R_cap + j0 + i];
-      }
-    }
-  }
   int32_t seq;
   int64_t ncand;
-  unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
   int N = 0;
-  if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
-  const int K = N < TK ? N : TK;
   // the thread's keys (absent candidates 0) and its 4 group maxima
   uint32_t kh[TK_PER];
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
+  uint32_t* const kl_lds = reinterpret_cast<uint32_t*>(sm.xb);  // fused: lower keys by id
+  if constexpr (FUSED) {
+    unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
+    N = (int)(ncand < FUSED_MAX_N ? ncand : FUSED_MAX_N);
+    float w4[4];
 #pragma unroll
-  for (int k = 0; k < TK_PER; ++k) {
-    const bool have = tid + TK_THREADS * k < N;
-    const uint32_t lo = have ? ord_key(raw[k].x) : 0u;
-    kh[k] = EXACT ? lo : (have ? ord_key(raw[k].y) : 0u);
-    mx[k & 3] = lo > mx[k & 3] ? lo : mx[k & 3];
+    for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
+#pragma unroll
+    for (int k = 0; k < TK_PER; ++k) kh[k] = 0u;
+    if (N > 0)  // block-uniform
+      fused_keys(kh, mx, kl_lds, q8 + row * qs8, S + (int64_t)seq * ssb + g * 64, g, N, w4, tid);
+  } else {
+    const int nslot = (int)((R_cap - j0 < chunk) ? R_cap - j0 : chunk);
+#pragma unroll
+    for (int k = 0; k < TK_PER; ++k) {
+      raw[k] = make_float2(0.f, 0.f);
+      if (TK_THREADS * k < nslot) {
+        const int i = min(tid + TK_THREADS * k, nslot - 1);
+        if constexpr (EXACT) {
+          const float s = reinterpret_cast<const float*>(bounds)[unit * R_cap + j0 + i];
+          raw[k] = make_float2(s, s);
+        } else {
+          raw[k] = bounds[unit * R_cap + j0 + i];
+        }
+      }
+    }
+    unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
+    if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
+#pragma unroll
+    for (int k = 0; k < TK_PER; ++k) {
+      const bool have = tid + TK_THREADS * k < N;
+      const uint32_t lo = have ? ord_key(raw[k].x) : 0u;
+      kh[k] = EXACT ? lo : (have ? ord_key(raw[k].y) : 0u);
+      mx[k & 3] = lo > mx[k & 3] ? lo : mx[k & 3];
+    }
   }
+  const int K = N < TK ? N : TK;
   // 1. tau = least over the waves of the wave's 32nd largest group maximum
   //    (at least 1: absent candidates, key 0, never survive)
   const uint32_t tw = wave_kth_largest4(mx, TK / TK_WAVES);
@@ -548,24 +635,28 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   }
   // 2. survivors: upper key >= tau, appended per wave (their order is free:
   //    the selection sorts by (key, id))
-  int M = compact_keys(sm, kh, tau, j0, EXACT);
+  int M = compact_keys<FUSED>(sm, kh, tau, j0, EXACT);
   if constexpr (!EXACT) {
     if (M > TK_SORT) {
       // too many to sort directly: cut by T from the lower keys >= tau
       uint32_t kl[TK_PER];
 #pragma unroll
       for (int k = 0; k < TK_PER; ++k) {
-        const bool have = tid + TK_THREADS * k < N;
-        kl[k] = have ? ord_key(raw[k].x) : 0u;
+        if constexpr (FUSED) {
+          const int j = fused_id(tid, k);
+          kl[k] = (lane < 16 && j < N) ? kl_lds[j] : 0u;
+        } else {
+          kl[k] = tid + TK_THREADS * k < N ? ord_key(raw[k].x) : 0u;
+        }
       }
       if (tid == 0) sm.misc[56] = 0u;
       __syncthreads();
-      M = compact_keys(sm, kl, tau, j0, true);
+      M = compact_keys<FUSED>(sm, kl, tau, j0, true);
       const Boundary bd = radix_boundary(sm, M, K, 2);
       const uint32_t T = bd.P > 1u ? bd.P : 1u;
       if (tid == 0) sm.misc[56] = 0u;
       __syncthreads();
-      M = compact_keys(sm, kh, T, j0, false);
+      M = compact_keys<FUSED>(sm, kh, T, j0, false);
     }
     // 3. exact scores of the survivors (matrix cores)
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
@@ -671,26 +762,38 @@ size_t topk_partial_bytes(int32_t rows, int64_t R_cap) {
 
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  const TopkPlan p = topk_plan(a.rows, a.R_cap);
   const unsigned units = (unsigned)a.rows * 4u;
+  if (a.fused) {
+    const size_t sm = tk_smem_bytes(FUSED_MAX_N);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel<TK_FUSED>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_chunk_kernel<TK_FUSED>, dim3(units, 1), dim3(TK_THREADS), sm, stream,
+                       0, nullptr, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb,
+                       (int64_t)FUSED_MAX_N, 1, a.partial, a.arrivals, a.sel_ids, a.sel_scores);
+    return hipGetLastError();
+  }
+  const TopkPlan p = topk_plan(a.rows, a.R_cap);
   size_t sm = tk_smem_bytes((int)p.chunk);
   const size_t sm_merge = (size_t)(p.nchunks + 4) * TK * sizeof(unsigned long long);
   if (p.nchunks > 1 && sm_merge > sm) sm = sm_merge;
-  const void* fn = a.exact ? (const void*)topk_chunk_kernel<true> : (const void*)topk_chunk_kernel<false>;
+  const void* fn = a.exact ? (const void*)topk_chunk_kernel<TK_EXACT>
+                           : (const void*)topk_chunk_kernel<TK_INTERVAL>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const int mode = p.nchunks == 1 ? 0 : 1;
   const dim3 grid(units, (unsigned)p.nchunks);
   if (a.exact)
-    hipLaunchKernelGGL(topk_chunk_kernel<true>, grid, dim3(TK_THREADS), sm, stream, mode,
-                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit, a.q64,
-                       a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks, a.partial,
-                       a.arrivals, a.sel_ids, a.sel_scores);
+    hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
+                       a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
+                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores);
   else
-    hipLaunchKernelGGL(topk_chunk_kernel<false>, grid, dim3(TK_THREADS), sm, stream, mode,
-                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B, a.pos_limit, a.q64,
-                       a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk, p.nchunks, a.partial,
-                       a.arrivals, a.sel_ids, a.sel_scores);
+    hipLaunchKernelGGL(topk_chunk_kernel<TK_INTERVAL>, grid, dim3(TK_THREADS), sm, stream, mode,
+                       a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
+                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores);
   return hipGetLastError();
 }
 

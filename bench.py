@@ -59,9 +59,9 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle's sample until this much time has passed")
-    ap.add_argument("--extra", default="prefill2048_ctx32k,decode1_ctx1m,hbm_copy",
+    ap.add_argument("--extra", default="prefill2048_ctx32k,decode1_ctx1m,attn_geometry,hbm_copy",
                     help="comma-separated extra lines to measure after the headline "
-                         "(workload names and/or hbm_copy; 'none' for none)")
+                         "(workload names, attn_geometry and/or hbm_copy; 'none' for none)")
     ap.add_argument("--eager", action="store_true", help="launch the calls directly, no HIP graphs")
     return ap.parse_args()
 
@@ -314,6 +314,42 @@ def attn_traffic(workload):
     return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["source_sha256"] else None
 
 
+def attn_geometry(torch, s5):
+    """step5_sparse_attn alone at the 128K decode shape (16 rows, each its own
+    131,072-token sequence at position 131,071, 512 random regions per (row,
+    KV head)) for 4, 8 and 16 query heads per KV head of 128 dims and 16 of
+    192 (Step-5's own layer shape). Algorithmic bytes: the K and V rows the
+    selection names, D x 2 bytes each, per (row, KV head)."""
+    rows, T = 16, 131072
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    pos = torch.full((rows,), T - 1, dtype=torch.int64, device=dev)
+    seq = torch.arange(rows, dtype=torch.int32, device=dev)
+    ids = torch.stack([torch.randperm(T // 8 - 1, generator=g, device=dev)[:512]
+                       for _ in range(rows * 4)]).to(torch.int32).view(rows, 4, 512).contiguous()
+    res = {"shape": f"{rows} rows x {T} tokens, 512 regions + own per (row, KV head)"}
+    for D, hqs in ((128, (16, 32, 64)), (192, (64,))):
+        k = torch.randn((rows, T, 4, D), generator=g, device=dev, dtype=torch.bfloat16)
+        v = torch.randn((rows, T, 4, D), generator=g, device=dev, dtype=torch.bfloat16)
+        for Hq in hqs:
+            q = torch.randn((rows, Hq, D), generator=g, device=dev, dtype=torch.bfloat16)
+            out = torch.empty((rows, Hq, D), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((rows, Hq), dtype=torch.float32, device=dev)
+            nb = s5.step5_sparse_attn_workspace(rows, Hq, D)
+            ws = torch.empty(max(1, nb) + 256, dtype=torch.uint8, device=dev)
+            ws = ws[(-ws.data_ptr()) % 256:]
+            f = lambda: s5.step5_sparse_attn(q, k, v, ids, seq, pos, 1.0 / math.sqrt(D), out, lse,
+                                             workspace=ws)
+            us = Timer(torch, [("attn", f)], 3, False).per_call()["attn"]
+            b = rows * 4 * (8 * 512 + 8) * D * 2 * 2
+            res[f"q{Hq}_d{D}"] = {"heads_per_kv": Hq // 4, "us": round(us, 2),
+                                  "algorithmic_bytes": b, "GBs": round(b / us / 1e3, 1),
+                                  "frac_hbm": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del k, v
+    return res
+
+
 def copy_ceiling(torch):
     """A plain device-to-device copy of 1 GiB: the HBM rate a streaming kernel
     reaches on this GPU (read + write bytes per second)."""
@@ -352,6 +388,10 @@ def main():
         if name == "hbm_copy":
             log("plain copy of 1 GiB")
             extra[name] = copy_ceiling(torch)
+        elif name == "attn_geometry":
+            log("sparse attention of other query-head geometries at the 128K decode shape")
+            extra[name] = attn_geometry(torch, s5)
+            torch.cuda.empty_cache()
         elif name != args.workload:
             r, dd, SS = run_workload(name, args, torch, s5, W)
             del dd, SS

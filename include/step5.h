@@ -58,9 +58,12 @@
 extern "C" {
 #endif
 
-/* Layer geometry. Supported: {16, 4, 64, 32, 8, 512, 16, 4, 128}, the
- * Step-5 full-attention layer with 4 query heads per KV head. Geometry that
- * breaks the rules above is STEP5_E_INVALID; other valid geometry is
+/* Layer geometry. Supported: the indexer part {16, 4, 64, 32, 8, 512} with
+ * 4 KV heads, q_heads 16, 32 or 64 (4, 8 or 16 per KV head) and head_dim 128
+ * or 192 ({..., 16, 4, 128} is the configuration of the workloads; 64 heads
+ * of 192 dims is the TensorFold page's shape of Step-5's layers). Only
+ * step5_sparse_attn depends on q_heads and head_dim. Geometry that breaks
+ * the rules above is STEP5_E_INVALID; other valid geometry is
  * STEP5_E_UNSUPPORTED. */
 typedef struct step5_geom {
   int32_t idx_heads; /* indexer query heads (16) */
@@ -69,9 +72,9 @@ typedef struct step5_geom {
   int32_t rope_dim;  /* NEOX-rotated leading dims of the indexer q and k (32) */
   int32_t region;    /* tokens per region (8) */
   int32_t topk;      /* regions kept per (row, group) (512) */
-  int32_t q_heads;   /* attention query heads (16) */
+  int32_t q_heads;   /* attention query heads (16, 32 or 64) */
   int32_t kv_heads;  /* attention KV heads (4) */
-  int32_t head_dim;  /* attention head dim (128) */
+  int32_t head_dim;  /* attention head dim (128 or 192) */
 } step5_geom;
 
 enum {

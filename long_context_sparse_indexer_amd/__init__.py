@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "Step5Error", "GEOM", "lib", "step5_status_str", "step5_index_summarize",
     "step5_index_append", "step5_index_score_topk", "step5_index_score_topk_workspace", "step5_sparse_attn",
-    "step5_sparse_attn_workspace", "STEP5_Q_E4M3", "STEP5_APPEND_ONE_PER_SEQ",
+    "step5_sparse_attn_workspace", "attn_geom", "STEP5_Q_E4M3", "STEP5_APPEND_ONE_PER_SEQ",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstep5.so")
@@ -180,8 +180,15 @@ def step5_index_score_topk_workspace(rows: int, R_cap: int) -> int:
     return int(lib().step5_index_score_topk_workspace(C.byref(GEOM), int(rows), int(R_cap)))
 
 
-def step5_sparse_attn_workspace(rows: int) -> int:
-    return int(lib().step5_sparse_attn_workspace(C.byref(GEOM), int(rows)))
+def attn_geom(q_heads: int = Q_HEADS, head_dim: int = HEAD_DIM) -> Step5Geom:
+    """The layer geometry with the given attention query heads (4, 8 or 16 per
+    KV head) and head dim (128 or 192); the indexer part is fixed."""
+    return Step5Geom(IDX_HEADS, GROUPS, IDX_DIM, ROPE_DIM, 8, TOPK, int(q_heads), KV_HEADS,
+                     int(head_dim))
+
+
+def step5_sparse_attn_workspace(rows: int, q_heads: int = Q_HEADS, head_dim: int = HEAD_DIM) -> int:
+    return int(lib().step5_sparse_attn_workspace(C.byref(attn_geom(q_heads, head_dim)), int(rows)))
 
 
 def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
@@ -238,27 +245,31 @@ def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       softmax_scale: float, out: torch.Tensor,
                       out_lse: Optional[torch.Tensor] = None, *,
                       workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Attention over selected regions plus the own region into out (bf16 [rows, 16, 128])."""
+    """Attention over selected regions plus the own region into out (bf16 [rows, Hq, D]).
+    The geometry comes from q: Hq query heads (16, 32 or 64: 4, 8 or 16 per KV
+    head) of D = 128 or 192 dims; k_cache, v_cache bf16 [B, T, 4, D]."""
     rows = q.shape[0]
-    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and tuple(q.shape[1:]) == (Q_HEADS, HEAD_DIM)
-          and q.stride(2) == 1 and q.stride(1) == HEAD_DIM, "q must be bf16 [rows, 16, 128]")
+    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.stride(2) == 1 and
+          q.stride(1) == q.shape[2], "q must be bf16 [rows, Hq, D] with contiguous heads")
+    Hq, D = q.shape[1], q.shape[2]
     _need(k_cache.dtype == torch.bfloat16 and v_cache.dtype == torch.bfloat16 and
           k_cache.shape == v_cache.shape and k_cache.stride() == v_cache.stride() and
-          k_cache.dim() == 4 and tuple(k_cache.shape[2:]) == (KV_HEADS, HEAD_DIM) and
-          k_cache.stride(3) == 1 and k_cache.stride(2) == HEAD_DIM,
-          "k_cache, v_cache must be bf16 [B, T, 4, 128] with equal strides")
+          k_cache.dim() == 4 and tuple(k_cache.shape[2:]) == (KV_HEADS, D) and
+          k_cache.stride(3) == 1 and k_cache.stride(2) == D,
+          "k_cache, v_cache must be bf16 [B, T, 4, D] with equal strides")
     _need(sel_ids.dtype == torch.int32 and tuple(sel_ids.shape) == (rows, GROUPS, TOPK) and
           sel_ids.is_contiguous(), "sel_ids must be int32 [rows, 4, 512]")
-    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (rows, Q_HEADS, HEAD_DIM) and
-          out.is_contiguous(), "out must be contiguous bf16 [rows, 16, 128]")
+    _need(out.dtype == torch.bfloat16 and tuple(out.shape) == (rows, Hq, D) and
+          out.is_contiguous(), "out must be contiguous bf16 [rows, Hq, D]")
     if out_lse is not None:
-        _need(out_lse.dtype == torch.float32 and tuple(out_lse.shape) == (rows, Q_HEADS) and
-              out_lse.is_contiguous(), "out_lse must be fp32 [rows, 16]")
+        _need(out_lse.dtype == torch.float32 and tuple(out_lse.shape) == (rows, Hq) and
+              out_lse.is_contiguous(), "out_lse must be fp32 [rows, Hq]")
     _need(row_seq.dtype == torch.int32 and row_pos.dtype == torch.int64, "row_seq int32, row_pos int64")
-    nbytes = step5_sparse_attn_workspace(rows)
+    geom = attn_geom(Hq, D)
+    nbytes = int(lib().step5_sparse_attn_workspace(C.byref(geom), int(rows)))
     workspace = _workspace(nbytes, q.device, workspace)
     st = lib().step5_sparse_attn(
-        C.byref(GEOM), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+        C.byref(geom), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
         k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _ptr(sel_ids), _ptr(row_seq),
         _ptr(row_pos), rows, float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         nbytes, _stream(stream))

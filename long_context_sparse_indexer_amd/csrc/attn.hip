@@ -381,6 +381,7 @@ size_t attn_workspace_bytes(int32_t rows) {
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
+  if (a.qpk != 4 || a.head_dim != 128) return launch_attn_mh(a, stream);
   const AttnPlan pl = attn_plan(a.rows);
   const unsigned units = (unsigned)a.rows * 4u;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);

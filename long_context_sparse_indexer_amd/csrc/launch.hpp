@@ -139,6 +139,8 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int32_t rows);
 size_t attn_workspace_bytes(int32_t rows);
+// the same for qpk query heads per KV head and a head dim of 128 or 192
+size_t attn_mh_workspace_bytes(int32_t rows, int32_t qpk, int32_t head_dim);
 
 struct AttnArgs {
   const void* q;
@@ -150,11 +152,15 @@ struct AttnArgs {
   const int32_t* row_seq;
   const int64_t* row_pos;
   int32_t rows;
+  int32_t qpk;       // query heads per KV head (4, 8, 16)
+  int32_t head_dim;  // 128 or 192
   float scale;
   void* out;
   float* lse;
   float* partial;
 };
+// qpk 4, head dim 128: attn_kernel (attn.hip); the rest: attn_mh_kernel (attn_mh.hip)
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_mh(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace s5

@@ -17,7 +17,7 @@
 namespace {
 
 constexpr int32_t kIdxHeads = 16, kGroups = 4, kIdxDim = 64, kRopeDim = 32, kRegion = 8,
-                  kTopk = 512, kQHeads = 16, kKvHeads = 4, kHeadDim = 128;
+                  kTopk = 512, kKvHeads = 4;
 constexpr int64_t kRegionBytes = (int64_t)kGroups * kIdxDim;  // e4m3 summary bytes per region
 constexpr int64_t kMaxRcap = 524288;                            // 32 chunks of 16,384 candidates
 constexpr int32_t kMaxScoreRows = 65535 * 4;                    // score grid: 4 rows per block row
@@ -39,7 +39,7 @@ int check_geom(const step5_geom* g) {
   if (g->rope_dim > g->idx_dim || (g->rope_dim & 1)) return STEP5_E_INVALID;
   if (g->idx_heads != kIdxHeads || g->groups != kGroups || g->idx_dim != kIdxDim ||
       g->rope_dim != kRopeDim || g->region != kRegion || g->topk != kTopk ||
-      g->q_heads != kQHeads || g->kv_heads != kKvHeads || g->head_dim != kHeadDim)
+      g->kv_heads != kKvHeads || (g->head_dim != 128 && g->head_dim != 192))
     return STEP5_E_UNSUPPORTED;
   return STEP5_OK;
 }
@@ -289,7 +289,10 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
 
 STEP5_EXPORT size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows) {
   if (check_geom(geom) || rows <= 0 || rows > (INT32_MAX / 4)) return 0;
-  const size_t b = s5::attn_workspace_bytes(rows);
+  const int32_t qpk = geom->q_heads / geom->kv_heads;
+  const size_t b = (qpk == 4 && geom->head_dim == 128)
+                       ? s5::attn_workspace_bytes(rows)
+                       : s5::attn_mh_workspace_bytes(rows, qpk, geom->head_dim);
   return b ? up(b) : 0;
 }
 
@@ -305,11 +308,12 @@ STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_
   if (rows < 0) return STEP5_E_INVALID;
   if (rows == 0) return STEP5_OK;
   if (rows > INT32_MAX / 4) return STEP5_E_UNSUPPORTED;
-  if (!q || !aligned(q, 16) || q_stride_row < (int64_t)kQHeads * kHeadDim || (q_stride_row % 8))
+  const int64_t hd = geom->head_dim;
+  if (!q || !aligned(q, 16) || q_stride_row < (int64_t)geom->q_heads * hd || (q_stride_row % 8))
     return STEP5_E_INVALID;
   if (!k_cache || !v_cache || !aligned(k_cache, 16) || !aligned(v_cache, 16)) return STEP5_E_INVALID;
   if (B < 1 || T_cap < 1) return STEP5_E_INVALID;
-  if (kv_stride_t < (int64_t)kKvHeads * kHeadDim || (kv_stride_t % 8)) return STEP5_E_INVALID;
+  if (kv_stride_t < (int64_t)kKvHeads * hd || (kv_stride_t % 8)) return STEP5_E_INVALID;
   if (kv_stride_b < 0 || (kv_stride_b % 8)) return STEP5_E_INVALID;
   if (B > 1 && kv_stride_b < T_cap * kv_stride_t) return STEP5_E_INVALID;
   if (!sel_ids || !aligned(sel_ids, 4)) return STEP5_E_INVALID;
@@ -333,6 +337,8 @@ STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_
   a.row_seq = row_seq;
   a.row_pos = row_pos;
   a.rows = rows;
+  a.qpk = geom->q_heads / geom->kv_heads;
+  a.head_dim = geom->head_dim;
   a.scale = softmax_scale;
   a.out = out;
   a.lse = out_lse;

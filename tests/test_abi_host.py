@@ -65,9 +65,13 @@ def test_status_strings(s5):
     ({"q_heads": 12}, E_INVALID),               # 3 per KV head
     ({"rope_dim": 33}, E_INVALID),
     ({"topk": 0}, E_INVALID),
-    ({"q_heads": 32}, E_UNSUPPORTED),           # 8 per KV head: valid, not built
-    ({"q_heads": 64}, E_UNSUPPORTED),           # 16 per KV head
-    ({"head_dim": 192}, E_UNSUPPORTED),
+    ({"q_heads": 32}, OK),                      # 8 per KV head
+    ({"q_heads": 64}, OK),                      # 16 per KV head
+    ({"head_dim": 192}, OK),
+    ({"q_heads": 64, "head_dim": 192}, OK),     # Step-5's own layer shape
+    ({"head_dim": 256}, E_UNSUPPORTED),
+    ({"head_dim": 64}, E_UNSUPPORTED),
+    ({"groups": 8, "kv_heads": 8, "q_heads": 32}, E_UNSUPPORTED),  # valid rules, 8 groups not built
     ({"topk": 256}, E_UNSUPPORTED),
 ])
 def test_geometry_rules(s5, kw, code):
@@ -154,11 +158,11 @@ def _append(s5, **over):
     ({"ssb": 16384 * 256 + 8}, E_INVALID),
     ({"flags": 2}, E_INVALID),       # unknown flag bit
     ({"flags": 1, "k": None}, E_INVALID),
-    ({"q_heads": 32}, E_UNSUPPORTED),
+    ({"head_dim": 256}, E_UNSUPPORTED),
 ])
 def test_append_rejections(s5, over, code):
-    if "q_heads" in over:
-        g = geom(s5, q_heads=over.pop("q_heads"))
+    if "head_dim" in over:
+        g = geom(s5, head_dim=over.pop("head_dim"))
         assert s5.lib().step5_index_append(C.byref(g), 0, A, A, 256, A, A, 16, A, A, 16, 520,
                                            520 * 256, A, A, 1e-6, A, 131072, A, 16384 * 256,
                                            16384, None) == code
@@ -274,6 +278,24 @@ def _attn(s5, **over):
 ])
 def test_sparse_attn_rejections(s5, over, code):
     assert _attn(s5, **over) == code
+
+
+def test_sparse_attn_geometry_strides_and_workspace(s5):
+    """16 query heads per KV head of 192 dims: q rows need 64 x 192 elements,
+    K/V token rows 4 x 192, and the split states grow with the heads and dims."""
+    L = s5.lib()
+    g = geom(s5, q_heads=64, head_dim=192)
+    need = L.step5_sparse_attn_workspace(C.byref(g), 16)
+    assert need >= 16 * 4 * 2 * 16 * 194 * 4        # at least 2 splits of 16 heads x (m, l, o)
+    assert need > L.step5_sparse_attn_workspace(C.byref(geom(s5)), 16)
+
+    def call(qs, kvt):
+        return L.step5_sparse_attn(C.byref(g), A, qs, A, A, 16, 4096 * kvt, kvt, 4096, A, A, A, 16,
+                                   0.072, A, None, None if need == 0 else A, need, None)
+    assert call(64 * 192 - 8, 4 * 192) == E_INVALID
+    assert call(64 * 192, 4 * 192 - 8) == E_INVALID
+    assert L.step5_sparse_attn(C.byref(g), A, 64 * 192, A, A, 16, 4096 * 768, 768, 4096, A, A, A,
+                               16, 0.072, A, None, A, need - 1, None) == E_WORKSPACE
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):

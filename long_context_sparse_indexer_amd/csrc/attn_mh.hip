@@ -6,24 +6,27 @@
 // summed in fp32, probabilities applied to the values as bf16 parts). vLLM's
 // geometry rules allow 4, 8 or 16 query heads per KV head.
 //
-// The unit's entries (own region first, then the selected regions), the
-// splits and the fixed-order merges are those of attn.hip. Per 32-token
-// chunk, per wave:
+// The unit's entries (own region first, then the selected regions) and the
+// fixed-order split merge are those of attn.hip. A workgroup takes one split
+// and walks it in 32-token chunks (4 entries), all four waves on the same
+// chunk:
+//  - the chunk's K and V rows go straight from memory into LDS
+//    (global_load_lds, 16 B per lane, no registers), double-buffered so the
+//    next chunk loads while this one is computed. A token row's 16-byte
+//    pieces are stored in XOR-swizzled slots, so that the reads below fall
+//    in distinct LDS banks;
 //  - S = Q K^T on the 16x16x32 bf16 MFMA: A = the unit's query heads (MFMA
-//    rows; rows past QPK are zero), B = 16 gathered key tokens; each lane
-//    loads D/4 contiguous dims of one token (the MFMAs take its 16-byte
-//    slices in turn, the same slices of the query), so K needs no reordering;
+//    rows; rows past QPK are zero), B = 16 key tokens, each lane's D/4 dims
+//    read from LDS as 16-byte slices; every wave computes all of S;
 //  - online softmax in the log2 domain per head: output lane (n, qd) holds
-//    heads 4qd..4qd+3 for token n, so a head's max and sum are reductions
-//    over one 16-lane row;
-//  - O += P V on the same MFMA: A = P (heads x 32 tokens), split into a bf16
-//    high part and the bf16 of the remainder (two MFMAs, error ~2^-17 of P),
-//    staged through LDS to reach the operand layout; B = V with tokens along
-//    the contraction, which puts 8 tokens of one dim in a lane: V is staged
-//    in LDS in its row layout (rows padded by one dword so the lanes of a
-//    read fall in distinct banks) and read back 2 bytes at a time.
-// Output lane (n, qd) of the PV MFMA holds heads 4qd..4qd+3 of dim 16c + n,
-// the same heads as the softmax state it is rescaled by.
+//    heads 4qd..4qd+3 for token n, a head's max and sum are reductions over
+//    one 16-lane row; the state is the same in every wave;
+//  - O += P V on the same MFMA, each wave for a quarter of the dims: A = P
+//    (heads x 32 tokens), split into a bf16 high part and the bf16 of the
+//    remainder (two MFMAs, error ~2^-17 of P), through LDS to reach the
+//    operand layout; B = V with tokens along the contraction, read from LDS
+//    2 bytes at a time (8 tokens of one dim per lane).
+// The waves' states need no merge: each holds its own dims.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -37,12 +40,13 @@ template <int QPK, int D>
 struct MhCfg {
   static constexpr int KS = D / 32;               // QK^T MFMA steps of 32 dims
   static constexpr int NT = D / 16;               // PV output tiles of 16 dims
+  static constexpr int TPW = NT / 4;              // PV tiles per wave
   static constexpr int PIECES = D / 8;            // 16-byte pieces of a token row
-  static constexpr int VPL = 32 * PIECES / 64;    // V pieces per lane per chunk (D / 16)
-  static constexpr int VROW = D + 2;              // staged V row, elements (one dword of padding)
+  static constexpr int CP = 32 * PIECES;          // pieces of a chunk's K (or V)
+  static constexpr int PPT = CP / 256;            // pieces per thread per chunk
   static constexpr int PART = 2 + D;              // split state per head: m, l, o[D]
   static_assert(QPK == 4 || QPK == 8 || QPK == 16, "query heads per KV head");
-  static_assert(D % 32 == 0 && (32 * PIECES) % 64 == 0, "head dim");
+  static_assert(D % 64 == 0 && PIECES % 8 == 0 && CP % 256 == 0, "head dim");
 };
 
 __device__ inline void mh_wave_sync() {
@@ -56,10 +60,19 @@ __device__ inline f32x4 mh_mfma(uint4 a, uint4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <typename T>
-__device__ inline T mh_pick4(int i, T a, T b, T c, T d) {
-  return i < 2 ? (i == 0 ? a : b) : (i == 2 ? c : d);
+// 16 bytes from global memory straight into LDS: the lane's bytes land at
+// lds + 16 * lane (lds the same in every lane)
+__device__ inline void mh_load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
+
+// wait for this wave's loads, those into LDS included
+__device__ inline void mh_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// slot of piece P of chunk token tt: K rows are read 16 B per lane by 8
+// consecutive tokens, V rows 2 B per lane by 16 dims x 4 token groups
+__device__ inline int mh_kslot(int tt, int P) { return P ^ (tt & 7); }
+__device__ inline int mh_vslot(int tt, int P) { return P ^ ((tt & 7) ^ (2 * (tt >> 3))); }
 
 }  // namespace
 
@@ -71,17 +84,18 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
     const int64_t* __restrict__ row_pos, float scale_log2, int per_split, int nsplit,
     float* __restrict__ partial, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using C = MhCfg<QPK, D>;
-  // per wave: the chunk's V rows; after the loop the waves' states (o, then m
-  // and l) for the merge, which need exactly as many bytes
-  __shared__ __align__(16) uint16_t v_lds[4][32 * C::VROW];
-  __shared__ __align__(16) uint16_t p_lds[4][2][16 * 32];  // per wave: P high, low [head][token]
+  __shared__ __align__(16) uint4 kv_lds[2][2][C::CP];         // [buffer][K | V][slot]
+  __shared__ __align__(16) uint16_t p_lds[4][2][16 * 32];     // per wave: P high, low [head][token]
   __shared__ uint32_t ids_lds[512];
+  __shared__ int32_t ent_j[MH_ENTRIES + 3];                   // the split's entries: region id
+  __shared__ uint8_t ent_n[MH_ENTRIES + 3];                   // and token count (0: empty)
 
   const int64_t unit = blockIdx.x;
   const int split = blockIdx.y;
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, qd = lane >> 4;
 
   const int32_t seq = row_seq[row];
@@ -91,12 +105,11 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
   const int nent = valid ? 1 + (int)(ncand < 512 ? ncand : 512) : 0;
   const int e0 = split * per_split;
   const int e1 = min(e0 + per_split, nent);
-  const int wb = e0 + 4 * wave;
-  const int niter = wb < e1 ? (e1 - wb + 15) >> 4 : 0;
+  const int nch = e1 > e0 ? (e1 - e0 + 3) >> 2 : 0;
   const int32_t* sl = sel + unit * 512;
   if (nsplit == 1) {
     // unsplit (many rows): visit the selected regions in id order, as attn.hip does
-    for (int i = threadIdx.x; i < 512; i += 256) ids_lds[i] = (uint32_t)sl[i];
+    for (int i = tid; i < 512; i += 256) ids_lds[i] = (uint32_t)sl[i];
     __syncthreads();
 #pragma unroll 1
     for (int kk = 2; kk <= 512; kk <<= 1)
@@ -104,7 +117,7 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
       for (int jj = kk >> 1; jj > 0; jj >>= 1) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int i = threadIdx.x + 256 * h;
+          const int i = tid + 256 * h;
           const int pi = i ^ jj;
           if (pi > i) {
             const uint32_t a = ids_lds[i], b = ids_lds[pi];
@@ -119,27 +132,47 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
       }
     sl = reinterpret_cast<const int32_t*>(ids_lds);
   }
-  // lane 4 (i % 16) + e4 describes entry wb + 16 i + e4 of this wave
-  int64_t lj = 0;
-  int lcnt = 0;
-  auto load_table = [&](int ibase) {
-    const int e = wb + 16 * (ibase + (lane >> 2)) + (lane & 3);
-    lj = 0;
-    lcnt = 0;
-    if (e < e1) {
-      if (e == 0) {
-        lj = p >> 3;
-        lcnt = (int)(p & 7) + 1;
+  // the split's entries, padded to whole chunks with empty ones
+  for (int e = tid; e < 4 * nch; e += 256) {
+    const int ge = e0 + e;
+    int32_t j = 0;
+    int cnt = 0;
+    if (ge < e1) {
+      if (ge == 0) {
+        j = (int32_t)(p >> 3);
+        cnt = (int)(p & 7) + 1;
       } else {
-        const int32_t j = sl[e - 1];
-        if (j >= 0 && j < ncand) {
-          lj = j;
-          lcnt = 8;
+        const int32_t s = sl[ge - 1];
+        if (s >= 0 && s < ncand) {
+          j = s;
+          cnt = 8;
         }
       }
     }
+    ent_j[e] = j;
+    ent_n[e] = (uint8_t)cnt;
+  }
+  __syncthreads();
+
+  const int64_t sb = valid ? (int64_t)seq * kv_sb : 0;
+  const uint16_t* kb = kc + sb + (int64_t)g * D;
+  const uint16_t* vb = vc + sb + (int64_t)g * D;
+  const int64_t pc = valid ? p : 0;  // a token that is always in range
+  // chunk c into buffer bf: thread tid fills slots r * 256 + tid of K and V
+  auto stage = [&](int c, int bf) {
+#pragma unroll
+    for (int r = 0; r < C::PPT; ++r) {
+      const int s = r * 256 + tid;
+      const int tt = s / C::PIECES, sg = s - tt * C::PIECES;
+      const int e = 4 * c + (tt >> 3), ti = tt & 7;
+      const int64_t tok = ti < (int)ent_n[e] ? 8 * (int64_t)ent_j[e] + ti : pc;
+      const uint16_t* krow = kb + tok * kv_st;
+      const uint16_t* vrow = vb + tok * kv_st;
+      // slot sg holds piece mh_kslot(tt, sg) (an involution)
+      mh_load_lds16(krow + 8 * mh_kslot(tt, sg), &kv_lds[bf][0][r * 256 + wave * 64]);
+      mh_load_lds16(vrow + 8 * mh_vslot(tt, sg), &kv_lds[bf][1][r * 256 + wave * 64]);
+    }
   };
-  load_table(0);
 
   // A operand of S: head n of the unit (zero past QPK), dims qd*D/4 ...
   uint4 qa[C::KS];
@@ -150,69 +183,42 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
 #pragma unroll
     for (int u = 0; u < C::KS; ++u) qa[u] = ldg16(qp + 8 * u);
   }
-  const int64_t sb = valid ? (int64_t)seq * kv_sb : 0;
-  const uint16_t* kb = kc + sb + (int64_t)g * D;
-  const uint16_t* vb = vc + sb + (int64_t)g * D;
-  const int64_t pc = valid ? p : 0;  // a token that is always in range
 
   float m[4], l[4];
-  f32x4 o[C::NT];
+  f32x4 o[C::TPW];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     m[r] = -INFINITY;
     l[r] = 0.f;
   }
 #pragma unroll
-  for (int c = 0; c < C::NT; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  uint16_t* vw = v_lds[wave];
+  for (int c = 0; c < C::TPW; ++c) o[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
   uint16_t* pw_hi = p_lds[wave][0];
   uint16_t* pw_lo = p_lds[wave][1];
 
+  if (nch > 0) stage(0, 0);
 #pragma unroll 1
-  for (int i = 0; i < niter; ++i) {
-    if (i > 0 && (i & 15) == 0) load_table(i);
-    const int src0 = 4 * (i & 15);
-    int64_t jr[4];
-    int cnt[4];
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)lj, src0 + e4);
-      const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(lj >> 32), src0 + e4);
-      jr[e4] = (int64_t)(((uint64_t)hi << 32) | lo);
-      cnt[e4] = __builtin_amdgcn_readlane(lcnt, src0 + e4);
-    }
-    // K: lane (n, qd) of tile st holds token 16 st + n, dims qd*D/4 ...
-    uint4 kr[2][C::KS];
+  for (int c = 0; c < nch; ++c) {
+    const int bf = c & 1;
+    // this thread's loads of chunk c are done; after the barrier every
+    // thread's are, and every wave has finished chunk c - 1 (whose buffer
+    // chunk c + 1 reuses)
+    mh_wait_loads();
+    __syncthreads();
+    if (c + 1 < nch) stage(c + 1, bf ^ 1);
+    const uint4* kl = kv_lds[bf][0];
+    const uint16_t* vl = reinterpret_cast<const uint16_t*>(kv_lds[bf][1]);
+    // S for tokens 16 st + n of the chunk
+    f32x4 acc[2];
     bool kok[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int e4 = 2 * st + (n >> 3), ti = n & 7;
-      kok[st] = ti < mh_pick4(e4, cnt[0], cnt[1], cnt[2], cnt[3]);
-      const int64_t tok = kok[st] ? 8 * mh_pick4(e4, jr[0], jr[1], jr[2], jr[3]) + ti : pc;
-      const uint16_t* kp = kb + tok * kv_st + qd * (D / 4);
-#pragma unroll
-      for (int u = 0; u < C::KS; ++u) kr[st][u] = ldg16(kp + 8 * u);
-    }
-    // V: piece x = lane + 64 v of the chunk's 32 x D/8 pieces (absent tokens
-    // load the own token; their probability is 0)
-    uint4 vr[C::VPL];
-#pragma unroll
-    for (int v = 0; v < C::VPL; ++v) {
-      const int x = lane + 64 * v;
-      const int tt = x / C::PIECES, dp = x - tt * C::PIECES;
-      const int e4 = tt >> 3, ti = tt & 7;
-      const int64_t tok = ti < mh_pick4(e4, cnt[0], cnt[1], cnt[2], cnt[3])
-                              ? 8 * mh_pick4(e4, jr[0], jr[1], jr[2], jr[3]) + ti
-                              : pc;
-      vr[v] = ldg16(vb + tok * kv_st + 8 * dp);
-    }
-    // S, then the online softmax per head (lane row qd holds heads 4qd..4qd+3)
-    f32x4 acc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
+      const int tt = 16 * st + n;
+      kok[st] = (tt & 7) < (int)ent_n[4 * c + (tt >> 3)];
       acc[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < C::KS; ++u) acc[st] = mh_mfma(qa[u], kr[st][u], acc[st]);
+      for (int u = 0; u < C::KS; ++u)
+        acc[st] = mh_mfma(qa[u], kl[tt * C::PIECES + mh_kslot(tt, qd * C::KS + u)], acc[st]);
     }
     float alpha[4];
 #pragma unroll
@@ -235,116 +241,122 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
       pw_lo[h * 32 + n] = (uint16_t)bf16_bits(p0 - __builtin_bit_cast(float, h0 << 16));
       pw_lo[h * 32 + 16 + n] = (uint16_t)bf16_bits(p1 - __builtin_bit_cast(float, h1 << 16));
     }
-    // V rows into LDS (4-byte stores: the padded rows are 4-byte aligned)
-#pragma unroll
-    for (int v = 0; v < C::VPL; ++v) {
-      const int x = lane + 64 * v;
-      const int tt = x / C::PIECES, dp = x - tt * C::PIECES;
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vw + tt * C::VROW + 8 * dp);
-      dst[0] = vr[v].x;
-      dst[1] = vr[v].y;
-      dst[2] = vr[v].z;
-      dst[3] = vr[v].w;
-    }
     mh_wave_sync();
     const uint4 pa_hi = *reinterpret_cast<const uint4*>(pw_hi + n * 32 + 8 * qd);
     const uint4 pa_lo = *reinterpret_cast<const uint4*>(pw_lo + n * 32 + 8 * qd);
 #pragma unroll
-    for (int c = 0; c < C::NT; ++c) {
+    for (int ct = 0; ct < C::TPW; ++ct) {
+      const int tile = wave * C::TPW + ct;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[c][r] *= alpha[r];
-      // B: V[tokens 8qd .. 8qd+7][dim 16c + n]
-      const uint16_t* vp = vw + (8 * qd) * C::VROW + 16 * c + n;
+      for (int r = 0; r < 4; ++r) o[ct][r] *= alpha[r];
+      // B: V[tokens 8qd .. 8qd+7][dim 16 tile + n]
+      const int P = 2 * tile + (n >> 3), e8 = n & 7;
       uint32_t bw[4];
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2)
-        bw[t2] = (uint32_t)vp[(2 * t2) * C::VROW] | ((uint32_t)vp[(2 * t2 + 1) * C::VROW] << 16);
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const int t0 = 8 * qd + 2 * t2, t1 = t0 + 1;
+        const uint32_t v0 = vl[(t0 * C::PIECES + mh_vslot(t0, P)) * 8 + e8];
+        const uint32_t v1 = vl[(t1 * C::PIECES + mh_vslot(t1, P)) * 8 + e8];
+        bw[t2] = v0 | (v1 << 16);
+      }
       const uint4 bv = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-      o[c] = mh_mfma(pa_hi, bv, o[c]);
-      o[c] = mh_mfma(pa_lo, bv, o[c]);
+      o[ct] = mh_mfma(pa_hi, bv, o[ct]);
+      o[ct] = mh_mfma(pa_lo, bv, o[ct]);
     }
     mh_wave_sync();
   }
 
-  // ---- merge the four waves (fixed order), through the V staging area
-  __syncthreads();
-  float* mo = reinterpret_cast<float*>(&v_lds[0][0]);          // [wave][16 heads][D]
-  float* ml = mo + 4 * 16 * D;                                  // [wave][m | l][16 heads]
+  // ---- the wave's dims of every head: split state or final output
 #pragma unroll
-  for (int c = 0; c < C::NT; ++c)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mo[(wave * 16 + 4 * qd + r) * D + 16 * c + n] = o[c][r];
-  if (n == 0) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ml[(wave * 2 + 0) * 16 + 4 * qd + r] = m[r];
-      ml[(wave * 2 + 1) * 16 + 4 * qd + r] = l[r];
-    }
-  }
-  __syncthreads();
-  for (int x = threadIdx.x; x < QPK * D; x += 256) {
-    const int h = x / D, d = x - h * D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * 2) * 16 + h]);
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float f = __builtin_amdgcn_exp2f(ml[(w * 2) * 16 + h] - Mu);
-      L = L + f * ml[(w * 2 + 1) * 16 + h];
-      O = O + f * mo[(w * 16 + h) * D + d];
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int h = 4 * qd + r;
+    if (h >= QPK) continue;
+    const float L = l[r], M = m[r];
     if (nsplit > 1) {
       float* dst = partial + ((unit * nsplit + split) * QPK + h) * C::PART;
-      if (d == 0) {
+      if (wave == 0 && n == 0) {
         dst[0] = M;
         dst[1] = L;
       }
-      dst[2 + d] = O;
+#pragma unroll
+      for (int ct = 0; ct < C::TPW; ++ct) dst[2 + 16 * (wave * C::TPW + ct) + n] = o[ct][r];
     } else {
       const float inv = L > 0.f ? 1.0f / L : 0.f;
-      out[(row * 4 * QPK + QPK * g + h) * D + d] = (uint16_t)bf16_bits(O * inv);
-      if (lse && d == 0)
-        lse[row * 4 * QPK + QPK * g + h] =
-            L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+      uint16_t* dst = out + (row * 4 * QPK + QPK * g + h) * D;
+#pragma unroll
+      for (int ct = 0; ct < C::TPW; ++ct)
+        dst[16 * (wave * C::TPW + ct) + n] = (uint16_t)bf16_bits(o[ct][r] * inv);
+      if (lse && wave == 0 && n == 0)
+        lse[row * 4 * QPK + QPK * g + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
     }
   }
 }
 
-// Merge of a unit's split states in split order: thread x takes output
-// (head, dim) pairs; every split's m and l are read by all threads of a head.
+// Merge of a unit's split states: one workgroup per (unit, head). Wave 0
+// takes the splits' m and l (at most 64 splits), forms each split's weight
+// f_s = 2^(m_s - M) and L = sum_s f_s l_s (a fixed-order shuffle tree), and
+// thread d then sums f_s o_s[d] over the splits in split order.
 template <int QPK, int D>
 __global__ __launch_bounds__(256) void attn_mh_merge_kernel(const float* __restrict__ partial,
                                                             int nsplit,
                                                             uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
   using C = MhCfg<QPK, D>;
+  __shared__ float f_lds[64];
+  __shared__ float ml_lds[2];
   const int64_t unit = blockIdx.x;
+  const int h = blockIdx.y;
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
-  const float* st = partial + unit * (int64_t)nsplit * QPK * C::PART;
-  for (int x = threadIdx.x; x < QPK * D; x += 256) {
-    const int h = x / D, d = x - h * D;
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, st[(s * QPK + h) * C::PART]);
+  const int t = threadIdx.x;
+  const int64_t sstride = (int64_t)QPK * C::PART;  // between a head's states of consecutive splits
+  const float* st = partial + (unit * nsplit * QPK + h) * C::PART;
+  if (t < 64) {
+    const float ms = t < nsplit ? st[t * sstride] : -INFINITY;
+    float M = ms;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
     const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float* sp = st + (s * QPK + h) * C::PART;
-      const float f = __builtin_amdgcn_exp2f(sp[0] - Mu);
-      L = L + f * sp[1];
-      O = O + f * sp[2 + d];
+    const float f = t < nsplit ? __builtin_amdgcn_exp2f(ms - Mu) : 0.f;
+    float L = t < nsplit ? f * st[t * sstride + 1] : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L = L + __shfl_xor(L, o, 64);
+    f_lds[t] = f;
+    if (t == 0) {
+      ml_lds[0] = M;
+      ml_lds[1] = L;
     }
-    const float inv = L > 0.f ? 1.0f / L : 0.f;
-    out[(row * 4 * QPK + QPK * g + h) * D + d] = (uint16_t)bf16_bits(O * inv);
-    if (lse && d == 0)
-      lse[row * 4 * QPK + QPK * g + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
   }
+  __syncthreads();
+  if (t >= D) return;
+  float O = 0.f;
+  for (int s = 0; s < nsplit; ++s) O = O + f_lds[s] * st[s * sstride + 2 + t];
+  const float M = ml_lds[0], L = ml_lds[1];
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  out[(row * 4 * QPK + QPK * g + h) * D + t] = (uint16_t)bf16_bits(O * inv);
+  if (lse && t == 0)
+    lse[row * 4 * QPK + QPK * g + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
+}
+
+// Splits: a multiple of 4 entries (one chunk) each, about S5_ATTN_MH_BLOCKS
+// workgroups in all for decode; many rows run unsplit.
+#ifndef S5_ATTN_MH_BLOCKS
+#define S5_ATTN_MH_BLOCKS 512
+#endif
+static AttnPlan attn_mh_plan(int32_t rows) {
+  const int64_t units = (int64_t)rows * 4;
+  int64_t ns = units > 0 ? (S5_ATTN_MH_BLOCKS + units - 1) / units : 1;
+  int64_t per = (MH_ENTRIES + ns - 1) / ns;
+  per = (per + 3) / 4 * 4;
+  if (per < 16) per = 16;
+  AttnPlan a;
+  a.per_split = (int32_t)per;
+  a.nsplit = (int32_t)((MH_ENTRIES + per - 1) / per);
+  return a;
 }
 
 size_t attn_mh_workspace_bytes(int32_t rows, int32_t qpk, int32_t head_dim) {
-  const AttnPlan a = attn_plan(rows);
+  const AttnPlan a = attn_mh_plan(rows);
   if (a.nsplit <= 1) return 0;
   return (size_t)rows * 4 * a.nsplit * qpk * (2 + head_dim) * sizeof(float);
 }
@@ -360,14 +372,14 @@ static hipError_t launch_mh(const AttnArgs& a, const AttnPlan& pl, hipStream_t s
                      a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_mh_merge_kernel<QPK, D>), dim3(units), dim3(256), 0, stream,
+  hipLaunchKernelGGL((attn_mh_merge_kernel<QPK, D>), dim3(units, QPK), dim3(256), 0, stream,
                      (const float*)a.partial, pl.nsplit, (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_mh(const AttnArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
-  const AttnPlan pl = attn_plan(a.rows);
+  const AttnPlan pl = attn_mh_plan(a.rows);
   if (a.head_dim == 128) {
     if (a.qpk == 4) return launch_mh<4, 128>(a, pl, stream);
     if (a.qpk == 8) return launch_mh<8, 128>(a, pl, stream);

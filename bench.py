@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0
 # profiles/sparse_attn_hbm_counters_decode16_ctx128k.md), each scaled by what
 # the counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # Valid only for the attention source the counters were taken on.
-ATTN_TRAFFIC = {"source_sha256": "160b71d393dd71878dbc5bc92ed749fcb153b5e43c947792eaa7f14608696b71",
-                "bytes_per_launch": 136092877}
+ATTN_TRAFFIC = {"source_sha256": "bd90a360a58583735ccb9c405268fce6b6525376b0287cdfdb0dd65c20003d97",
+                "bytes_per_launch": 136093559}
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"

@@ -8,8 +8,9 @@
 // region first, then the 512 selected regions) is cut into splits of
 // `per_split` entries, one 256-thread workgroup each; inside a workgroup the
 // four waves take 4-entry chunks (32 tokens) in turn; wave states merge in
-// wave order, split states merge in split order. Results are therefore
-// independent of scheduling.
+// wave order, split states merge in split order (attn_mh_merge_kernel, one
+// workgroup per (unit, head)). Results are therefore independent of
+// scheduling.
 //
 // Per 32-token chunk, per wave:
 //  - QK^T with the 16x16x32 bf16 MFMA: A = the unit's 4 query heads (MFMA
@@ -316,45 +317,6 @@ __global__ __launch_bounds__(256) void attn_kernel(
   if (lse && d0 == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
 }
 
-// Merge of a unit's split states, in split order. The block first copies the
-// unit's states into LDS with all loads in flight at once (splits hold at
-// least 16 entries, so there are at most ceil(513 / 16) = 33 of them), then wave r merges head r: the max of the splits' m, and
-// lane d accumulates dims 2d, 2d+1 and the weighted l over the splits in order.
-constexpr int AT_MERGE_MAX = (AT_ENTRIES + 15) / 16;
-__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ partial,
-                                                         int nsplit, uint16_t* __restrict__ out,
-                                                         float* __restrict__ lse) {
-  __shared__ float4 st_lds[AT_MERGE_MAX * 4 * AT_PART / 4];
-  const int64_t unit = blockIdx.x;
-  const int64_t row = unit >> 2;
-  const int g = (int)(unit & 3);
-  const int r = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int d0 = 2 * lane;
-  const int n4 = nsplit * AT_PART;  // float4s of the unit's states (4 heads x 130 floats each)
-  const float4* src = reinterpret_cast<const float4*>(partial + unit * nsplit * 4 * AT_PART);
-  for (int i = threadIdx.x; i < n4; i += 256) st_lds[i] = src[i];
-  __syncthreads();
-  const float* st = reinterpret_cast<const float*>(st_lds) + r * AT_PART;  // split s at + s*4*AT_PART
-  float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmaxf(M, st[s * 4 * AT_PART]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f, O0 = 0.f, O1 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* sp = st + s * 4 * AT_PART;
-    const float f = __builtin_amdgcn_exp2f(sp[0] - Mu);
-    const float2 v = *reinterpret_cast<const float2*>(sp + 2 + d0);
-    L = L + f * sp[1];
-    O0 = O0 + f * v.x;
-    O1 = O1 + f * v.y;
-  }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const uint32_t packed = bf16_bits(O0 * inv) | (bf16_bits(O1 * inv) << 16);
-  *reinterpret_cast<uint32_t*>(out + (row * 16 + 4 * g + r) * 128 + d0) = packed;
-  if (lse && lane == 0) lse[row * 16 + 4 * g + r] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -INFINITY;
-}
-
 // Decode units are few (rows x 4): each gets enough splits for about
 // S5_ATTN_BLOCKS workgroups in all, each split a multiple of 16 entries (four
 // per wave per chunk); prefill units are many and run unsplit.
@@ -392,9 +354,8 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
                      a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(units), dim3(256), 0, stream,
-                     (const float*)a.partial, pl.nsplit, (uint16_t*)a.out, a.lse);
-  return hipGetLastError();
+  // the split states are laid out as attn_mh.hip's, 4 heads x 128 dims
+  return launch_attn_merge(a.partial, pl.nsplit, a.rows, 4, 128, a.out, a.lse, stream);
 }
 
 }  // namespace s5

@@ -372,9 +372,27 @@ static hipError_t launch_mh(const AttnArgs& a, const AttnPlan& pl, hipStream_t s
                      a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
-  hipLaunchKernelGGL((attn_mh_merge_kernel<QPK, D>), dim3(units, QPK), dim3(256), 0, stream,
-                     (const float*)a.partial, pl.nsplit, (uint16_t*)a.out, a.lse);
-  return hipGetLastError();
+  return launch_attn_merge(a.partial, pl.nsplit, a.rows, QPK, D, a.out, a.lse, stream);
+}
+
+hipError_t launch_attn_merge(const float* partial, int32_t nsplit, int32_t rows, int32_t qpk,
+                             int32_t head_dim, void* out, float* lse, hipStream_t stream) {
+  const dim3 grid((unsigned)rows * 4u, (unsigned)qpk);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, partial, (int)nsplit, (uint16_t*)out,
+                       lse);
+    return hipGetLastError();
+  };
+  if (head_dim == 128) {
+    if (qpk == 4) return go(attn_mh_merge_kernel<4, 128>);
+    if (qpk == 8) return go(attn_mh_merge_kernel<8, 128>);
+    if (qpk == 16) return go(attn_mh_merge_kernel<16, 128>);
+  } else if (head_dim == 192) {
+    if (qpk == 4) return go(attn_mh_merge_kernel<4, 192>);
+    if (qpk == 8) return go(attn_mh_merge_kernel<8, 192>);
+    if (qpk == 16) return go(attn_mh_merge_kernel<16, 192>);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_mh(const AttnArgs& a, hipStream_t stream) {

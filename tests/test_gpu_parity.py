@@ -138,6 +138,34 @@ def test_select_tie_heavy_72_rows_matrix_core_path():
     assert ex == 0
 
 
+@pytest.mark.parametrize("codes", ["random", "tie_heavy"])
+def test_select_stored_intervals_72_rows_5000_regions(codes):
+    """More than 64 rows over more than 4,096 regions: the interval scorer
+    stores its intervals and a separate selection pass rescores and selects
+    (smaller summaries fuse the two). 72 decode rows of 72 sequences at
+    position 39,999 (4,999 candidates), e4m3 query and summaries drawn
+    directly: every finite code at random, or the tie-heavy {+-1/4 .. +-2}."""
+    rows, R = 72, 5000
+    g = torch.Generator().manual_seed(31)
+    if codes == "random":
+        def draw(shape):
+            c = torch.randint(0, 0x7F, shape, generator=g, dtype=torch.int32)   # 0x7F is NaN
+            return (c | (torch.randint(0, 2, shape, generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
+        w = torch.rand(16, generator=g)
+    else:
+        tie = torch.tensor(W.TIE_CODES, dtype=torch.uint8)
+        draw = lambda shape: tie[torch.randint(0, 8, shape, generator=g)]
+        w = torch.arange(1, 17, dtype=torch.float32) / 16
+    d = {"rows": rows, "q8": draw((rows, 16, 64)).to(DEV), "w_head": w.to(DEV),
+         "row_seq": torch.arange(rows, dtype=torch.int32, device=DEV),
+         "row_pos": torch.full((rows,), 8 * R - 1, dtype=torch.int64, device=DEV)}
+    S = draw((rows, R, 4, 64)).to(DEV)
+    P.say(f"[case] stored intervals {codes}: {rows} rows x {R} regions")
+    sample = [0, 1, 40, 71]
+    _, ex = _select_check(d, S, P.host8(S), sample, exact=True)
+    assert ex == 0
+
+
 def test_select_prefill2048_ctx32k_sampled():
     d = _case("prefill2048_ctx32k", 17, DEV, with_kv=False)
     S = P.gpu_summary(d)

@@ -292,46 +292,37 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
   }
 }
 
-// Merge of a unit's split states: one workgroup per (unit, head). Wave 0
-// takes the splits' m and l (at most 64 splits), forms each split's weight
-// f_s = 2^(m_s - M) and L = sum_s f_s l_s (a fixed-order shuffle tree), and
-// thread d then sums f_s o_s[d] over the splits in split order.
+// Merge of a unit's split states: one workgroup per (unit, head), thread d
+// for dim d. Every thread reads the splits' m and l itself (the same address
+// across a wave: one load each) besides its o values, all in flight at once,
+// and forms M = max m_s, the weights 2^(m_s - M), L and its dim in split
+// order: one memory round trip, the same result in every thread.
 template <int QPK, int D>
 __global__ __launch_bounds__(256) void attn_mh_merge_kernel(const float* __restrict__ partial,
                                                             int nsplit,
                                                             uint16_t* __restrict__ out,
                                                             float* __restrict__ lse) {
   using C = MhCfg<QPK, D>;
-  __shared__ float f_lds[64];
-  __shared__ float ml_lds[2];
   const int64_t unit = blockIdx.x;
   const int h = blockIdx.y;
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
   const int t = threadIdx.x;
+  if (t >= D) return;
   const int64_t sstride = (int64_t)QPK * C::PART;  // between a head's states of consecutive splits
   const float* st = partial + (unit * nsplit * QPK + h) * C::PART;
-  if (t < 64) {
-    const float ms = t < nsplit ? st[t * sstride] : -INFINITY;
-    float M = ms;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    const float f = t < nsplit ? __builtin_amdgcn_exp2f(ms - Mu) : 0.f;
-    float L = t < nsplit ? f * st[t * sstride + 1] : 0.f;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) L = L + __shfl_xor(L, o, 64);
-    f_lds[t] = f;
-    if (t == 0) {
-      ml_lds[0] = M;
-      ml_lds[1] = L;
-    }
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, st[s * sstride]);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f, O = 0.f;
+#pragma unroll 8
+  for (int s = 0; s < nsplit; ++s) {
+    const float* sp = st + s * sstride;
+    const float f = __builtin_amdgcn_exp2f(sp[0] - Mu);
+    L = L + f * sp[1];
+    O = O + f * sp[2 + t];
   }
-  __syncthreads();
-  if (t >= D) return;
-  float O = 0.f;
-  for (int s = 0; s < nsplit; ++s) O = O + f_lds[s] * st[s * sstride + 2 + t];
-  const float M = ml_lds[0], L = ml_lds[1];
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   out[(row * 4 * QPK + QPK * g + h) * D + t] = (uint16_t)bf16_bits(O * inv);
   if (lse && t == 0)

@@ -24,6 +24,7 @@
 //    loads (16 lanes cover a 256-byte row) and P from LDS.
 // Decode units are few (rows x 4), so they get many splits to spread the
 // gather over the GPU; prefill units are many and run unsplit.
+#include "attn_tile.hpp"
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -154,8 +155,9 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const uint16_t* __restrict__ q, int64_t qs, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, int64_t B, int64_t kv_sb, int64_t kv_st, int64_t T_cap,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ row_seq,
-    const int64_t* __restrict__ row_pos, float scale_log2, int per_split, int nsplit,
-    float* __restrict__ partial, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const int64_t* __restrict__ row_pos, int32_t rows, int32_t sweep_maxr, float scale_log2,
+    int per_split, int nsplit, float* __restrict__ partial, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
   __shared__ float4 p_lds[4][32];            // per wave: P of 32 tokens, 4 heads each
   __shared__ float o_lds[4][4][4][128];      // [wave][token slot][head][dim]
   __shared__ float ml_lds[4][2][4];          // [wave][m | l][head]
@@ -164,6 +166,12 @@ __global__ __launch_bounds__(256) void attn_kernel(
   const int split = blockIdx.y;
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
+  if (sweep_maxr > 0) {
+    // rows of a tile the context sweep (attn_tile_kernel) takes are its work
+    int32_t sq;
+    if (tl_tile_taken(row / TL_ROWS * TL_ROWS, rows, row_seq, row_pos, B, T_cap, sweep_maxr, &sq))
+      return;
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
 
@@ -341,17 +349,34 @@ size_t attn_workspace_bytes(int32_t rows) {
   return (size_t)rows * 4 * a.nsplit * 4 * AT_PART * sizeof(float);
 }
 
+// Many rows (a prompt chunk) go to the context sweep, tile by tile, when the
+// contexts are at most S5_ATTN_TILE_MAX_REGIONS regions long; attn_kernel
+// takes the rest.
+#ifndef S5_ATTN_TILE_MIN_ROWS
+#define S5_ATTN_TILE_MIN_ROWS 1024
+#endif
+#ifndef S5_ATTN_TILE_MAX_REGIONS
+#define S5_ATTN_TILE_MAX_REGIONS 8192
+#endif
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   if (a.qpk != 4 || a.head_dim != 128) return launch_attn_mh(a, stream);
   const AttnPlan pl = attn_plan(a.rows);
+  int32_t maxr = 0;
+  if (pl.nsplit == 1 && a.rows >= S5_ATTN_TILE_MIN_ROWS && a.T_cap > 0) {
+    const int64_t nr = (a.T_cap + 7) / 8;
+    maxr = (int32_t)(nr < S5_ATTN_TILE_MAX_REGIONS ? nr : S5_ATTN_TILE_MAX_REGIONS);
+    const hipError_t e = launch_attn_tile(a, maxr, stream);
+    if (e != hipSuccess) return e;
+  }
   const unsigned units = (unsigned)a.rows * 4u;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
   hipLaunchKernelGGL(attn_kernel, dim3(units, (unsigned)pl.nsplit), dim3(256), 0, stream,
                      (const uint16_t*)a.q, a.q_stride_row, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.B, a.kv_sb, a.kv_st, a.T_cap, a.sel, a.row_seq,
-                     a.row_pos, scale_log2, pl.per_split, pl.nsplit, a.partial, (uint16_t*)a.out,
-                     a.lse);
+                     a.row_pos, a.rows, maxr, scale_log2, pl.per_split, pl.nsplit, a.partial,
+                     (uint16_t*)a.out, a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.nsplit == 1) return e;
   // the split states are laid out as attn_mh.hip's, 4 heads x 128 dims

@@ -162,6 +162,9 @@ struct AttnArgs {
 // qpk 4, head dim 128: attn_kernel (attn.hip); the rest: attn_mh_kernel (attn_mh.hip)
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_mh(const AttnArgs& a, hipStream_t stream);
+// the context sweep over tiles of 32 rows for contexts below maxr regions
+// (attn_tile.hip); tiles it does not take are left to attn_kernel
+hipError_t launch_attn_tile(const AttnArgs& a, int32_t maxr, hipStream_t stream);
 // merge of split states [rows*4 units][nsplit][qpk heads][m, l, o[head_dim]]
 // into out and lse, in split order (attn_mh.hip)
 hipError_t launch_attn_merge(const float* partial, int32_t nsplit, int32_t rows, int32_t qpk,

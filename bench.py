@@ -34,13 +34,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per step5_sparse_attn call (attn_kernel + attn_merge_kernel) on
+# HBM bytes per step5_sparse_attn call (attn_kernel + attn_mh_merge_kernel) on
 # decode16_ctx128k, from two rocprofv3 --pmc passes (FETCH_SIZE, WRITE_SIZE;
 # profiles/sparse_attn_hbm_counters_decode16_ctx128k.md), each scaled by what
 # the counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # Valid only for the attention source the counters were taken on.
-ATTN_TRAFFIC = {"source_sha256": "bd90a360a58583735ccb9c405268fce6b6525376b0287cdfdb0dd65c20003d97",
-                "bytes_per_launch": 136093559}
+ATTN_TRAFFIC = {"source_sha256": "a3881f86e50b8fcfccc6a49a2142210c953fdf52abbe6b34ebcebb5c76ecf5e1",
+                "bytes_per_launch": 136237670}
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"
@@ -308,10 +308,19 @@ def attn_traffic(workload):
     import hashlib
     if workload != HEADLINE:
         return None
-    path = os.path.join(ROOT, "long_context_sparse_indexer_amd", "csrc", "attn.hip")
-    with open(path, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    return ATTN_TRAFFIC["bytes_per_launch"] if digest == ATTN_TRAFFIC["source_sha256"] else None
+    return ATTN_TRAFFIC["bytes_per_launch"] if attn_source_sha() == ATTN_TRAFFIC["source_sha256"] else None
+
+
+def attn_source_sha():
+    """sha256 over the sources of the decode attention call: attn_kernel and
+    the tile predicate it evaluates (attn.hip, attn_tile.hpp) and the split
+    merge (attn_mh.hip)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in ("attn.hip", "attn_tile.hpp", "attn_mh.hip"):
+        with open(os.path.join(ROOT, "long_context_sparse_indexer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def attn_geometry(torch, s5):
@@ -416,7 +425,7 @@ def main():
                    "sequences": head["sequences"], "topk": 512, "region": 8, "idx_heads": 16,
                    "kv_groups": 4, "q_heads": 16, "head_dim": 128, "inputs": wl.dist},
         "roofline": {"bound": "hbm",
-                     "kernel": "step5_sparse_attn (attn_kernel + attn_merge_kernel)",
+                     "kernel": "step5_sparse_attn (attn_kernel + attn_mh_merge_kernel)",
                      "achieved": sa["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": sa["frac_hbm"], "traffic": attn_traffic(args.workload),
                      "algorithmic_bytes_per_launch": sa["algorithmic_bytes"]},

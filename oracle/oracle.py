@@ -54,6 +54,8 @@ def lib():
         L.o_score.argtypes = [P, I32, I32, P, I64, P, P, I64, P, I64, I64, I64, P, C.c_int]
         L.o_select.restype = C.c_int
         L.o_select.argtypes = [P, P, I64, I32, I64, I32, P, P, C.c_int]
+        L.o_project.restype = C.c_int
+        L.o_project.argtypes = [P, I64, I64, P, I64, P, C.c_int]
         L.o_attend.restype = C.c_int
         L.o_attend.argtypes = [P, I64, I32, I32, I32, P, P, I64, I64, I64, P, I32, P, P, I64, D,
                                P, P, C.c_int]
@@ -259,3 +261,40 @@ def attend(q16, k16, v16, sel, row_seq, row_pos, scale, nthreads=None):
     if rc:
         raise ValueError("oracle attend rejected its arguments")
     return out, lse
+
+
+# ---- fused projection [VLLM-proj] ---------------------------------------------
+
+# Column blocks of the fused weight, in the order of its rows: the main
+# attention's q, k, v, then the indexer's q, k, z, then the gate.
+PROJ_PARTS = ("q", "k", "v", "index_q", "index_k", "index_z", "gate")
+
+
+def proj_sizes(q_heads=16, kv_heads=4, head_dim=128, idx_heads=16, groups=4, idx_dim=64,
+               gate=16):
+    """Columns of each part (PROJ_PARTS order). The gate is per query head:
+    one column per head by default."""
+    return (q_heads * head_dim, kv_heads * head_dim, kv_heads * head_dim, idx_heads * idx_dim,
+            groups * idx_dim, groups * idx_dim, gate)
+
+
+def project(hidden16, w16, sizes, nthreads=None):
+    """hidden16 bf16 [rows, H]; w16 bf16 [N, H] with N = sum(sizes).
+
+    Returns (out fp64 [rows, N], {part: fp64 [rows, size]}) where the parts
+    are consecutive column ranges of out in PROJ_PARTS order."""
+    hidden16 = _c(hidden16, np.uint16)
+    w16 = _c(w16, np.uint16)
+    rows, H = hidden16.shape
+    N, H2 = w16.shape
+    assert H2 == H and N == sum(sizes) and len(sizes) == len(PROJ_PARTS)
+    out = np.empty((rows, N), np.float64)
+    rc = lib().o_project(_p(hidden16), rows, H, _p(w16), N, _p(out),
+                         nthreads or default_threads())
+    if rc:
+        raise ValueError("oracle project rejected its arguments")
+    parts, c0 = {}, 0
+    for name, n in zip(PROJ_PARTS, sizes):
+        parts[name] = out[:, c0:c0 + n]
+        c0 += n
+    return out, parts

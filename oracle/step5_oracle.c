@@ -21,6 +21,12 @@
  *  [TF903-glue]  Same page, commit note on the native Step-5 family: the glue
  *                keeps StepFun's rounding points, among them zero-centred
  *                norms and the NEOX rotation read from bf16 cos/sin.
+ *  [VLLM-proj]   vLLM, "vllm.models.step5.nvidia.model", class
+ *                Step5FusedQKVIndexerLinear: the main attention's q, k, v and
+ *                the indexer's q, k, z and the gate come from one product
+ *                hidden @ W^T of the normed hidden state with one weight whose
+ *                rows are [q | k | v | index_q | index_k | index_z | gate],
+ *                split by column afterwards (split_indexer).
  *  [TF903-ref]   Same page, first commit note: the reference attends densely,
  *                which is exact while the indexer selects every region.
  *
@@ -469,6 +475,31 @@ int o_attend(const uint16_t* q, int64_t q_stride_row, int32_t q_heads, int32_t k
     free(lg);
   }
   return bad ? O_BAD : O_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fused projection [VLLM-proj]                                             */
+/* ------------------------------------------------------------------------ */
+/* out[r, n] = sum over k of hidden[r, k] * w[n, k], the bf16 inputs widened
+ * and the sum taken in fp64 in k order. hidden: bf16 [rows, hsize]
+ * (contiguous rows); w: bf16 [n_out, hsize] (the weight's rows are output
+ * columns); out: fp64 [rows, n_out]. The split into q, k, v and the indexer's
+ * q, k, z and gate is by column ranges (oracle.py, project). */
+int o_project(const uint16_t* hidden, int64_t rows, int64_t hsize, const uint16_t* w,
+              int64_t n_out, double* out, int nthreads) {
+  if (rows < 0 || hsize <= 0 || n_out <= 0) return O_BAD;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1)
+  for (int64_t r = 0; r < rows; ++r) {
+    const uint16_t* hr = hidden + r * hsize;
+    for (int64_t n = 0; n < n_out; ++n) {
+      const uint16_t* wn = w + n * hsize;
+      double acc = 0.0;
+      for (int64_t k = 0; k < hsize; ++k)
+        acc += (double)o_bf16_to_f32(hr[k]) * (double)o_bf16_to_f32(wn[k]);
+      out[r * n_out + n] = acc;
+    }
+  }
+  return O_OK;
 }
 
 /* ------------------------------------------------------------------------ */

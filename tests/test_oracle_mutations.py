@@ -74,6 +74,13 @@ MUTANTS = [
     ("attend_no_scale", "lg[i] = scale * dot;", "lg[i] = dot;"),
     ("attend_region_7_tokens", "for (int t = 0; t < REGION; ++t) toks[ntok++]",
      "for (int t = 0; t < REGION - 1; ++t) toks[ntok++]"),
+    # fused projection
+    ("project_drops_last_k", "for (int64_t k = 0; k < hsize; ++k)\n        acc +=",
+     "for (int64_t k = 0; k < hsize - 1; ++k)\n        acc +="),
+    ("project_weight_transposed", "(double)o_bf16_to_f32(wn[k]);", "(double)o_bf16_to_f32(w[k * n_out + n]);"),
+    ("project_first_row_only", "const uint16_t* hr = hidden + r * hsize;", "const uint16_t* hr = hidden;"),
+    ("project_hidden_column_off_by_one", "acc += (double)o_bf16_to_f32(hr[k])",
+     "acc += (double)o_bf16_to_f32(hr[k > 0 ? k - 1 : 0])"),
 ]
 
 CFLAGS = ["-O2", "-std=gnu11", "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",

@@ -499,3 +499,67 @@ def test_attend_rejects_noncausal_selection(orc):
     sel[0, 0, 0] = 5                              # region 5 is the row's own (p = 43)
     with pytest.raises(ValueError):
         orc.attend(q, k, v, sel, np.zeros(1, np.int32), np.array([43]), 0.1)
+
+
+# ---- fused projection [vLLM Step5FusedQKVIndexerLinear] -----------------------
+# One product hidden @ W^T with the weight's rows ordered [q | k | v |
+# index_q | index_k | index_z | gate], split by column ranges.
+
+
+def test_project_one_hot_weights_pick_hidden_columns(orc):
+    """W[n] one-hot at column perm[n]: out[r, n] is hidden[r, perm[n]]
+    exactly (catches a transposed operand or a wrong row or column)."""
+    rng = np.random.default_rng(3)
+    H, N = 96, 150
+    h = _bf(rng.standard_normal((5, H)))
+    perm = rng.integers(0, H, N)
+    perm[:3] = [0, H - 1, H // 2]
+    w = np.zeros((N, H), np.float32)
+    w[np.arange(N), perm] = 1.0
+    out, _ = orc.project(h, _bf(w), (N, 0, 0, 0, 0, 0, 0))
+    assert np.array_equal(out, _f(h).astype(np.float64)[:, perm])
+
+
+def test_project_rank_one_closed_form(orc):
+    """W = u v^T with small integers: out[r, n] = u[n] (hidden[r] . v),
+    exact in fp64 (every product and partial sum is a small integer)."""
+    rng = np.random.default_rng(5)
+    H, N = 200, 70
+    h = rng.integers(-8, 9, (4, H)).astype(np.float32)
+    u = rng.integers(-5, 6, N).astype(np.float32)
+    v = rng.integers(-5, 6, H).astype(np.float32)
+    out, _ = orc.project(_bf(h), _bf(np.outer(u, v)), (30, 10, 10, 10, 5, 4, 1))
+    assert np.array_equal(out, np.outer(h.astype(np.float64) @ v, u))
+
+
+def test_project_linear_in_hidden(orc):
+    rng = np.random.default_rng(7)
+    H, N = 64, 40
+    h1 = rng.integers(-16, 17, (3, H)).astype(np.float32)
+    h2 = rng.integers(-16, 17, (3, H)).astype(np.float32)
+    w = _bf(rng.integers(-4, 5, (N, H)).astype(np.float32))
+    sizes = (N, 0, 0, 0, 0, 0, 0)
+    a, _ = orc.project(_bf(h1), w, sizes)
+    b, _ = orc.project(_bf(h2), w, sizes)
+    c, _ = orc.project(_bf(h1 + h2), w, sizes)
+    assert np.array_equal(c, a + b)
+
+
+def test_project_split_follows_the_weight_row_order(orc):
+    """The layer's geometry (16 q heads x 128, 4 KV heads x 128, indexer
+    16 x 64 q and 4 x 64 k and z, a 16-column gate): weight row n holds the
+    binary digits of n, hidden the powers of two, so out[:, n] = n and each
+    part is its column range: q 0.., k 2048.., v 2560.., index_q 3072..,
+    index_k 4096.., index_z 4352.., gate 4608..4623."""
+    sizes = orc.proj_sizes()
+    assert sizes == (2048, 512, 512, 1024, 256, 256, 16)
+    N, H = sum(sizes), 16
+    n = np.arange(N)
+    w = ((n[:, None] >> np.arange(H)[None, :]) & 1).astype(np.float32)
+    h = np.tile((2.0 ** np.arange(H)).astype(np.float32), (2, 1))
+    out, parts = orc.project(_bf(h), _bf(w), sizes)
+    assert np.array_equal(out[0], n.astype(np.float64))
+    starts = dict(q=0, k=2048, v=2560, index_q=3072, index_k=4096, index_z=4352, gate=4608)
+    for name, size in zip(orc.PROJ_PARTS, sizes):
+        assert parts[name].shape == (2, size)
+        assert np.array_equal(parts[name][1], starts[name] + np.arange(size, dtype=np.float64))

@@ -253,6 +253,40 @@ int step5_sparse_attn(const step5_geom* geom, const void* q, int64_t q_stride_ro
  * needed or the geometry is not accepted). */
 size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows);
 
+/*
+ * The fused projection of a full-attention layer: one product of the normed
+ * hidden state with a weight whose rows are the attention's q, k, v and the
+ * indexer's q, k, z and gate rows, written straight into seven outputs.
+ * [vLLM, "vllm.models.step5.nvidia.model", Step5FusedQKVIndexerLinear:
+ * forward (one hidden @ W^T) and split_indexer]
+ *
+ * hidden      bf16 [rows, hidden_size], row stride hidden_stride_row
+ *             elements (a multiple of 8); 16-byte aligned.
+ * weight      bf16 [N, hidden_size], rows contiguous, 16-byte aligned;
+ *             N = q_heads*head_dim + 2*kv_heads*head_dim + idx_heads*idx_dim
+ *             + 2*groups*idx_dim + gate_size, its rows in the order of the
+ *             outputs below.
+ * gate_size   columns of the gate (0 or more, a multiple of 16; one per query
+ *             head for the Step-5 layer: 16).
+ * out         step5_proj_out[7], in the weight's row order: q [rows,
+ *             q_heads*head_dim], k and v [rows, kv_heads*head_dim], index_q
+ *             [rows, idx_heads*idx_dim], index_k and index_z [rows,
+ *             groups*idx_dim], gate [rows, gate_size]; each bf16, 16-byte
+ *             aligned, row stride stride_row elements (a multiple of 8, at
+ *             least the part's width); a part of width 0 is not touched.
+ * Each output element is the fp32 sum of the bf16 products over hidden_size,
+ * rounded once to bf16 (nearest even). hidden_size must be a multiple of 128
+ * (else STEP5_E_UNSUPPORTED). No workspace. rows == 0 is a successful no-op.
+ */
+typedef struct step5_proj_out {
+  void* ptr;
+  int64_t stride_row;
+} step5_proj_out;
+
+int step5_qkv_index_project(const step5_geom* geom, const void* hidden, int64_t hidden_stride_row,
+                            int32_t rows, int32_t hidden_size, const void* weight,
+                            int32_t gate_size, const step5_proj_out* out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

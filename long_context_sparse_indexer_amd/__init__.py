@@ -40,6 +40,14 @@ class Step5Geom(C.Structure):
 GEOM = Step5Geom(IDX_HEADS, GROUPS, IDX_DIM, ROPE_DIM, REGION, TOPK, Q_HEADS, KV_HEADS, HEAD_DIM)
 
 
+class Step5ProjOut(C.Structure):
+    _fields_ = [("ptr", C.c_void_p), ("stride_row", C.c_int64)]
+
+
+# outputs of the fused projection, in the order of the weight's rows
+PROJ_PARTS = ("q", "k", "v", "index_q", "index_k", "index_z", "gate")
+
+
 class Step5Error(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn}: status {status} ({step5_status_str(status)})")
@@ -77,6 +85,8 @@ def lib():
                                         P, P, SZ, P]
         L.step5_sparse_attn_workspace.restype = SZ
         L.step5_sparse_attn_workspace.argtypes = [G, I32]
+        L.step5_qkv_index_project.restype = C.c_int
+        L.step5_qkv_index_project.argtypes = [G, P, I64, I32, I32, P, I32, C.POINTER(Step5ProjOut), P]
         _lib = L
     return _lib
 
@@ -274,3 +284,34 @@ def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(row_pos), rows, float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         nbytes, _stream(stream))
     _check("step5_sparse_attn", st)
+
+
+def proj_widths(gate_size: int = Q_HEADS, q_heads: int = Q_HEADS, head_dim: int = HEAD_DIM):
+    """Columns of each output of the fused projection (PROJ_PARTS order)."""
+    return (q_heads * head_dim, KV_HEADS * head_dim, KV_HEADS * head_dim, IDX_HEADS * IDX_DIM,
+            GROUPS * IDX_DIM, GROUPS * IDX_DIM, gate_size)
+
+
+def step5_qkv_index_project(hidden: torch.Tensor, weight: torch.Tensor, outs, *,
+                            gate_size: int = Q_HEADS, q_heads: int = Q_HEADS,
+                            head_dim: int = HEAD_DIM, stream=None) -> None:
+    """outs[part] = the part's columns of hidden (bf16 [rows, H]) @ weight^T
+    (weight bf16 [N, H], rows in PROJ_PARTS order); outs: a sequence of 7
+    bf16 tensors [rows, width] (PROJ_PARTS order, rows of stride >= width)."""
+    _need(hidden.dtype == torch.bfloat16 and hidden.dim() == 2 and hidden.stride(1) == 1,
+          "hidden must be bf16 [rows, H] with contiguous rows")
+    rows, H = hidden.shape
+    widths = proj_widths(gate_size, q_heads, head_dim)
+    _need(weight.dtype == torch.bfloat16 and tuple(weight.shape) == (sum(widths), H) and
+          weight.is_contiguous(), f"weight must be contiguous bf16 [{sum(widths)}, {H}]")
+    _need(len(outs) == len(PROJ_PARTS), "outs must hold 7 tensors")
+    arr = (Step5ProjOut * len(PROJ_PARTS))()
+    for i, (t, wdt) in enumerate(zip(outs, widths)):
+        _need(t.dtype == torch.bfloat16 and t.dim() == 2 and tuple(t.shape) == (rows, wdt) and
+              t.stride(1) == 1, f"{PROJ_PARTS[i]} must be bf16 [{rows}, {wdt}] with contiguous rows")
+        arr[i].ptr = t.data_ptr() if wdt else None
+        arr[i].stride_row = t.stride(0) if rows > 1 else max(wdt, 8)
+    geom = attn_geom(q_heads, head_dim)
+    st = lib().step5_qkv_index_project(C.byref(geom), _ptr(hidden), hidden.stride(0) if rows > 1 else H,
+                                       rows, H, _ptr(weight), gate_size, arr, _stream(stream))
+    _check("step5_qkv_index_project", st)

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libstep5.so")
-SOURCES = ["summarize.hip", "score.hip", "topk.hip", "attn.hip", "attn_mh.hip", "attn_tile.hip", "step5.cpp"]
+SOURCES = ["summarize.hip", "score.hip", "topk.hip", "attn.hip", "attn_mh.hip", "attn_tile.hip", "proj.hip", "step5.cpp"]
 ARCH = "gfx950"
 
 

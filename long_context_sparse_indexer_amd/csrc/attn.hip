@@ -367,8 +367,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (pl.nsplit == 1 && a.rows >= S5_ATTN_TILE_MIN_ROWS && a.T_cap > 0) {
     const int64_t nr = (a.T_cap + 7) / 8;
     maxr = (int32_t)(nr < S5_ATTN_TILE_MAX_REGIONS ? nr : S5_ATTN_TILE_MAX_REGIONS);
-    const hipError_t e = launch_attn_tile(a, maxr, stream);
-    if (e != hipSuccess) return e;
+    // the sweep addresses a sequence's swept tokens with 32-bit byte offsets
+    if ((int64_t)maxr * 8 * a.kv_st * 2 + 4096 >= INT32_MAX) maxr = 0;
+    if (maxr > 0) {
+      const hipError_t e = launch_attn_tile(a, maxr, stream);
+      if (e != hipSuccess) return e;
+    }
   }
   const unsigned units = (unsigned)a.rows * 4u;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);

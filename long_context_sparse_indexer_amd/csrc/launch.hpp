@@ -170,4 +170,26 @@ hipError_t launch_attn_tile(const AttnArgs& a, int32_t maxr, hipStream_t stream)
 hipError_t launch_attn_merge(const float* partial, int32_t nsplit, int32_t rows, int32_t qpk,
                              int32_t head_dim, void* out, float* lse, hipStream_t stream);
 
+// Fused projection (proj.hip): hidden [rows, K] @ W[N, K]^T, the N output
+// columns split over PROJ_PARTS outputs (part p: columns start[p] ..
+// start[p+1]-1, every boundary a multiple of 16), bf16 with fp32 sums.
+constexpr int PROJ_PARTS = 7;
+struct ProjOuts {
+  uint16_t* ptr[PROJ_PARTS];
+  int64_t stride[PROJ_PARTS];  // elements between rows
+  int32_t start[PROJ_PARTS + 1];
+};
+struct ProjArgs {
+  const void* hidden;
+  int64_t hidden_stride;
+  int32_t rows;
+  int32_t K;  // a multiple of 128
+  const void* weight;  // bf16 [N, K], rows contiguous
+  ProjOuts outs;
+};
+#ifndef S5_PROJ_WIDE_MIN_ROWS
+#define S5_PROJ_WIDE_MIN_ROWS 256
+#endif
+hipError_t launch_proj(const ProjArgs& a, hipStream_t stream);
+
 }  // namespace s5

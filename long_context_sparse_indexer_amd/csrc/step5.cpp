@@ -345,3 +345,39 @@ STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_
   a.partial = static_cast<float*>(workspace);
   return from_hip(s5::launch_attn(a, stream));
 }
+
+STEP5_EXPORT int step5_qkv_index_project(const step5_geom* geom, const void* hidden,
+                                         int64_t hidden_stride_row, int32_t rows,
+                                         int32_t hidden_size, const void* weight, int32_t gate_size,
+                                         const step5_proj_out* out, hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
+  if (rows < 0 || hidden_size <= 0 || gate_size < 0) return STEP5_E_INVALID;
+  if (!hidden || !aligned(hidden, 16) || hidden_stride_row < hidden_size || (hidden_stride_row % 8))
+    return STEP5_E_INVALID;
+  if (!weight || !aligned(weight, 16) || !out) return STEP5_E_INVALID;
+  if ((hidden_size % 128) || (gate_size % 16) || rows > 65535 * 16) return STEP5_E_UNSUPPORTED;
+  const int64_t width[s5::PROJ_PARTS] = {
+      (int64_t)geom->q_heads * geom->head_dim, (int64_t)geom->kv_heads * geom->head_dim,
+      (int64_t)geom->kv_heads * geom->head_dim, (int64_t)geom->idx_heads * geom->idx_dim,
+      (int64_t)geom->groups * geom->idx_dim,    (int64_t)geom->groups * geom->idx_dim,
+      gate_size};
+  s5::ProjArgs a;
+  a.outs.start[0] = 0;
+  for (int p = 0; p < s5::PROJ_PARTS; ++p) {
+    const step5_proj_out& o = out[p];
+    if (width[p] > 0 && (!o.ptr || !aligned(o.ptr, 16) || o.stride_row < width[p] ||
+                         (o.stride_row % 8)))
+      return STEP5_E_INVALID;
+    a.outs.ptr[p] = static_cast<uint16_t*>(o.ptr);
+    a.outs.stride[p] = o.stride_row;
+    a.outs.start[p + 1] = a.outs.start[p] + (int32_t)width[p];
+  }
+  if (rows == 0) return STEP5_OK;
+  a.hidden = hidden;
+  a.hidden_stride = hidden_stride_row;
+  a.rows = rows;
+  a.K = hidden_size;
+  a.weight = weight;
+  return from_hip(s5::launch_proj(a, stream));
+}

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(s5):
     declared = set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(step5_\w+)\s*\(", text, re.M))
     assert {"step5_index_summarize", "step5_index_append", "step5_index_score_topk", "step5_sparse_attn",
             "step5_index_score_topk_workspace", "step5_sparse_attn_workspace",
-            "step5_status_str"} <= declared
+            "step5_qkv_index_project", "step5_status_str"} <= declared
     nm = subprocess.run(["nm", "-D", "--defined-only", s5.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
     exported = set(re.findall(r" T (step5_\w+)$", nm, re.M))
@@ -304,3 +304,56 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(m, "_lib", None)
     with pytest.raises(ImportError):
         m.lib()
+
+
+# ---- fused projection --------------------------------------------------------
+
+def _proj(s5, widths=(2048, 512, 512, 1024, 256, 256, 16), **over):
+    g = over.pop("g", geom(s5))
+    a = dict(h=A, hs=4096, rows=16, H=4096, w=A, gate=widths[6])
+    a.update(over)
+    outs = (s5.Step5ProjOut * 7)()
+    for i, wdt in enumerate(widths):
+        outs[i].ptr = over.get(f"out{i}", A)
+        outs[i].stride_row = over.get(f"stride{i}", wdt)
+    return s5.lib().step5_qkv_index_project(C.byref(g), a["h"], a["hs"], a["rows"], a["H"], a["w"],
+                                            a["gate"], outs, None)
+
+
+@pytest.mark.parametrize("over,code", [
+    ({"rows": 0}, OK),
+    ({"rows": -1}, E_INVALID),
+    ({"h": None}, E_INVALID),
+    ({"h": A + 8}, E_INVALID),
+    ({"hs": 4088}, E_INVALID),
+    ({"hs": 4100}, E_INVALID),
+    ({"w": None}, E_INVALID),
+    ({"w": A + 2}, E_INVALID),
+    ({"H": 0}, E_INVALID),
+    ({"H": 4032, "hs": 4096}, E_UNSUPPORTED),   # not a multiple of 128
+    ({"gate": -16}, E_INVALID),
+    ({"out0": None}, E_INVALID),
+    ({"out3": A + 4}, E_INVALID),
+    ({"stride1": 504}, E_INVALID),
+    ({"stride5": 260}, E_INVALID),
+    ({"g": None}, E_INVALID),
+])
+def test_project_rejections(s5, over, code):
+    if "g" in over and over["g"] is None:
+        outs = (s5.Step5ProjOut * 7)()
+        assert s5.lib().step5_qkv_index_project(None, A, 4096, 16, 4096, A, 16, outs, None) == code
+        return
+    assert _proj(s5, **over) == code
+
+
+def test_project_gate_and_geometry(s5):
+    """A gate of 24 columns is not a multiple of 16 (unsupported); a gate of
+    0 leaves the seventh output untouched (its pointer may be null); the
+    16-heads-per-KV-head x 192 geometry widens q, k and v."""
+    assert _proj(s5, widths=(2048, 512, 512, 1024, 256, 256, 24), rows=0) == E_UNSUPPORTED
+    assert _proj(s5, widths=(2048, 512, 512, 1024, 256, 256, 0), out6=None, rows=0) == OK
+    g = geom(s5, q_heads=64, head_dim=192)
+    assert _proj(s5, widths=(64 * 192, 768, 768, 1024, 256, 256, 64), g=g, rows=0) == OK
+    assert _proj(s5, widths=(64 * 192, 768, 768, 1024, 256, 256, 64), g=g, stride0=64 * 192 - 8,
+                 rows=0) == E_INVALID
+    assert _proj(s5, g=geom(s5, topk=256), rows=0) == E_UNSUPPORTED

@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0
 # profiles/sparse_attn_hbm_counters_decode16_ctx128k.md), each scaled by what
 # the counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # Valid only for the attention source the counters were taken on.
-ATTN_TRAFFIC = {"source_sha256": "a3881f86e50b8fcfccc6a49a2142210c953fdf52abbe6b34ebcebb5c76ecf5e1",
-                "bytes_per_launch": 136237670}
+ATTN_TRAFFIC = {"source_sha256": "2c10ec08ba759aaa21d605295ea46c3d477938d30d556da548256561f8c93a01",
+                "bytes_per_launch": 136237875}
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"
@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--cpu-rows", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle's sample until this much time has passed")
-    ap.add_argument("--extra", default="prefill2048_ctx32k,decode1_ctx1m,attn_geometry,hbm_copy",
+    ap.add_argument("--extra", default="prefill2048_ctx32k,decode1_ctx1m,attn_geometry,qkv_projection,hbm_copy",
                     help="comma-separated extra lines to measure after the headline "
                          "(workload names, attn_geometry and/or hbm_copy; 'none' for none)")
     ap.add_argument("--eager", action="store_true", help="launch the calls directly, no HIP graphs")
@@ -359,6 +359,35 @@ def attn_geometry(torch, s5):
     return res
 
 
+def qkv_projection(torch, s5):
+    """step5_qkv_index_project at the layer's shape (hidden 4,096; q 16 x 128,
+    k and v 4 x 128, indexer q 16 x 64, k and z 4 x 64, a 16-column gate:
+    4,624 columns) for the decode shape (16 rows) and a prompt chunk (2,048
+    rows), with synthetic bf16 weights. Algorithmic work: 2 x rows x 4,624 x
+    4,096 flop; bytes: the weight (37.9 MB) plus the hidden rows and outputs."""
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(91)
+    widths = s5.proj_widths()
+    N, H = sum(widths), 4096
+    w = (torch.randn((N, H), generator=g, device=dev) / 64).to(torch.bfloat16)
+    res = {"shape": f"hidden {H} -> {N} columns (q, k, v, index_q, index_k, index_z, gate)"}
+    for rows in (16, 2048):
+        h = torch.randn((rows, H), generator=g, device=dev).to(torch.bfloat16)
+        outs = [torch.empty((rows, wd), dtype=torch.bfloat16, device=dev) for wd in widths]
+        f = lambda: s5.step5_qkv_index_project(h, w, outs)
+        us = Timer(torch, [("proj", f)], 3, False).per_call()["proj"]
+        flop = 2.0 * rows * N * H
+        byts = N * H * 2 + rows * H * 2 + rows * N * 2
+        res[f"rows{rows}"] = {"us": round(us, 2), "TFLOPs": round(flop / us / 1e6, 1),
+                              "frac_bf16_mfma": round(flop / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+                              "GBs": round(byts / us / 1e3, 1),
+                              "frac_hbm": round(byts / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del h, outs
+    del w
+    return res
+
+
 def copy_ceiling(torch):
     """A plain device-to-device copy of 1 GiB: the HBM rate a streaming kernel
     reaches on this GPU (read + write bytes per second)."""
@@ -397,6 +426,10 @@ def main():
         if name == "hbm_copy":
             log("plain copy of 1 GiB")
             extra[name] = copy_ceiling(torch)
+        elif name == "qkv_projection":
+            log("fused qkv + indexer projection at the layer's shape")
+            extra[name] = qkv_projection(torch, s5)
+            torch.cuda.empty_cache()
         elif name == "attn_geometry":
             log("sparse attention of other query-head geometries at the 128K decode shape")
             extra[name] = attn_geometry(torch, s5)

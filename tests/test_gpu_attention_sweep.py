@@ -1,5 +1,5 @@
-"""GPU parity of the context sweep: many rows of one sequence (1,024 rows or
-more) are attended tile by tile, 32 rows sharing one pass over the context,
+"""GPU parity of the context sweep: many rows of one sequence (2,048 rows or
+more, contexts up to 5,120 regions) are attended tile by tile, 32 rows sharing one pass over the context,
 each row masked to its selected regions and its own region up to its
 position. Compared with the fp64 oracle (every output element within
 2e-3 + 1e-2 |ref|, the log-sum-exp within 2e-3) on sampled rows, and on every
@@ -113,8 +113,8 @@ def test_sweep_prefill_2048_rows_ragged_context():
 
 def test_sweep_peaked_scores():
     """Queries scaled by 12: the scores spread over about +-40 so the
-    running max moves often (the rescale path), 1,024 rows."""
-    T, rows = 4096, 1024
+    running max moves often (the rescale path), 2,048 rows."""
+    T, rows = 4096, 2048
     g, k, v = _kv(1, T, 8)
     q = (torch.randn(rows, 16, 128, generator=g) * 12).to(torch.bfloat16)
     pos = np.arange(T - rows, T, dtype=np.int64)
@@ -122,7 +122,7 @@ def test_sweep_peaked_scores():
     sel = _selection(g, pos)
     P.say(f"[case] sweep peaked scores {rows} rows")
     out, lse = _gpu(q, k, v, sel, seq, pos)
-    pick = [0, 5, 31, 32, 400, 777, 1000, 1023]
+    pick = [0, 5, 31, 32, 400, 777, 1000, 1023, 2047]
     oo, ol = _oracle(q, k, v, sel, seq, pos, pick)
     e = P.compare_attention(out[pick], lse[pick], oo, ol, "peaked")
     e2 = _vs_gather(out, lse, q, k, v, sel, seq, pos, "peaked")
@@ -131,23 +131,23 @@ def test_sweep_peaked_scores():
 
 def test_sweep_nan_past_the_rows():
     """Cache slots past each sequence's last row hold NaN (unwritten slots);
-    the rows' own regions end inside those chunks. Two sequences, 544 rows
-    each (positions 2,000 .. 2,543 and 3,000 .. 3,543 of 4,096 slots)."""
+    the rows' own regions end inside those chunks. Two sequences, 1,056 rows
+    each (positions 2,000 .. 3,055 and 3,000 .. 4,055 of 4,096 slots)."""
     T = 4096
     g, k, v = _kv(2, T, 12)
-    pos = np.concatenate([np.arange(2000, 2544), np.arange(3000, 3544)]).astype(np.int64)
-    seq = np.concatenate([np.zeros(544), np.ones(544)]).astype(np.int32)
-    k[0, 2544:] = float("nan")
-    v[0, 2544:] = float("nan")
-    k[1, 3544:] = float("nan")
-    v[1, 3544:] = float("nan")
+    pos = np.concatenate([np.arange(2000, 3056), np.arange(3000, 4056)]).astype(np.int64)
+    seq = np.concatenate([np.zeros(1056), np.ones(1056)]).astype(np.int32)
+    k[0, 3056:] = float("nan")
+    v[0, 3056:] = float("nan")
+    k[1, 4056:] = float("nan")
+    v[1, 4056:] = float("nan")
     rows = len(pos)
     q = torch.randn(rows, 16, 128, generator=g).to(torch.bfloat16)
     sel = _selection(g, pos)
     P.say(f"[case] sweep NaN past the rows, {rows} rows")
     out, lse = _gpu(q, k, v, sel, seq, pos)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    pick = [0, 31, 543, 544, 545, 1000, 1087]
+    pick = [0, 31, 1055, 1056, 1057, 2000, 2111]
     oo, ol = _oracle(q, k, v, sel, seq, pos, pick)
     e = P.compare_attention(out[pick], lse[pick], oo, ol, "NaN past the rows")
     P.say(f"  max err {e:.2e}")
@@ -156,9 +156,9 @@ def test_sweep_nan_past_the_rows():
 def test_sweep_nan_in_unselected_regions():
     """The rows select even regions only; the odd regions below every row's
     own region hold NaN in K and V. The gather never reads them; the sweep
-    reads whole chunks and must keep them out of scores and outputs. 1,024
-    rows at positions 3,072 .. 4,095 of one sequence."""
-    T, rows = 4096, 1024
+    reads whole chunks and must keep them out of scores and outputs. 2,048
+    rows at positions 2,048 .. 4,095 of one sequence."""
+    T, rows = 4096, 2048
     g, k, v = _kv(1, T, 33)
     pos = np.arange(T - rows, T, dtype=np.int64)
     seq = np.zeros(rows, np.int32)
@@ -175,19 +175,19 @@ def test_sweep_nan_in_unselected_regions():
     P.say(f"[case] sweep NaN in unselected regions, {rows} rows")
     out, lse = _gpu(q, k, v, sel, seq, pos)
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    pick = [0, 1, 31, 32, 500, 1000, 1023]
+    pick = [0, 1, 31, 32, 500, 1000, 2047]
     oo, ol = _oracle(q, k, v, sel, seq, pos, pick)
     e = P.compare_attention(out[pick], lse[pick], oo, ol, "NaN in unselected regions")
     P.say(f"  max err {e:.2e}")
 
 
 def test_sweep_mixed_tiles_invalid_rows_short_positions():
-    """1,030 rows (a ragged last tile of 6) over 3 sequences of 3,000 slots:
+    """2,054 rows (a ragged last tile of 6) over 3 sequences of 3,000 slots:
     tiles of one sequence at random positions (some below 8: own region only;
     some below 4,096: fewer than 512 candidates), tiles mixing sequences (left
     to the gather), invalid rows (no such sequence, position past the cache)
     inside tiles of one sequence, and a tile of invalid rows only."""
-    T, rows = 3000, 1030
+    T, rows = 3000, 2054
     g, k, v = _kv(3, T, 21)
     q = torch.randn(rows, 16, 128, generator=g).to(torch.bfloat16)
     seq = np.zeros(rows, np.int32)
@@ -206,10 +206,10 @@ def test_sweep_mixed_tiles_invalid_rows_short_positions():
     pos[0:8] = np.arange(8)                  # own region only
     pos[40:48] = [8, 9, 15, 16, 100, 200, 1000, 2999]
     invalid = np.zeros(rows, bool)
-    for r in (3, 70, 71, 200, 1029):
+    for r in (3, 70, 71, 200, 2053):
         invalid[r] = True
     seq[3], seq[70] = -1, 7
-    pos[71], pos[200], pos[1029] = T, T + 5, 10 ** 6
+    pos[71], pos[200], pos[2053] = T, T + 5, 10 ** 6
     invalid[32 * 20:32 * 21] = True          # a tile of invalid rows only
     seq[32 * 20:32 * 21] = -1
     sel = _selection(g, np.minimum(pos, T - 1), valid=~invalid)
@@ -219,7 +219,7 @@ def test_sweep_mixed_tiles_invalid_rows_short_positions():
     l = lse.cpu().numpy()
     assert np.all(o[invalid] == 0.0) and np.all(np.isneginf(l[invalid]))
     valid_rows = np.nonzero(~invalid)[0]
-    pick = [0, 1, 7, 40, 41, 42, 43, 44, 45, 46, 47, 64, 65, 72, 100, 130, 500, 1000, 1024, 1028]
+    pick = [0, 1, 7, 40, 41, 42, 43, 44, 45, 46, 47, 64, 65, 72, 100, 130, 500, 1000, 2048, 2052]
     pick += valid_rows[torch.randint(0, len(valid_rows), (8,), generator=g).numpy()].tolist()
     pick = sorted(set(r for r in pick if not invalid[r]))
     oo, ol = _oracle(q, k, v, sel, seq, pos, pick)
@@ -229,19 +229,19 @@ def test_sweep_mixed_tiles_invalid_rows_short_positions():
 
 
 def test_sweep_region_bound():
-    """A 66,000-slot context (8,250 regions): tiles whose own regions reach
-    region 8,192 are left to the gather, the others are swept; 1,024 rows at
-    positions 60,000 .. 60,511 and 65,488 .. 65,999."""
-    T = 66000
+    """A 42,000-slot context (5,250 regions): tiles whose own regions reach
+    region 5,120 are left to the gather, the others are swept; 2,048 rows at
+    positions 39,000 .. 40,023 and 40,976 .. 41,999."""
+    T = 42000
     g, k, v = _kv(1, T, 30)
-    pos = np.concatenate([np.arange(60000, 60512), np.arange(65488, 66000)]).astype(np.int64)
+    pos = np.concatenate([np.arange(39000, 40024), np.arange(40976, 42000)]).astype(np.int64)
     seq = np.zeros(len(pos), np.int32)
     rows = len(pos)
     q = torch.randn(rows, 16, 128, generator=g).to(torch.bfloat16)
     sel = _selection(g, pos)
     P.say(f"[case] sweep region bound, {rows} rows, T={T}")
     out, lse = _gpu(q, k, v, sel, seq, pos)
-    pick = [0, 511, 512, 530, 543, 544, 545, 1000, 1023]
+    pick = [0, 1023, 1024, 1040, 1055, 1056, 1057, 2000, 2047]
     oo, ol = _oracle(q, k, v, sel, seq, pos, pick)
     e = P.compare_attention(out[pick], lse[pick], oo, ol, "region bound")
     P.say(f"  max err {e:.2e}")

@@ -266,12 +266,18 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
   // others are stored as zero, so whatever their slots hold never reaches
   // a score or an output
   auto write = [&](const TlRegs& R, uint32_t um, int bf) {
-    const bool okk = (um >> kt) & 1u;
-    const bool oka = (um >> (2 * vi)) & 1u, okb = (um >> (2 * vi + 1)) & 1u;
-    const uint4 k = __builtin_bit_cast(uint4, R.k);
-    kbuf[bf * 512 + kwo] = okk ? k : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t a0 = oka ? R.va.x : 0u, a1 = oka ? R.va.y : 0u;
-    const uint32_t b0 = okb ? R.vb.x : 0u, b1 = okb ? R.vb.y : 0u;
+    uint4 k = __builtin_bit_cast(uint4, R.k);
+    uint32_t a0 = R.va.x, a1 = R.va.y, b0 = R.vb.x, b1 = R.vb.y;
+    if (um != 0xffffffffu) {  // uniform: most chunks of a prompt are attended throughout
+      const bool okk = (um >> kt) & 1u;
+      const bool oka = (um >> (2 * vi)) & 1u, okb = (um >> (2 * vi + 1)) & 1u;
+      k = okk ? k : make_uint4(0u, 0u, 0u, 0u);
+      a0 = oka ? a0 : 0u;
+      a1 = oka ? a1 : 0u;
+      b0 = okb ? b0 : 0u;
+      b1 = okb ? b1 : 0u;
+    }
+    kbuf[bf * 512 + kwo] = k;
     unsigned char* vd = reinterpret_cast<unsigned char*>(vbuf + bf * 512);
     *reinterpret_cast<uint32_t*>(vd + vwo[0]) = __builtin_amdgcn_perm(b0, a0, sel_even);
     *reinterpret_cast<uint32_t*>(vd + vwo[1]) = __builtin_amdgcn_perm(b0, a0, sel_odd);

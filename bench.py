@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0
 # profiles/sparse_attn_hbm_counters_decode16_ctx128k.md), each scaled by what
 # the counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # Valid only for the attention source the counters were taken on.
-ATTN_TRAFFIC = {"source_sha256": "2c10ec08ba759aaa21d605295ea46c3d477938d30d556da548256561f8c93a01",
-                "bytes_per_launch": 136237875}
+ATTN_TRAFFIC = {"source_sha256": "ef4e4fc315f463f7547b519935e05edc200a1f4595d7d35352148ede8fe7204c",
+                "bytes_per_launch": 136238464}
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"

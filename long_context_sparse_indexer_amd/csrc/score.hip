@@ -60,37 +60,45 @@ namespace s5 {
 // The bf16 and e4m3 roundings use gfx950's conversion instructions
 // (bf16x2_hw, e4m3x2_hw), which give the same bits as the software forms.
 // ---------------------------------------------------------------------------
-__device__ inline uint2 qprep8(int mode, const void* __restrict__ qin, int64_t qs, int64_t r,
-                               int h, int c, int lane, const float* __restrict__ w, float eps,
-                               const uint16_t* __restrict__ rope, int64_t rope_rows,
-                               const int64_t* __restrict__ row_pos) {
-  if (mode == 1)
-    return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(qin) + r * qs + h * 64 + c * 8);
-  const uint16_t* q = static_cast<const uint16_t*>(qin);
-  int64_t p = row_pos[r];
-  if (p < 0 || p >= rope_rows) p = 0;  // such a row selects nothing later; keep reads in range
-  const bool rotated = c < 4, first_half = c < 2;
+// The bf16 path in two halves, so that a caller can issue the loads first
+// and keep other loads in flight while they arrive: qprep8_load reads dims
+// 8c..8c+7 of head h of row r, the rotation's cos and sin at position p
+// (already clamped to the table) and the norm weights; qprep8_math does the
+// arithmetic.
+struct QPrep8In {
+  uint4 q, c, s;
+  float4 w0, w1;
+};
+__device__ inline QPrep8In qprep8_load(const uint16_t* __restrict__ q, int64_t qs, int64_t r, int h,
+                                       int c, const float* __restrict__ w,
+                                       const uint16_t* __restrict__ rope, int64_t p) {
   const int fi = (c & 1) * 8;
-  const uint4 qraw = ldg16(q + r * qs + h * 64 + c * 8);
-  const uint4 craw = ldg16(rope + p * 32 + fi);
-  const uint4 sraw = ldg16(rope + p * 32 + 16 + fi);
+  QPrep8In in;
+  in.q = ldg16(q + r * qs + h * 64 + c * 8);
+  in.c = ldg16(rope + p * 32 + fi);
+  in.s = ldg16(rope + p * 32 + 16 + fi);
+  in.w0 = reinterpret_cast<const float4*>(w)[2 * c];
+  in.w1 = reinterpret_cast<const float4*>(w)[2 * c + 1];
+  return in;
+}
+
+__device__ inline uint2 qprep8_math(const QPrep8In& in, int c, int lane, float eps) {
+  const bool rotated = c < 4, first_half = c < 2;
   float x[8], sq[8], y[8];
-  unpack_bf16x8(qraw, x);
+  unpack_bf16x8(in.q, x);
 #pragma unroll
   for (int i = 0; i < 8; ++i) sq[i] = x[i] * x[i];
   const float ms = sum8_lanes(pair8(sq), lane) / 64.0f;
   const float rr = 1.0f / sqrtf(ms + eps);
-  const float4 w0 = reinterpret_cast<const float4*>(w)[2 * c];
-  const float4 w1 = reinterpret_cast<const float4*>(w)[2 * c + 1];
-  const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  const float wv[8] = {in.w0.x, in.w0.y, in.w0.z, in.w0.w, in.w1.x, in.w1.y, in.w1.z, in.w1.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float scale = 1.0f + wv[i];
     y[i] = (x[i] * rr) * scale;
   }
   float cf[8], sf[8], v[8];
-  unpack_bf16x8(craw, cf);
-  unpack_bf16x8(sraw, sf);
+  unpack_bf16x8(in.c, cf);
+  unpack_bf16x8(in.s, sf);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float other = dpp<DPP_QUAD_XOR2>(y[i]);
@@ -111,6 +119,31 @@ __device__ inline uint2 qprep8(int mode, const void* __restrict__ qin, int64_t q
   uint32_t hi = e4m3x2_hw<false>(bf[4], bf[5], 0u);
   hi = e4m3x2_hw<true>(bf[6], bf[7], hi);
   return make_uint2(lo, hi);
+}
+
+// Keeps the compiler from starting the arithmetic on a QPrep8In before this
+// point (it would wait for the loads there, ahead of later loads).
+__device__ inline void qprep8_fence(QPrep8In& in) {
+  asm volatile("" : "+v"(in.q.x), "+v"(in.q.y), "+v"(in.q.z), "+v"(in.q.w));
+  asm volatile("" : "+v"(in.c.x), "+v"(in.c.y), "+v"(in.c.z), "+v"(in.c.w));
+  asm volatile("" : "+v"(in.s.x), "+v"(in.s.y), "+v"(in.s.z), "+v"(in.s.w));
+  asm volatile("" : "+v"(in.w0.x), "+v"(in.w0.y), "+v"(in.w0.z), "+v"(in.w0.w));
+  asm volatile("" : "+v"(in.w1.x), "+v"(in.w1.y), "+v"(in.w1.z), "+v"(in.w1.w));
+}
+
+__device__ inline int64_t qprep_pos(int64_t p, int64_t rope_rows) {
+  return (p < 0 || p >= rope_rows) ? 0 : p;  // such a row selects nothing later; keep reads in range
+}
+
+__device__ inline uint2 qprep8(int mode, const void* __restrict__ qin, int64_t qs, int64_t r,
+                               int h, int c, int lane, const float* __restrict__ w, float eps,
+                               const uint16_t* __restrict__ rope, int64_t rope_rows,
+                               const int64_t* __restrict__ row_pos) {
+  if (mode == 1)
+    return *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(qin) + r * qs + h * 64 + c * 8);
+  const QPrep8In in = qprep8_load(static_cast<const uint16_t*>(qin), qs, r, h, c, w, rope,
+                                  qprep_pos(row_pos[r], rope_rows));
+  return qprep8_math(in, c, lane, eps);
 }
 
 // exact values of 8 packed e4m3 codes (every e4m3 value is an fp32 value)
@@ -299,10 +332,12 @@ __global__ __launch_bounds__(256) void score_kernel(
 // score is then rounded as the oracle rounds it (exact.hpp). Waves 0 and 1
 // prep the row's 16 heads into LDS once per block (the same steps as
 // qprep_kernel); the first candidate block zeroes the row's top-k arrival
-// counters. Each wave's summary loads are issued before the prep.
+// counters. The prep's loads are issued first, then each wave's first 8
+// quads of summary loads, then the prep's arithmetic.
 // ---------------------------------------------------------------------------
 constexpr int SM_CB = 256;  // candidates per block
 
+template <bool PREPARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_exact_mfma_kernel(
     const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
     const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
@@ -320,10 +355,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int64_t cb0 = (int64_t)blockIdx.x * SM_CB + 64 * wave;
   const bool live = cb0 < nc;
   const int64_t jend = live ? (cb0 + 64 < nc ? cb0 + 64 : nc) : 0;
+  // The query prep's loads go out first (every wave loads the heads of wave
+  // & 1, waves 0 and 1 store the result), then the summary loads, so that
+  // the prep waits for its own loads only.
+  const int ph = 8 * (wave & 1) + (lane >> 3), pc = lane & 7;
+  QPrep8In pin;
+  uint2 pre;
+  if constexpr (PREPARED)
+    pre = *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(prep.q) +
+                                          row * prep.q_stride_row + ph * 64 + pc * 8);
+  else
+    pin = qprep8_load(static_cast<const uint16_t*>(prep.q), prep.q_stride_row, row, ph, pc,
+                      prep.w, static_cast<const uint16_t*>(prep.rope), qprep_pos(p, prep.rope_rows));
   // this lane's 16 summary bytes of quad u: candidate cb0 + 4u + ij, group
-  // g, dims 16k..16k+15 (candidates past jend load jend - 1 again). Quads
-  // are loaded four at a time, two groups ahead of the one computed.
-  const uint8_t* Sw = S + (int64_t)s * ssb + cb0 * 256;
+  // g, dims 16k..16k+15 (candidates past jend load jend - 1 again; a wave
+  // past the row's candidates loads region 0 and stops after the prep).
+  // Quads are loaded four at a time, two groups ahead of the one computed.
+  const uint8_t* Sw = S + (int64_t)s * ssb + (live ? cb0 * 256 : 0);
   const uint32_t jlast = live ? (uint32_t)(jend - cb0 - 1) : 0u;
   auto load4 = [&](int u0, uint4 (&dst)[4]) {
 #pragma unroll
@@ -333,17 +381,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
   };
   uint4 bA[4], bB[4], bC[4];
-  if (live) {
-    load4(0, bA);
-    load4(4, bB);
+  load4(0, bA);
+  load4(4, bB);
+  uint2 pk;
+  if constexpr (PREPARED) {
+    pk = pre;
+  } else {
+    qprep8_fence(pin);
+    pk = qprep8_math(pin, pc, lane, prep.eps);
   }
-  if (wave < 2) {
-    const int h = 8 * wave + (lane >> 3), c = lane & 7;
-    const uint2 pk = qprep8(prep.prepared ? 1 : 0, prep.q, prep.q_stride_row, row, h, c, lane,
-                            prep.w, prep.eps, static_cast<const uint16_t*>(prep.rope),
-                            prep.rope_rows, prep.row_pos);
-    *reinterpret_cast<uint2*>(&q_lds[h * 64 + c * 8]) = pk;
-  }
+  if (wave < 2) *reinterpret_cast<uint2*>(&q_lds[ph * 64 + pc * 8]) = pk;
   __syncthreads();
   if (!live) return;
   // A operand: head 4g + ij, dims 16k..16k+15 as packed e4m3, converted per use
@@ -403,9 +450,14 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.rows == 0 || a.R_cap == 0) return hipSuccess;
   if (a.exact) {
     const dim3 grid((unsigned)((a.R_cap + SM_CB - 1) / SM_CB), (unsigned)a.rows);
-    hipLaunchKernelGGL(score_exact_mfma_kernel, grid, dim3(256), 0, stream, a.w_head,
-                       a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                       a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
+    if (a.prep.prepared)
+      hipLaunchKernelGGL(score_exact_mfma_kernel<true>, grid, dim3(256), 0, stream, a.w_head,
+                         a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
+                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
+    else
+      hipLaunchKernelGGL(score_exact_mfma_kernel<false>, grid, dim3(256), 0, stream, a.w_head,
+                         a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
+                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));

@@ -13,7 +13,11 @@
 // a chunk no row of the tile needs is skipped; inside a chunk, a row's scores
 // for tokens outside its selected regions and its own region (up to its
 // position) are -inf before its softmax. The result is the same attention as
-// the per-row gather, up to summation order.
+// the per-row gather, up to summation order, wherever the K and V the tile's
+// rows attend are finite: the rows of a tile share the staged chunk, so a
+// NaN or inf in a token that one row attends also reaches the tile's other
+// rows (through their -inf scores and zero probabilities), where the gather
+// keeps rows apart. Tokens no row of the tile attends are staged as zero.
 //
 // Work per chunk, per wave (rows 4w .. 4w+3 of the tile; MFMA row n = row
 // 4w + n/4, query head n%4):

@@ -16,8 +16,10 @@
 // rows (output columns) are the A operand, hidden rows the B operand, so a
 // lane ends with 4 consecutive output columns of one row (an 8-byte store).
 // fp32 accumulation, one rounding to bf16 at the end.
-//  - proj_wide_kernel (many rows): 256 columns x 128 rows a workgroup, 8 waves
-//    of 64 x 64; k in steps of 64 through LDS, double-buffered; tiles go from
+//  - proj_wide_kernel (many rows): 320 columns x 128 rows a workgroup (the
+//    layer's 4,624 columns x 2,048 rows make 240 workgroups, one round on 256
+//    CUs; 256-column tiles made 304, two rounds), 8 waves of 80 columns x 64
+//    rows; k in steps of 64 through LDS, double-buffered; tiles go from
 //    memory straight into LDS (global_load_lds, 16 B a lane) with 16-byte
 //    pieces XOR-swizzled by row so the fragment reads hit distinct banks.
 //  - proj_narrow_kernel (a few rows, decode): the weight's 38 MB dominate, so
@@ -59,12 +61,13 @@ __device__ inline uint2 pj_pack4(f32x4 v) {
                     bf16_bits(v[2]) | (bf16_bits(v[3]) << 16));
 }
 
-constexpr int WD_BC = 256, WD_BR = 128, WD_BK = 64;  // wide tile
+constexpr int WD_BC = 320, WD_BR = 128, WD_BK = 64;  // wide tile
+constexpr int WD_CB = WD_BC / 64;                  // 16-column blocks per wave (4 waves across)
 constexpr int WD_PIECES = WD_BK / 8;                // 16-byte pieces per tile row
 
 }  // namespace
 
-// one stage of the wide kernel's LDS: [W tile 256 x 64 | hidden tile 128 x 64]
+// one stage of the wide kernel's LDS: [W tile 320 x 64 | hidden tile 128 x 64]
 struct WdStage {
   uint4 v[(WD_BC + WD_BR) * WD_PIECES];
 };
@@ -79,16 +82,16 @@ __global__ __launch_bounds__(512) void proj_wide_kernel(const uint16_t* __restri
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, qd = lane >> 4;
   const int c0 = blockIdx.x * WD_BC, r0 = blockIdx.y * WD_BR;
-  const int wc = wave & 3, wr = wave >> 2;  // this wave: columns 64 wc.., rows 64 wr..
+  const int wc = wave & 3, wr = wave >> 2;  // this wave: columns 80 wc.., rows 64 wr..
 
   // staging: a wave's load fills 1 KB = 8 tile rows; lane -> (row l/8, slot l%8)
-  // holding the row's piece slot ^ (row & 7). W tile: 32 such loads, hidden: 16.
+  // holding the row's piece slot ^ (row & 7). W tile: 40 such loads, hidden: 16.
   const int lrow = lane >> 3, lslot = lane & 7;
-  const uint16_t* wsrc[4];
+  const uint16_t* wsrc[WD_CB];
   const uint16_t* hsrc[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tr = 32 * wave + 8 * i + lrow;
+  for (int i = 0; i < WD_CB; ++i) {
+    const int tr = 8 * WD_CB * wave + 8 * i + lrow;
     wsrc[i] = w + (int64_t)min(c0 + tr, N - 1) * K + 8 * (lslot ^ (tr & 7));
   }
 #pragma unroll
@@ -99,15 +102,16 @@ __global__ __launch_bounds__(512) void proj_wide_kernel(const uint16_t* __restri
   auto stage = [&](int kt, WdStage& sd) {
     const int k0 = kt * WD_BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pj_load_lds16(wsrc[i] + k0, &sd.v[(32 * wave + 8 * i) * WD_PIECES]);
+    for (int i = 0; i < WD_CB; ++i)
+      pj_load_lds16(wsrc[i] + k0, &sd.v[(8 * WD_CB * wave + 8 * i) * WD_PIECES]);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       pj_load_lds16(hsrc[i] + k0, &sd.v[(WD_BC + 16 * wave + 8 * i) * WD_PIECES]);
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[WD_CB][4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < WD_CB; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const WdStage& sd) {
@@ -115,10 +119,10 @@ __global__ __launch_bounds__(512) void proj_wide_kernel(const uint16_t* __restri
     const uint4* hl = &sd.v[WD_BC * WD_PIECES];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint4 af[4], bfr[4];
+      uint4 af[WD_CB], bfr[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int tr = 64 * wc + 16 * a + n;
+      for (int a = 0; a < WD_CB; ++a) {
+        const int tr = 16 * WD_CB * wc + 16 * a + n;
         af[a] = wl[tr * WD_PIECES + ((4 * ks + qd) ^ (tr & 7))];
       }
 #pragma unroll
@@ -127,7 +131,7 @@ __global__ __launch_bounds__(512) void proj_wide_kernel(const uint16_t* __restri
         bfr[b] = hl[tr * WD_PIECES + ((4 * ks + qd) ^ (tr & 7))];
       }
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < WD_CB; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = pj_mfma(af[a], bfr[b], acc[a][b]);
     }
@@ -149,10 +153,10 @@ __global__ __launch_bounds__(512) void proj_wide_kernel(const uint16_t* __restri
     compute(st1);
   }
 
-  // lane (n, qd) of tile (a, b): row 64 wr + 16 b + n, columns 64 wc + 16 a + 4 qd ..
+  // lane (n, qd) of tile (a, b): row 64 wr + 16 b + n, columns 80 wc + 16 a + 4 qd ..
 #pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    const int ct = c0 + 64 * wc + 16 * a;  // the 16-column tile
+  for (int a = 0; a < WD_CB; ++a) {
+    const int ct = c0 + 16 * WD_CB * wc + 16 * a;  // the 16-column tile
     if (ct >= N) continue;
     const int p = pj_part(o, ct);
     const int cc = ct - o.start[p] + 4 * qd;

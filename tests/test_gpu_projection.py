@@ -139,3 +139,19 @@ def test_project_64_heads_of_192():
     P.say("[case] projection 64 x 192 geometry")
     _, outs = _run(h, w, widths, q_heads=64, head_dim=192)
     _compare(outs, h, w, widths, range(70), "64x192")
+
+
+def test_project_wide_tiles_64_heads_of_192():
+    """The tiled kernel on Step-5's own shape: 300 rows (two full 128-row
+    tiles and a ragged one), 15,424 columns (48 full 320-column tiles and a
+    last one of 64), hidden 512; 24 rows compared, among them each tile's
+    first and last."""
+    widths = orc.proj_sizes(q_heads=64, head_dim=192, gate=64)
+    g, h, w = _inputs(300, 512, sum(widths), 12)
+    P.say("[case] projection 300 rows, 64 x 192 geometry (tiled kernel)")
+    bufs, outs = _run(h, w, widths, pad=16, q_heads=64, head_dim=192)
+    pick = sorted(set([0, 1, 127, 128, 255, 256, 257, 298, 299] +
+                      torch.randint(0, 300, (15,), generator=g).tolist()))
+    _compare(outs, h, w, widths, pick, "wide 64x192")
+    for b, wd in zip(bufs, widths):
+        assert torch.all(b[:, wd:].float() == -7.0), "wrote past a part's width"

@@ -19,7 +19,8 @@
 //  - proj_wide_kernel (many rows): 320 columns x 128 rows a workgroup (the
 //    layer's 4,624 columns x 2,048 rows make 240 workgroups, one round on 256
 //    CUs; 256-column tiles made 304, two rounds), 8 waves of 80 columns x 64
-//    rows; k in steps of 64 through LDS, double-buffered; tiles go from
+//    rows, the tiles of a chip die adjacent in column-tile order; k in steps
+//    of 64 through LDS, double-buffered; tiles go from
 //    memory straight into LDS (global_load_lds, 16 B a lane) with 16-byte
 //    pieces XOR-swizzled by row so the fragment reads hit distinct banks.
 //  - proj_narrow_kernel (a few rows, decode): the weight's 38 MB dominate, so
@@ -81,7 +82,18 @@ __global__ __launch_bounds__(512) void proj_wide_kernel(const uint16_t* __restri
   __shared__ WdStage st0, st1;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, qd = lane >> 4;
-  const int c0 = blockIdx.x * WD_BC, r0 = blockIdx.y * WD_BR;
+  int bx, by;
+  {
+    // tiles of one 8-way round-robin slot (workgroup id mod 8, the chip die
+    // the workgroup lands on) are consecutive in column-tile-major order, so
+    // a die's workgroups share weight tiles through its L2
+    const int ncol = (N + WD_BC - 1) / WD_BC, nrow = (rows + WD_BR - 1) / WD_BR, nt = ncol * nrow;
+    const int L = blockIdx.x, per = (nt + 7) >> 3, r = nt & 7, x = L & 7, s = L >> 3;
+    const int T = (r == 0 || x < r) ? x * per + s : r * per + (x - r) * (per - 1) + s;
+    bx = T / nrow;
+    by = T - bx * nrow;
+  }
+  const int c0 = bx * WD_BC, r0 = by * WD_BR;
   const int wc = wave & 3, wr = wave >> 2;  // this wave: columns 80 wc.., rows 64 wr..
 
   // staging: a wave's load fills 1 KB = 8 tile rows; lane -> (row l/8, slot l%8)
@@ -293,7 +305,7 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   const int N = a.outs.start[PROJ_PARTS];
   if (a.rows >= S5_PROJ_WIDE_MIN_ROWS) {
-    const dim3 grid((unsigned)((N + WD_BC - 1) / WD_BC), (unsigned)((a.rows + WD_BR - 1) / WD_BR));
+    const dim3 grid((unsigned)(((N + WD_BC - 1) / WD_BC) * ((a.rows + WD_BR - 1) / WD_BR)));
     hipLaunchKernelGGL(proj_wide_kernel, grid, dim3(512), 0, stream, (const uint16_t*)a.hidden,
                        a.hidden_stride, a.rows, a.K, (const uint16_t*)a.weight, N, a.outs);
   } else {

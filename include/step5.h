@@ -215,6 +215,54 @@ int step5_index_score_topk(const step5_geom* geom, uint32_t flags, const void* q
  * geometry or sizes are not accepted). */
 size_t step5_index_score_topk_workspace(const step5_geom* geom, int32_t rows, int64_t R_cap);
 
+/* The append half of step5_index_append_score_topk: the arguments of
+ * step5_index_append that step5_index_score_topk does not have. */
+typedef struct step5_append_in {
+  const void* k_new;       /* bf16 [rows, groups, idx_dim], row stride new_stride_row */
+  const void* z_new;
+  int64_t new_stride_row;
+  void* k_ring;            /* bf16 [B, ring_slots, groups, idx_dim] */
+  void* z_ring;
+  int64_t ring_slots;
+  int64_t ring_stride_b;
+  const float* ln_w;       /* the indexer k LayerNorm, as in step5_index_append */
+  const float* ln_b;
+  float ln_eps;
+} step5_append_in;
+
+/*
+ * A decode step's indexer work in one call: step5_index_append of each
+ * row's new token (as with STEP5_APPEND_ONE_PER_SEQ) and
+ * step5_index_score_topk of the rows, with the same results as those two
+ * calls made one after the other.
+ * [TensorFold #903, indexer commit note: every completed region summarised;
+ * q prep, scores, top 512; prompt-path commit note: the k and z rings]
+ *
+ * A row scores only regions before its own, and the append writes a row's
+ * ring slot and, when the token completes it, the row's own region, so the
+ * two halves touch different data when no two rows share a sequence: the
+ * appends then run in extra workgroups of the selection's launch, on
+ * compute units the selection leaves idle, instead of a launch of their own.
+ * Precondition (device values, not checked): no two rows share a sequence,
+ * as STEP5_APPEND_ONE_PER_SEQ guarantees for step5_index_append.
+ *
+ * ap          the append's own arguments (step5_append_in), not null.
+ * flags, q .. ws_bytes, stream: as for step5_index_score_topk, except that
+ *             rope_cs is required (the append's k prep uses it) and the
+ *             summary is written (each completed region); ap and these
+ *             arguments are checked as the two calls check theirs, and an
+ *             error from either writes nothing.
+ * rows == 0 is a successful no-op.
+ */
+int step5_index_append_score_topk(const step5_geom* geom, uint32_t flags,
+                                  const step5_append_in* ap, const void* q, int64_t q_stride_row,
+                                  const float* q_norm_w, float q_eps, const void* rope_cs,
+                                  int64_t rope_rows, const float* w_head, int64_t w_stride_row,
+                                  const int32_t* row_seq, const int64_t* row_pos, int32_t rows,
+                                  void* summary, int64_t B, int64_t R_cap, int64_t s_stride_b,
+                                  int32_t* sel_ids, float* sel_scores, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream);
+
 /*
  * Attention of each row over its selected regions plus its own region.
  * [TensorFold #903, indexer commit note: attention over the picks and the

@@ -78,6 +78,10 @@ def lib():
         L.step5_index_score_topk.restype = C.c_int
         L.step5_index_score_topk.argtypes = [G, U32, P, I64, P, F, P, I64, P, I64, P, P, I32, P,
                                              I64, I64, I64, P, P, P, SZ, P]
+        L.step5_index_append_score_topk.restype = C.c_int
+        L.step5_index_append_score_topk.argtypes = [G, U32, C.POINTER(Step5AppendIn), P, I64, P, F,
+                                                    P, I64, P, I64, P, P, I32, P, I64, I64, I64, P,
+                                                    P, P, SZ, P]
         L.step5_index_score_topk_workspace.restype = SZ
         L.step5_index_score_topk_workspace.argtypes = [G, I32, I64]
         L.step5_sparse_attn.restype = C.c_int
@@ -145,15 +149,7 @@ def step5_index_summarize(k: torch.Tensor, z: torch.Tensor, t0: int, ln_w: torch
     _check("step5_index_summarize", st)
 
 
-def step5_index_append(k_new: torch.Tensor, z_new: torch.Tensor, row_seq: torch.Tensor,
-                       row_pos: torch.Tensor, k_ring: torch.Tensor, z_ring: torch.Tensor,
-                       ln_w: torch.Tensor, ln_b: torch.Tensor, ln_eps: float, rope: torch.Tensor,
-                       summary: torch.Tensor, one_per_seq: bool = False, stream=None) -> None:
-    """Write each row's new token (k_new, z_new: bf16 [rows, 4, 64]) to slot
-    row_pos mod slots of its sequence's rings (k_ring, z_ring: bf16
-    [B, slots, 4, 64]) and summarise the regions those tokens complete into
-    summary (e4m3 as uint8 [B, R_cap, 4, 64]). one_per_seq: no two rows share a
-    sequence (a decode step), which lets the call run as one launch."""
+def _append_checks(k_new, z_new, row_seq, row_pos, k_ring, z_ring, summary, rope):
     _need(k_new.dtype == torch.bfloat16 and z_new.dtype == torch.bfloat16, "k_new, z_new must be bf16")
     _need(k_new.dim() == 3 and k_new.shape == z_new.shape and
           tuple(k_new.shape[1:]) == (GROUPS, IDX_DIM), "k_new, z_new must be [rows, 4, 64]")
@@ -177,6 +173,19 @@ def step5_index_append(k_new: torch.Tensor, z_new: torch.Tensor, row_seq: torch.
           row_seq.is_contiguous() and row_pos.is_contiguous() and
           row_seq.numel() == k_new.shape[0] and row_pos.numel() == k_new.shape[0],
           "row_seq int32 [rows], row_pos int64 [rows], contiguous")
+    return summary
+
+
+def step5_index_append(k_new: torch.Tensor, z_new: torch.Tensor, row_seq: torch.Tensor,
+                       row_pos: torch.Tensor, k_ring: torch.Tensor, z_ring: torch.Tensor,
+                       ln_w: torch.Tensor, ln_b: torch.Tensor, ln_eps: float, rope: torch.Tensor,
+                       summary: torch.Tensor, one_per_seq: bool = False, stream=None) -> None:
+    """Write each row's new token (k_new, z_new: bf16 [rows, 4, 64]) to slot
+    row_pos mod slots of its sequence's rings (k_ring, z_ring: bf16
+    [B, slots, 4, 64]) and summarise the regions those tokens complete into
+    summary (e4m3 as uint8 [B, R_cap, 4, 64]). one_per_seq: no two rows share a
+    sequence (a decode step), which lets the call run as one launch."""
+    summary = _append_checks(k_new, z_new, row_seq, row_pos, k_ring, z_ring, summary, rope)
     st = lib().step5_index_append(
         C.byref(GEOM), STEP5_APPEND_ONE_PER_SEQ if one_per_seq else 0, _ptr(k_new), _ptr(z_new),
         k_new.stride(0), _ptr(row_seq), _ptr(row_pos),
@@ -212,13 +221,8 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     return workspace
 
 
-def step5_index_score_topk(q: torch.Tensor, w_head: torch.Tensor, row_seq: torch.Tensor,
-                           row_pos: torch.Tensor, summary: torch.Tensor, sel_ids: torch.Tensor,
-                           sel_scores: Optional[torch.Tensor] = None, *,
-                           q_norm_w: Optional[torch.Tensor] = None, q_eps: float = 1e-6,
-                           rope: Optional[torch.Tensor] = None, q_is_e4m3: bool = False,
-                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Scores and top-512 per (row, group) into sel_ids (int32 [rows, 4, 512])."""
+def _score_checks(q, w_head, row_seq, row_pos, summary, sel_ids, sel_scores, q_norm_w, rope,
+                  q_is_e4m3, workspace):
     q = _u8(q) if q_is_e4m3 else q
     rows = q.shape[0]
     _need(q.dim() == 3 and tuple(q.shape[1:]) == (IDX_HEADS, IDX_DIM) and q.stride(2) == 1 and
@@ -242,12 +246,61 @@ def step5_index_score_topk(q: torch.Tensor, w_head: torch.Tensor, row_seq: torch
     B, R_cap = summary.shape[0], summary.shape[1]
     nbytes = step5_index_score_topk_workspace(rows, R_cap)
     workspace = _workspace(nbytes, q.device, workspace)
+    return q, rows, summary, w_stride, B, R_cap, nbytes, workspace
+
+
+def step5_index_score_topk(q: torch.Tensor, w_head: torch.Tensor, row_seq: torch.Tensor,
+                           row_pos: torch.Tensor, summary: torch.Tensor, sel_ids: torch.Tensor,
+                           sel_scores: Optional[torch.Tensor] = None, *,
+                           q_norm_w: Optional[torch.Tensor] = None, q_eps: float = 1e-6,
+                           rope: Optional[torch.Tensor] = None, q_is_e4m3: bool = False,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Scores and top-512 per (row, group) into sel_ids (int32 [rows, 4, 512])."""
+    q, rows, summary, w_stride, B, R_cap, nbytes, workspace = _score_checks(
+        q, w_head, row_seq, row_pos, summary, sel_ids, sel_scores, q_norm_w, rope, q_is_e4m3,
+        workspace)
     st = lib().step5_index_score_topk(
         C.byref(GEOM), STEP5_Q_E4M3 if q_is_e4m3 else 0, _ptr(q), q.stride(0), _ptr(q_norm_w),
         float(q_eps), _ptr(rope), rope.shape[0] if rope is not None else 0, _ptr(w_head), w_stride,
         _ptr(row_seq), _ptr(row_pos), rows, _ptr(summary), B, R_cap, summary.stride(0),
         _ptr(sel_ids), _ptr(sel_scores), _ptr(workspace), nbytes, _stream(stream))
     _check("step5_index_score_topk", st)
+
+
+class Step5AppendIn(C.Structure):
+    """The append half of step5_index_append_score_topk (step5_append_in)."""
+    _fields_ = [("k_new", C.c_void_p), ("z_new", C.c_void_p), ("new_stride_row", C.c_int64),
+                ("k_ring", C.c_void_p), ("z_ring", C.c_void_p), ("ring_slots", C.c_int64),
+                ("ring_stride_b", C.c_int64), ("ln_w", C.c_void_p), ("ln_b", C.c_void_p),
+                ("ln_eps", C.c_float)]
+
+
+def step5_index_append_score_topk(k_new: torch.Tensor, z_new: torch.Tensor, k_ring: torch.Tensor,
+                                  z_ring: torch.Tensor, ln_w: torch.Tensor, ln_b: torch.Tensor,
+                                  ln_eps: float, q: torch.Tensor, w_head: torch.Tensor,
+                                  row_seq: torch.Tensor, row_pos: torch.Tensor,
+                                  summary: torch.Tensor, sel_ids: torch.Tensor,
+                                  sel_scores: Optional[torch.Tensor] = None, *,
+                                  rope: torch.Tensor, q_norm_w: Optional[torch.Tensor] = None,
+                                  q_eps: float = 1e-6, q_is_e4m3: bool = False,
+                                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """step5_index_append (rows of distinct sequences) and
+    step5_index_score_topk of the same rows in one call: the appends run in
+    extra workgroups of the selection's launch. The rows must not share a
+    sequence (not checked: device values)."""
+    summary = _append_checks(k_new, z_new, row_seq, row_pos, k_ring, z_ring, summary, rope)
+    q, rows, summary, w_stride, B, R_cap, nbytes, workspace = _score_checks(
+        q, w_head, row_seq, row_pos, summary, sel_ids, sel_scores, q_norm_w, rope, q_is_e4m3,
+        workspace)
+    _need(k_new.shape[0] == rows, "k_new and q must have the same rows")
+    ap = Step5AppendIn(_ptr(k_new), _ptr(z_new), k_new.stride(0), _ptr(k_ring), _ptr(z_ring),
+                       k_ring.shape[1], k_ring.stride(0), _ptr(ln_w), _ptr(ln_b), float(ln_eps))
+    st = lib().step5_index_append_score_topk(
+        C.byref(GEOM), STEP5_Q_E4M3 if q_is_e4m3 else 0, C.byref(ap), _ptr(q), q.stride(0),
+        _ptr(q_norm_w), float(q_eps), _ptr(rope), rope.shape[0], _ptr(w_head), w_stride,
+        _ptr(row_seq), _ptr(row_pos), rows, _ptr(summary), B, R_cap, summary.stride(0),
+        _ptr(sel_ids), _ptr(sel_scores), _ptr(workspace), nbytes, _stream(stream))
+    _check("step5_index_append_score_topk", st)
 
 
 def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

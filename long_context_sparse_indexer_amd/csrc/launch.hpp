@@ -127,6 +127,9 @@ struct TopkArgs {
   unsigned* arrivals;    // [rows*4], zero on entry (q prep zeroes them)
   int32_t* sel_ids;
   float* sel_scores;
+  // optional: the cache append of a call whose rows are of distinct
+  // sequences, run by extra workgroups of the same launch (one per row)
+  const AppendArgs* append;
 };
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream);
 

@@ -123,17 +123,13 @@ STEP5_EXPORT int step5_index_summarize(const step5_geom* geom, const void* k, co
   return from_hip(s5::launch_summarize(a, stream));
 }
 
-STEP5_EXPORT int step5_index_append(const step5_geom* geom, uint32_t flags, const void* k_new,
-                                    const void* z_new,
-                                    int64_t new_stride_row, const int32_t* row_seq,
-                                    const int64_t* row_pos, int32_t rows, void* k_ring,
-                                    void* z_ring, int64_t B, int64_t ring_slots,
-                                    int64_t ring_stride_b, const float* ln_w, const float* ln_b,
-                                    float ln_eps, const void* rope_cs, int64_t rope_rows,
-                                    void* summary, int64_t s_stride_b, int64_t R_cap,
-                                    hipStream_t stream) {
-  const int gs = check_geom(geom);
-  if (gs) return gs;
+// Checks the arguments of an append and fills its launch arguments.
+static int append_args(uint32_t flags, const void* k_new, const void* z_new,
+                       int64_t new_stride_row, const int32_t* row_seq, const int64_t* row_pos,
+                       int32_t rows, void* k_ring, void* z_ring, int64_t B, int64_t ring_slots,
+                       int64_t ring_stride_b, const float* ln_w, const float* ln_b, float ln_eps,
+                       const void* rope_cs, int64_t rope_rows, void* summary, int64_t s_stride_b,
+                       int64_t R_cap, s5::AppendArgs* a) {
   if (rows < 0 || (flags & ~STEP5_APPEND_ONE_PER_SEQ) != 0) return STEP5_E_INVALID;
   if (rows == 0) return STEP5_OK;
   if (!k_new || !z_new || !row_seq || !row_pos || !k_ring || !z_ring || !ln_w || !ln_b ||
@@ -151,28 +147,45 @@ STEP5_EXPORT int step5_index_append(const step5_geom* geom, uint32_t flags, cons
   if (!finite_pos(ln_eps) || rope_rows < kRegion) return STEP5_E_INVALID;
   if (R_cap < 1 || s_stride_b < 0 || (s_stride_b % 16) != 0) return STEP5_E_INVALID;
   if (B > 1 && s_stride_b < R_cap * kRegionBytes) return STEP5_E_INVALID;
+  a->k_new = k_new;
+  a->z_new = z_new;
+  a->new_stride_row = new_stride_row;
+  a->row_seq = row_seq;
+  a->row_pos = row_pos;
+  a->rows = rows;
+  a->k_ring = k_ring;
+  a->z_ring = z_ring;
+  a->B = B;
+  a->slots = ring_slots;
+  a->ring_stride_b = ring_stride_b;
+  a->ln_w = ln_w;
+  a->ln_b = ln_b;
+  a->eps = ln_eps;
+  a->rope = rope_cs;
+  a->rope_rows = rope_rows;
+  a->summary = summary;
+  a->ssb = s_stride_b;
+  a->R_cap = R_cap;
+  a->one_per_seq = (flags & STEP5_APPEND_ONE_PER_SEQ) != 0;
+  return STEP5_OK;
+}
 
+STEP5_EXPORT int step5_index_append(const step5_geom* geom, uint32_t flags, const void* k_new,
+                                    const void* z_new,
+                                    int64_t new_stride_row, const int32_t* row_seq,
+                                    const int64_t* row_pos, int32_t rows, void* k_ring,
+                                    void* z_ring, int64_t B, int64_t ring_slots,
+                                    int64_t ring_stride_b, const float* ln_w, const float* ln_b,
+                                    float ln_eps, const void* rope_cs, int64_t rope_rows,
+                                    void* summary, int64_t s_stride_b, int64_t R_cap,
+                                    hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
   s5::AppendArgs a;
-  a.k_new = k_new;
-  a.z_new = z_new;
-  a.new_stride_row = new_stride_row;
-  a.row_seq = row_seq;
-  a.row_pos = row_pos;
-  a.rows = rows;
-  a.k_ring = k_ring;
-  a.z_ring = z_ring;
-  a.B = B;
-  a.slots = ring_slots;
-  a.ring_stride_b = ring_stride_b;
-  a.ln_w = ln_w;
-  a.ln_b = ln_b;
-  a.eps = ln_eps;
-  a.rope = rope_cs;
-  a.rope_rows = rope_rows;
-  a.summary = summary;
-  a.ssb = s_stride_b;
-  a.R_cap = R_cap;
-  a.one_per_seq = (flags & STEP5_APPEND_ONE_PER_SEQ) != 0;
+  const int st = append_args(flags, k_new, z_new, new_stride_row, row_seq, row_pos, rows, k_ring,
+                             z_ring, B, ring_slots, ring_stride_b, ln_w, ln_b, ln_eps, rope_cs,
+                             rope_rows, summary, s_stride_b, R_cap, &a);
+  if (st || rows == 0) return st;
   return from_hip(s5::launch_append(a, stream));
 }
 
@@ -184,15 +197,15 @@ STEP5_EXPORT size_t step5_index_score_topk_workspace(const step5_geom* geom, int
   return score_ws(rows, R_cap).total;
 }
 
-STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, const void* q,
-                                        int64_t q_stride_row, const float* q_norm_w, float q_eps,
-                                        const void* rope_cs, int64_t rope_rows,
-                                        const float* w_head, int64_t w_stride_row,
-                                        const int32_t* row_seq, const int64_t* row_pos,
-                                        int32_t rows, const void* summary, int64_t B,
-                                        int64_t R_cap, int64_t s_stride_b, int32_t* sel_ids,
-                                        float* sel_scores, void* workspace, size_t ws_bytes,
-                                        hipStream_t stream) {
+// score_topk; with `ap`, the selection launch also runs that append (rows of
+// distinct sequences, checked by the caller).
+static int score_topk(const step5_geom* geom, uint32_t flags, const void* q, int64_t q_stride_row,
+                      const float* q_norm_w, float q_eps, const void* rope_cs, int64_t rope_rows,
+                      const float* w_head, int64_t w_stride_row, const int32_t* row_seq,
+                      const int64_t* row_pos, int32_t rows, const void* summary, int64_t B,
+                      int64_t R_cap, int64_t s_stride_b, int32_t* sel_ids, float* sel_scores,
+                      void* workspace, size_t ws_bytes, const s5::AppendArgs* ap,
+                      hipStream_t stream) {
   const int gs = check_geom(geom);
   if (gs) return gs;
   if (flags & ~STEP5_Q_E4M3) return STEP5_E_INVALID;
@@ -284,7 +297,43 @@ STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, 
   ta.arrivals = qa.arrivals;
   ta.sel_ids = sel_ids;
   ta.sel_scores = sel_scores;
+  ta.append = ap;
   return from_hip(s5::launch_topk(ta, stream));
+}
+
+STEP5_EXPORT int step5_index_score_topk(const step5_geom* geom, uint32_t flags, const void* q,
+                                        int64_t q_stride_row, const float* q_norm_w, float q_eps,
+                                        const void* rope_cs, int64_t rope_rows,
+                                        const float* w_head, int64_t w_stride_row,
+                                        const int32_t* row_seq, const int64_t* row_pos,
+                                        int32_t rows, const void* summary, int64_t B,
+                                        int64_t R_cap, int64_t s_stride_b, int32_t* sel_ids,
+                                        float* sel_scores, void* workspace, size_t ws_bytes,
+                                        hipStream_t stream) {
+  return score_topk(geom, flags, q, q_stride_row, q_norm_w, q_eps, rope_cs, rope_rows, w_head,
+                    w_stride_row, row_seq, row_pos, rows, summary, B, R_cap, s_stride_b, sel_ids,
+                    sel_scores, workspace, ws_bytes, nullptr, stream);
+}
+
+STEP5_EXPORT int step5_index_append_score_topk(
+    const step5_geom* geom, uint32_t flags, const step5_append_in* ap, const void* q,
+    int64_t q_stride_row, const float* q_norm_w, float q_eps, const void* rope_cs,
+    int64_t rope_rows, const float* w_head, int64_t w_stride_row, const int32_t* row_seq,
+    const int64_t* row_pos, int32_t rows, void* summary, int64_t B, int64_t R_cap,
+    int64_t s_stride_b, int32_t* sel_ids, float* sel_scores, void* workspace, size_t ws_bytes,
+    hipStream_t stream) {
+  const int gs = check_geom(geom);
+  if (gs) return gs;
+  if (!ap) return STEP5_E_INVALID;
+  s5::AppendArgs a;
+  int st = append_args(STEP5_APPEND_ONE_PER_SEQ, ap->k_new, ap->z_new, ap->new_stride_row, row_seq,
+                       row_pos, rows, ap->k_ring, ap->z_ring, B, ap->ring_slots,
+                       ap->ring_stride_b, ap->ln_w, ap->ln_b, ap->ln_eps, rope_cs, rope_rows,
+                       summary, s_stride_b, R_cap, &a);
+  if (st) return st;
+  return score_topk(geom, flags, q, q_stride_row, q_norm_w, q_eps, rope_cs, rope_rows, w_head,
+                    w_stride_row, row_seq, row_pos, rows, summary, B, R_cap, s_stride_b, sel_ids,
+                    sel_scores, workspace, ws_bytes, &a, stream);
 }
 
 STEP5_EXPORT size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows) {

@@ -25,6 +25,7 @@
 // produces are stored 8 B per lane, contiguous across the 32 lanes.
 #include "device.hpp"
 #include "launch.hpp"
+#include "region_block.hpp"
 
 namespace s5 {
 
@@ -147,132 +148,16 @@ __global__ __launch_bounds__(256) void summarize_kernel(
   }
 }
 
-// One region by one 256-thread workgroup, lane (t, g, c) = token t, group g,
-// dims 8c..8c+7, so the 8 tokens run side by side. The same arithmetic in the
-// same order as summarize_kernel: the max over tokens (order-free), each
-// token's k prep and e_t, e_t * k_t, then den and num summed in token order by
-// the lanes of token 0, from LDS. kt, zt: this lane's 8 dims of its token;
-// cs: its token's rope row; dst: the region's 8 output bytes of this lane
-// (written by the lanes of token 0). Every thread of the block must call it.
+// summarize_region_lanes for a 256-thread workgroup, LDS of its own
 __device__ inline void summarize_region_block(const uint16_t* __restrict__ kt,
                                               const uint16_t* __restrict__ zt,
                                               const uint16_t* __restrict__ cs,
                                               const float* __restrict__ lnw,
                                               const float* __restrict__ lnb, float eps,
                                               uint8_t* __restrict__ dst) {
-  __shared__ uint4 z_lds[8][32];          // [token][lane of the token]: z, 8 bf16
-  __shared__ float4 ep_lds[8][32][4];     // [token][lane]: e[0..7], e*k[0..7]
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int t = tid >> 5, sub = tid & 31;
-  const int c = sub & 7;
-  const uint4 zraw = ldg16(zt);
-  const uint4 kraw = ldg16(kt);
-  z_lds[t][sub] = zraw;
-  float gw[8], gb[8];
-  {
-    const float4 w0 = reinterpret_cast<const float4*>(lnw)[2 * c];
-    const float4 w1 = reinterpret_cast<const float4*>(lnw)[2 * c + 1];
-    const float4 b0 = reinterpret_cast<const float4*>(lnb)[2 * c];
-    const float4 b1 = reinterpret_cast<const float4*>(lnb)[2 * c + 1];
-    gw[0] = w0.x; gw[1] = w0.y; gw[2] = w0.z; gw[3] = w0.w;
-    gw[4] = w1.x; gw[5] = w1.y; gw[6] = w1.z; gw[7] = w1.w;
-    gb[0] = b0.x; gb[1] = b0.y; gb[2] = b0.z; gb[3] = b0.w;
-    gb[4] = b1.x; gb[5] = b1.y; gb[6] = b1.z; gb[7] = b1.w;
-  }
-  const bool rotated = c < 4;
-  const bool first_half = c < 2;
-  const int fi = (c & 1) * 8;
-  const uint32_t sflip = first_half ? 0x80000000u : 0u;
-
-  // k prep of this lane's token
-  float x[8], d[8], d2[8], y[8];
-  unpack_bf16x8(kraw, x);
-  const float mu = sum8_lanes(pair8(x), lane) / 64.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    d[i] = x[i] - mu;
-    d2[i] = d[i] * d[i];
-  }
-  const float var = sum8_lanes(pair8(d2), lane) / 64.0f;
-  const float r = 1.0f / sqrtf(var + eps);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float tt = (d[i] * r) * gw[i];
-    y[i] = tt + gb[i];
-  }
-  float cf[8], sf[8];
-  unpack_bf16x8(ldg16(cs + fi), cf);
-  unpack_bf16x8(ldg16(cs + 16 + fi), sf);
-  float rv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float sfs = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sf[i]) ^ sflip);
-    const float own_c = y[i] * cf[i];
-    const float oth_s = dpp<DPP_QUAD_XOR2>(y[i]) * sfs;
-    const float rot = own_c + oth_s;
-    rv[i] = rotated ? rot : y[i];
-  }
-  float kv[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t pk = bf16x2_hw(rv[2 * i], rv[2 * i + 1]);
-    kv[2 * i] = bf_lo(pk);
-    kv[2 * i + 1] = bf_hi(pk);
-  }
-  __syncthreads();
-  // the max of each dim over the region's tokens
-  float m[8], zf[8];
-  unpack_bf16x8(z_lds[0][sub], m);
-#pragma unroll
-  for (int s2 = 1; s2 < 8; ++s2) {
-    unpack_bf16x8(z_lds[s2][sub], zf);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], zf[i]);
-  }
-  unpack_bf16x8(zraw, zf);
-  float e[8], pr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    e[i] = exp_fixed(zf[i] - m[i]);
-    pr[i] = e[i] * kv[i];
-  }
-  ep_lds[t][sub][0] = make_float4(e[0], e[1], e[2], e[3]);
-  ep_lds[t][sub][1] = make_float4(e[4], e[5], e[6], e[7]);
-  ep_lds[t][sub][2] = make_float4(pr[0], pr[1], pr[2], pr[3]);
-  ep_lds[t][sub][3] = make_float4(pr[4], pr[5], pr[6], pr[7]);
-  __syncthreads();
-  if (t != 0) return;
-  float den[8], num[8];
-#pragma unroll
-  for (int s2 = 0; s2 < 8; ++s2) {
-    const float4 e0 = ep_lds[s2][sub][0], e1 = ep_lds[s2][sub][1];
-    const float4 p0 = ep_lds[s2][sub][2], p1 = ep_lds[s2][sub][3];
-    const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-    const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (s2 == 0) {
-        den[i] = ev[i];
-        num[i] = pv[i];
-      } else {
-        den[i] = den[i] + ev[i];
-        num[i] = num[i] + pv[i];
-      }
-    }
-  }
-  float sbv[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t pk = bf16x2_hw(num[2 * i] / den[2 * i], num[2 * i + 1] / den[2 * i + 1]);
-    sbv[2 * i] = bf_lo(pk);
-    sbv[2 * i + 1] = bf_hi(pk);
-  }
-  uint32_t lo = e4m3x2_hw<false>(sbv[0], sbv[1], 0u);
-  lo = e4m3x2_hw<true>(sbv[2], sbv[3], lo);
-  uint32_t hi = e4m3x2_hw<false>(sbv[4], sbv[5], 0u);
-  hi = e4m3x2_hw<true>(sbv[6], sbv[7], hi);
-  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  __shared__ uint4 z_lds[8][32];
+  __shared__ float4 ep_lds[8][32][4];
+  summarize_region_lanes(kt, zt, cs, lnw, lnb, eps, dst, (int)threadIdx.x, z_lds, ep_lds);
 }
 
 // Few regions (a decode step's own regions, a prefill chunk): one workgroup
@@ -299,11 +184,6 @@ __global__ __launch_bounds__(256) void summarize_small_kernel(
 // token of step 1, summarises the region each row's token completes, from
 // the ring (a region's 8 slots are contiguous: slots is a multiple of 8).
 // ---------------------------------------------------------------------------
-__device__ inline bool append_row_ok(int32_t s, int64_t p, int64_t B, int64_t rope_rows,
-                                     int64_t R_cap) {
-  return s >= 0 && s < B && p >= 0 && p < rope_rows && (p >> 3) < R_cap;
-}
-
 // one wave per row: lanes 0..31 copy the 512 B of k, lanes 32..63 those of z
 __global__ __launch_bounds__(256) void append_scatter_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ z_new, int64_t nsr,
@@ -365,48 +245,18 @@ hipError_t launch_summarize(const SummarizeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// One launch when no two rows share a sequence (a decode step): the block of
-// row r copies its token into the ring and, if the token ends a region,
-// summarises it with the region's other 7 tokens from the ring (earlier
-// calls wrote them; no block of this launch writes this sequence's ring) and
-// its own token straight from k_new/z_new.
-__global__ __launch_bounds__(256) void append_one_per_seq_kernel(
-    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ z_new, int64_t nsr,
-    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
-    uint16_t* __restrict__ k_ring, uint16_t* __restrict__ z_ring, int64_t B, int64_t slots,
-    int64_t rsb, const float* __restrict__ lnw, const float* __restrict__ lnb, float eps,
-    const uint16_t* __restrict__ rope, int64_t rope_rows, uint8_t* __restrict__ S, int64_t ssb,
-    int64_t R_cap) {
-  const int64_t r = blockIdx.x;
-  const int32_t s = row_seq[r];
-  const int64_t p = row_pos[r];
-  if (!append_row_ok(s, p, B, rope_rows, R_cap)) return;  // block-uniform
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int64_t e = (int64_t)(tid & 31) * 8;
-    const int64_t dst = (int64_t)s * rsb + (p % slots) * 256 + e;
-    if (tid < 32) *reinterpret_cast<uint4*>(k_ring + dst) = ldg16(k_new + r * nsr + e);
-    else *reinterpret_cast<uint4*>(z_ring + dst) = ldg16(z_new + r * nsr + e);
-  }
-  if ((p & 7) != 7) return;  // block-uniform
-  const int t = tid >> 5, sub = tid & 31;
-  const int g = sub >> 3, c = sub & 7;
-  const int64_t a = p - 7;
-  const int64_t io = (int64_t)g * 64 + c * 8;
-  const uint16_t* kt = t == 7 ? k_new + r * nsr + io : k_ring + (int64_t)s * rsb + ((a % slots) + t) * 256 + io;
-  const uint16_t* zt = t == 7 ? z_new + r * nsr + io : z_ring + (int64_t)s * rsb + ((a % slots) + t) * 256 + io;
-  summarize_region_block(kt, zt, rope + (a + t) * 32, lnw, lnb, eps,
-                         S + (int64_t)s * ssb + (p >> 3) * 256 + io);
+// One launch when no two rows share a sequence (a decode step): one
+// workgroup per row (append_row_block).
+__global__ __launch_bounds__(256) void append_one_per_seq_kernel(AppendArgs a) {
+  __shared__ uint4 z_lds[8][32];
+  __shared__ float4 ep_lds[8][32][4];
+  append_row_block(a, blockIdx.x, z_lds, ep_lds);
 }
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   if (a.rows <= 0) return hipSuccess;
   if (a.one_per_seq) {
-    hipLaunchKernelGGL(append_one_per_seq_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream,
-                       (const uint16_t*)a.k_new, (const uint16_t*)a.z_new, a.new_stride_row,
-                       a.row_seq, a.row_pos, (uint16_t*)a.k_ring, (uint16_t*)a.z_ring, a.B,
-                       a.slots, a.ring_stride_b, a.ln_w, a.ln_b, a.eps, (const uint16_t*)a.rope,
-                       a.rope_rows, (uint8_t*)a.summary, a.ssb, a.R_cap);
+    hipLaunchKernelGGL(append_one_per_seq_kernel, dim3((unsigned)a.rows), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(append_scatter_kernel, dim3((unsigned)((a.rows + 3) / 4)), dim3(256), 0,

@@ -44,6 +44,7 @@
 #include "exact.hpp"
 #include "interval.hpp"
 #include "launch.hpp"
+#include "region_block.hpp"
 
 namespace s5 {
 
@@ -560,10 +561,18 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
     int64_t w_stride, const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
     unsigned long long* __restrict__ partial, unsigned* __restrict__ arrivals,
-    int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores) {
+    int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores, int64_t nunits, AppendArgs ap) {
   constexpr bool EXACT = KIND == TK_EXACT;
   constexpr bool FUSED = KIND == TK_FUSED;
   extern __shared__ __align__(16) unsigned char smem[];
+  if ((int64_t)blockIdx.x >= nunits) {
+    // workgroups past the units: the cache append of one decode row each
+    // (first column of chunks only), on CUs the selection leaves idle
+    if (blockIdx.y == 0)
+      append_row_block(ap, (int64_t)blockIdx.x - nunits, reinterpret_cast<uint4(*)[32]>(smem),
+                       reinterpret_cast<float4(*)[32][4]>(smem + 8 * 32 * 16));
+    return;
+  }
   const int64_t unit = blockIdx.x;
   const int c = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -760,18 +769,29 @@ size_t topk_partial_bytes(int32_t rows, int64_t R_cap) {
   return (size_t)rows * 4 * p.nchunks * TK * sizeof(unsigned long long);
 }
 
+// the append's LDS (z and e, e*k of 8 tokens x 32 lanes) fits in every
+// selection launch's dynamic LDS
+static_assert(8 * 32 * 16 + 8 * 32 * 64 <= TK * 8 + 2 * TK_SORT * 8, "append LDS");
+
 hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;
   const unsigned units = (unsigned)a.rows * 4u;
+  AppendArgs ap{};
+  unsigned napp = 0;
+  if (a.append) {
+    ap = *a.append;
+    napp = (unsigned)ap.rows;
+  }
   if (a.fused) {
     const size_t sm = tk_smem_bytes(FUSED_MAX_N);
     hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel<TK_FUSED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_chunk_kernel<TK_FUSED>, dim3(units, 1), dim3(TK_THREADS), sm, stream,
-                       0, nullptr, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos, a.B,
-                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb,
-                       (int64_t)FUSED_MAX_N, 1, a.partial, a.arrivals, a.sel_ids, a.sel_scores);
+    hipLaunchKernelGGL(topk_chunk_kernel<TK_FUSED>, dim3(units + napp, 1), dim3(TK_THREADS), sm,
+                       stream, 0, nullptr, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos,
+                       a.B, a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb,
+                       (int64_t)FUSED_MAX_N, 1, a.partial, a.arrivals, a.sel_ids, a.sel_scores,
+                       (int64_t)units, ap);
     return hipGetLastError();
   }
   const TopkPlan p = topk_plan(a.rows, a.R_cap);
@@ -783,17 +803,19 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const int mode = p.nchunks == 1 ? 0 : 1;
-  const dim3 grid(units, (unsigned)p.nchunks);
+  const dim3 grid(units + napp, (unsigned)p.nchunks);
   if (a.exact)
     hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
-                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores);
+                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores, (int64_t)units,
+                       ap);
   else
     hipLaunchKernelGGL(topk_chunk_kernel<TK_INTERVAL>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
-                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores);
+                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores, (int64_t)units,
+                       ap);
   return hipGetLastError();
 }
 

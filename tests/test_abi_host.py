@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(s5):
     declared = set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(step5_\w+)\s*\(", text, re.M))
     assert {"step5_index_summarize", "step5_index_append", "step5_index_score_topk", "step5_sparse_attn",
             "step5_index_score_topk_workspace", "step5_sparse_attn_workspace",
-            "step5_qkv_index_project", "step5_status_str"} <= declared
+            "step5_qkv_index_project", "step5_status_str", "step5_index_append_score_topk"} <= declared
     nm = subprocess.run(["nm", "-D", "--defined-only", s5.LIB_PATH], capture_output=True,
                         text=True, check=True).stdout
     exported = set(re.findall(r" T (step5_\w+)$", nm, re.M))
@@ -213,6 +213,55 @@ def test_score_topk_rejections(s5, over, code):
     if over.get("flags") == 1 and "wsb" not in over:
         over["wsb"] = 0          # then the call stops at the workspace check
     assert _score(s5, **over) == code
+
+
+def _fused(s5, ap_over=None, **over):
+    """step5_index_append_score_topk with valid arguments but those in
+    `over` (score part) and `ap_over` (append part); ap_over=False passes no
+    append struct."""
+    g = geom(s5)
+    rows = over.pop("rows", 4)
+    R_cap = over.pop("R_cap", 64)
+    need = s5.lib().step5_index_score_topk_workspace(C.byref(g), rows, R_cap)
+    a = dict(flags=0, q=A, qs=1024, qw=A, eps=1e-6, rope=A, rope_rows=1024, w=A, ws_row=0,
+             seq=A, pos=A, summary=A, B=1, ssb=R_cap * 256, ids=A, scores=None, ws=A, wsb=need)
+    a.update(over)
+    ap = None
+    if ap_over is not False:
+        f = dict(k_new=A, z_new=A, new_stride_row=256, k_ring=A, z_ring=A, ring_slots=520,
+                 ring_stride_b=520 * 256, ln_w=A, ln_b=A, ln_eps=1e-6)
+        f.update(ap_over or {})
+        ap = C.byref(s5.Step5AppendIn(**f))
+    return s5.lib().step5_index_append_score_topk(
+        C.byref(g), a["flags"], ap, a["q"], a["qs"], a["qw"], a["eps"], a["rope"],
+        a["rope_rows"], a["w"], a["ws_row"], a["seq"], a["pos"], rows, a["summary"], a["B"],
+        R_cap, a["ssb"], a["ids"], a["scores"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("ap_over,over,code", [
+    (None, {"rows": 0}, OK),
+    (False, {}, E_INVALID),                                  # no append struct
+    ({"k_new": None}, {}, E_INVALID),
+    ({"ring_slots": 4}, {}, E_INVALID),
+    ({"new_stride_row": 200}, {}, E_INVALID),
+    ({"ln_eps": 0.0}, {}, E_INVALID),
+    (None, {"flags": 1, "rope": None, "qw": None}, E_INVALID),  # the append needs rope
+    (None, {"ids": None}, E_INVALID),
+    (None, {"rows": -1}, E_INVALID),
+    (None, {"R_cap": 524289}, E_UNSUPPORTED),
+    (None, {"ws": None}, E_WORKSPACE),
+    (None, {"wsb": 0}, E_WORKSPACE),
+])
+def test_append_score_topk_rejections(s5, ap_over, over, code):
+    assert _fused(s5, ap_over, **over) == code
+
+
+def test_append_score_topk_unsupported_geometry(s5):
+    g = geom(s5, head_dim=256)
+    f = s5.Step5AppendIn(A, A, 256, A, A, 520, 520 * 256, A, A, 1e-6)
+    assert s5.lib().step5_index_append_score_topk(
+        C.byref(g), 0, C.byref(f), A, 1024, A, 1e-6, A, 1024, A, 0, A, A, 4, A, 1, 64, 64 * 256,
+        A, None, A, 1 << 20, None) == E_UNSUPPORTED
 
 
 def test_score_topk_workspace_too_small(s5):

@@ -107,3 +107,27 @@ def test_fused_stream_equals_batch_summary():
     O = orc.summarize(P.host16(d["k_idx"]), P.host16(d["z_idx"]), 0, d["ln_w"].numpy(),
                       d["ln_b"].numpy(), P.EPS, P.host16(d["rope"]), R_cap=R_cap, summary=base)
     assert np.array_equal(S.cpu().numpy(), O)
+
+
+def test_fused_multi_chunk_selection():
+    """2 rows over 40,000 regions (320,000 tokens): the selection runs in 3
+    chunks per unit plus a merge by the last chunk to finish, and the append
+    workgroups sit beside every chunk column (only the first runs them)."""
+    rows, R_cap, slots = 2, 40000, 16
+    g = torch.Generator().manual_seed(77)
+    T = R_cap * 8
+    d = {"q_norm_w": (torch.randn(64, generator=g) * 0.1).to(DEV),
+         "ln_w": (torch.randn(64, generator=g) * 0.1 + 1).to(DEV),
+         "ln_b": (torch.randn(64, generator=g) * 0.1).to(DEV),
+         "w_head": torch.rand(16, generator=g).to(DEV),
+         "rope": torch.rand(T, 32, generator=g).to(torch.bfloat16).to(DEV)}
+    pos = torch.tensor([T - 1, T - 9 - 3], dtype=torch.int64, device=DEV)   # completes / not
+    seq = torch.arange(rows, dtype=torch.int32, device=DEV)
+    q = torch.randn(rows, 16, 64, generator=g).to(torch.bfloat16).to(DEV)
+    k_new = torch.randn(rows, 4, 64, generator=g).to(torch.bfloat16).to(DEV)
+    z_new = torch.randn(rows, 4, 64, generator=g).to(torch.bfloat16).to(DEV)
+    k_ring, z_ring, S = _state(rows, slots, R_cap, 78)
+    P.say(f"[case] fused append + score_topk, {rows} rows x {R_cap} regions (chunked selection)")
+    a, b = _both(d, k_new, z_new, q, seq, pos, k_ring, z_ring, S)
+    _equal(a, b, "multi-chunk")
+    assert not torch.equal(a[4], S)

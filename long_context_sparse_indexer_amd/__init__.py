@@ -283,11 +283,17 @@ def step5_index_append_score_topk(k_new: torch.Tensor, z_new: torch.Tensor, k_ri
                                   sel_scores: Optional[torch.Tensor] = None, *,
                                   rope: torch.Tensor, q_norm_w: Optional[torch.Tensor] = None,
                                   q_eps: float = 1e-6, q_is_e4m3: bool = False,
-                                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                                  workspace: Optional[torch.Tensor] = None, stream=None,
+                                  check_distinct: bool = False) -> None:
     """step5_index_append (rows of distinct sequences) and
     step5_index_score_topk of the same rows in one call: the appends run in
     extra workgroups of the selection's launch. The rows must not share a
-    sequence (not checked: device values)."""
+    sequence: the library cannot check it (device values); check_distinct
+    checks it here first (a host synchronisation, so not inside a HIP graph
+    capture) and raises ValueError when two rows name one sequence."""
+    if check_distinct:
+        _need(row_seq.dim() == 1 and int(torch.unique(row_seq).numel()) == row_seq.numel(),
+              "step5_index_append_score_topk: two rows share a sequence")
     summary = _append_checks(k_new, z_new, row_seq, row_pos, k_ring, z_ring, summary, rope)
     q, rows, summary, w_stride, B, R_cap, nbytes, workspace = _score_checks(
         q, w_head, row_seq, row_pos, summary, sel_ids, sel_scores, q_norm_w, rope, q_is_e4m3,

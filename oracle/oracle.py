@@ -43,6 +43,7 @@ def lib():
         L.o_f32_to_bf16_n.argtypes = [P, P, I64]
         L.o_bf16_to_e4m3_n.argtypes = [P, P, I64]
         L.o_exp_n.argtypes = [P, P, I64, C.c_int]
+        L.o_exp_bits_range.argtypes = [C.c_uint32, I64, P, C.c_int]
         L.o_k_prep_n.argtypes = [P, I64, P, P, F, P, P, P]
         L.o_q_prep_head.argtypes = [P, P, F, P, P]
         L.o_q_prep.restype = C.c_int
@@ -106,6 +107,14 @@ def exp(x, nthreads=None) -> np.ndarray:
     x = _c(x, np.float32)
     y = np.empty(x.shape, np.float32)
     lib().o_exp_n(_p(x), _p(y), x.size, nthreads or default_threads())
+    return y
+
+
+def exp_bits_range(start: int, n: int, nthreads=None) -> np.ndarray:
+    """exp of the n fp32 inputs with bit patterns start, start + 1, ..."""
+    assert 0 <= start and start + n <= 1 << 32
+    y = np.empty(n, np.float32)
+    lib().o_exp_bits_range(start, n, _p(y), nthreads or default_threads())
     return y
 
 

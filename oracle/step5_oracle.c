@@ -515,6 +515,17 @@ void o_exp_n(const float* x, float* y, int64_t n, int nthreads) {
 #pragma omp parallel for num_threads(nthreads) schedule(static)
   for (int64_t i = 0; i < n; ++i) y[i] = o_exp(x[i]);
 }
+/* exp of the n inputs whose fp32 bit patterns are start, start + 1, ...
+   (a sweep of a range of the domain without an input array) */
+void o_exp_bits_range(uint32_t start, int64_t n, float* y, int nthreads) {
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const uint32_t b = start + (uint32_t)i;
+    float x;
+    memcpy(&x, &b, sizeof x);
+    y[i] = o_exp(x);
+  }
+}
 /* k prep of n vectors of 64 dims, all at their own positions pos[i] */
 void o_k_prep_n(const uint16_t* x, int64_t n, const float* g, const float* b, float eps,
                 const uint16_t* rope, const int64_t* pos, float* out) {

@@ -49,3 +49,30 @@ extern "C" __attribute__((visibility("default"))) int device_check_e4m3(unsigned
   hipLaunchKernelGGL(check_e4m3_kernel, dim3(256), dim3(256), 0, 0, mismatches, first);
   return (int)hipDeviceSynchronize();
 }
+
+// exp_fixed (the summary's exp) on the inputs whose fp32 bit patterns are
+// start, start + 1, ..., start + n - 1 (out[i] for start + i)
+__global__ void exp_range_kernel(uint32_t start, uint32_t n, float* out) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = exp_fixed(__builtin_bit_cast(float, start + i));
+}
+// exp_fixed of n given inputs
+__global__ void exp_list_kernel(const float* in, float* out, uint32_t n) {
+  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  out[i] = exp_fixed(in[i]);
+}
+
+extern "C" __attribute__((visibility("default"))) int device_exp_range(uint32_t start, uint32_t n,
+                                                                       float* out) {
+  if (n == 0 || n > (1u << 30)) return -1;
+  hipLaunchKernelGGL(exp_range_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, start, n, out);
+  return (int)hipDeviceSynchronize();
+}
+extern "C" __attribute__((visibility("default"))) int device_exp_list(const float* in, float* out,
+                                                                      uint32_t n) {
+  if (n == 0 || n > (1u << 30)) return -1;
+  hipLaunchKernelGGL(exp_list_kernel, dim3((n + 255) / 256), dim3(256), 0, 0, in, out, n);
+  return (int)hipDeviceSynchronize();
+}

@@ -355,6 +355,26 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
         m.lib()
 
 
+def test_fused_call_rejects_rows_sharing_a_sequence(s5):
+    """check_distinct: two rows naming one sequence are rejected by the binding
+    before anything reaches the library (the library cannot see device
+    values); distinct rows pass the check and go on to the argument checks."""
+    import torch
+    rows = 3
+    bf = dict(dtype=torch.bfloat16)
+    k_new, z_new = torch.zeros(rows, 4, 64, **bf), torch.zeros(rows, 4, 64, **bf)
+    ring = torch.zeros(4, 16, 4, 64, **bf)
+    S = torch.zeros(4, 100, 4, 64, dtype=torch.uint8)
+    args = (k_new, z_new, ring, ring.clone(), torch.ones(64), torch.zeros(64), 1e-6,
+            torch.zeros(rows, 16, 64, **bf), torch.ones(16))
+    pos = torch.full((rows,), 40, dtype=torch.int64)
+    ids = torch.zeros(rows, 4, 512, dtype=torch.int32)
+    with pytest.raises(ValueError, match="share a sequence"):
+        s5.step5_index_append_score_topk(*args, torch.tensor([0, 2, 0], dtype=torch.int32), pos, S,
+                                         ids, rope=torch.zeros(800, 32, **bf),
+                                         q_norm_w=torch.zeros(64), check_distinct=True)
+
+
 # ---- fused projection --------------------------------------------------------
 
 def _proj(s5, widths=(2048, 512, 512, 1024, 256, 256, 16), **over):

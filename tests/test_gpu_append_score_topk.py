@@ -131,3 +131,34 @@ def test_fused_multi_chunk_selection():
     a, b = _both(d, k_new, z_new, q, seq, pos, k_ring, z_ring, S)
     _equal(a, b, "multi-chunk")
     assert not torch.equal(a[4], S)
+
+
+@pytest.mark.parametrize("rows,R_cap", [(72, 2000), (72, 5000), (66, 20000)])
+def test_fused_interval_selection_with_a_cut(rows, R_cap):
+    """More than 64 rows, so the selection works on score intervals with exact
+    rescoring, over more than 512 candidates per row so the threshold,
+    compaction and rescoring all run beside the append workgroups: 2,000
+    regions (intervals computed inside the selection), 5,000 (intervals
+    stored by the score pass, one chunk per unit) and 20,000 (stored
+    intervals, two chunks per unit and a merge)."""
+    slots = 16
+    g = torch.Generator().manual_seed(rows + R_cap)
+    T = R_cap * 8
+    d = {"q_norm_w": (torch.randn(64, generator=g) * 0.1).to(DEV),
+         "ln_w": (torch.randn(64, generator=g) * 0.1 + 1).to(DEV),
+         "ln_b": (torch.randn(64, generator=g) * 0.1).to(DEV),
+         "w_head": torch.rand(16, generator=g).to(DEV),
+         "rope": torch.rand(T, 32, generator=g).to(torch.bfloat16).to(DEV)}
+    pos = T - 1 - torch.randint(0, 8 * 300, (rows,), generator=g, dtype=torch.int64)
+    pos[::4] = pos[::4] | 7                 # these complete their region
+    seq = torch.randperm(rows, generator=g).to(torch.int32)
+    pos, seq = pos.to(DEV), seq.to(DEV)
+    q = torch.randn(rows, 16, 64, generator=g).to(torch.bfloat16).to(DEV)
+    k_new = torch.randn(rows, 4, 64, generator=g).to(torch.bfloat16).to(DEV)
+    z_new = torch.randn(rows, 4, 64, generator=g).to(torch.bfloat16).to(DEV)
+    k_ring, z_ring, S = _state(rows, slots, R_cap, rows * 7 + 1)
+    P.say(f"[case] fused append + score_topk (intervals), {rows} rows x {R_cap} regions")
+    a, b = _both(d, k_new, z_new, q, seq, pos, k_ring, z_ring, S)
+    _equal(a, b, f"rows={rows} R_cap={R_cap}")
+    assert not torch.equal(a[4], S)
+    assert bool((a[0][:, :, 511] >= 0).all()), "every unit selects 512"

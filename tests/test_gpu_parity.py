@@ -59,17 +59,15 @@ def test_summary_offsets_ragged_and_strided():
 
 
 def test_summary_full_size_decode16_ctx128k():
-    """The 16 x 131,072-token Student-t cache: the GPU summarises all of it;
-    two whole sequences are checked against the oracle."""
+    """The 16 x 131,072-token Student-t cache: the GPU summarises all of it,
+    and every sequence is checked against the oracle."""
     d = _case("decode16_ctx128k", 17, DEV, with_kv=False)
     S = P.gpu_summary(d)
     torch.cuda.synchronize()
-    for b in (0, 15):
-        O = P.oracle_summary({**d, "k_idx": d["k_idx"][b:b + 1], "z_idx": d["z_idx"][b:b + 1]})
-        got = S[b:b + 1].cpu().numpy()
-        mism = int((got != O).sum())
-        P.say(f"  seq {b}: {O.size} values, mismatches {mism}")
-        assert mism == 0
+    O = P.oracle_summary(d)
+    mism = int((S.cpu().numpy() != O).sum())
+    P.say(f"  16 sequences: {O.size} values, mismatches {mism}")
+    assert mism == 0
 
 
 def test_summary_fresh_span_1m_workload():
@@ -173,16 +171,6 @@ def test_select_prefill2048_ctx32k_sampled():
     assert int((S.cpu().numpy() != O).sum()) == 0
     rows = [0, 1, 2, 3, 7, 100, 511, 512, 1023, 1500, 2044, 2045, 2046, 2047]
     _select_check(d, S, O, rows)
-
-
-def test_select_decode16_ctx128k_sampled():
-    d = _case("decode16_ctx128k", 41, DEV, with_kv=False)
-    S = P.gpu_summary(d)
-    rows = [0, 9]
-    O = np.concatenate([P.oracle_summary({**d, "k_idx": d["k_idx"][b:b + 1],
-                                          "z_idx": d["z_idx"][b:b + 1]}) for b in rows])
-    assert np.array_equal(S[rows].cpu().numpy(), O)
-    _select_check(d, S, O, rows, seq_map={0: 0, 9: 1})
 
 
 def test_select_tie_heavy_1m_exact():
@@ -379,22 +367,6 @@ def test_attention_prefill2048_ctx32k_sampled():
                           ids.cpu().numpy()[rows], np.zeros(len(rows), np.int32),
                           d["row_pos"].cpu().numpy()[rows], P.SCALE)
     e = P.compare_attention(out[rows], lse[rows], oo, ol, "prefill")
-    P.say(f"  max abs err {e:.3g}")
-
-
-def test_attention_decode16_ctx128k_sampled():
-    d = _case("decode16_ctx128k", 17, DEV)
-    S = P.gpu_summary(d)
-    ids, _ = P.gpu_select(d, S)
-    out, lse = P.gpu_attn(d, ids)
-    torch.cuda.synchronize()
-    rows = [3, 12]
-    kh = np.concatenate([P.host16(d["k_cache"][b:b + 1]) for b in rows])
-    vh = np.concatenate([P.host16(d["v_cache"][b:b + 1]) for b in rows])
-    oo, ol = P.orc.attend(P.host16(d["q"])[rows], kh, vh, ids.cpu().numpy()[rows],
-                          np.arange(len(rows), dtype=np.int32), d["row_pos"].cpu().numpy()[rows],
-                          P.SCALE)
-    e = P.compare_attention(out[rows], lse[rows], oo, ol, "decode16_ctx128k")
     P.say(f"  max abs err {e:.3g}")
 
 

@@ -155,3 +155,13 @@ def test_exp_special_values_and_monotone(orc):
     y = orc.exp(x)
     assert np.all(np.diff(y) >= 0)
     assert orc.exp(np.array([-math.log(2)], np.float32))[0] == pytest.approx(0.5, rel=1.2e-7)
+
+
+def test_exp_bits_range_is_exp_of_those_inputs(orc):
+    """The range sweep helper (used to check the GPU's exp over whole ranges
+    of bit patterns) evaluates the same exp as exp() on an input array."""
+    for start, n in ((0x80000000, 5000), (0xC2AD0000, 70000), (0x3F800000 - 100, 300)):
+        x = np.arange(start, start + n, dtype=np.uint64).astype(np.uint32).view(np.float32)
+        want = orc.exp(x)
+        got = orc.exp_bits_range(start, n)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32))

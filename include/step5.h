@@ -302,6 +302,30 @@ int step5_sparse_attn(const step5_geom* geom, const void* q, int64_t q_stride_ro
 size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows);
 
 /*
+ * step5_sparse_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The same arguments, results and kernels as step5_sparse_attn,
+ * without the workspace arguments: the split states live in a device array
+ * of the library, 16 MiB (STEP5_SPARSE_ATTN_STATIC_BYTES) per GPU, held from
+ * the library's load until the process ends. The call allocates and frees
+ * nothing; its first call on a device looks the array's address up once.
+ * Calls whose step5_sparse_attn_workspace() exceeds the array return
+ * STEP5_E_WORKSPACE (no accepted geometry needs more than about 12.7 MB);
+ * a stream that belongs to another device than the current one returns
+ * STEP5_E_INVALID. Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (different streams, or different host threads) race
+ * and must be ordered by the caller. Nothing in the array needs to start
+ * at any value.
+ */
+#define STEP5_SPARSE_ATTN_STATIC_BYTES ((size_t)16 << 20)
+int step5_sparse_attn_noalloc(const step5_geom* geom, const void* q, int64_t q_stride_row,
+                              const void* k_cache, const void* v_cache, int64_t B,
+                              int64_t kv_stride_b, int64_t kv_stride_t, int64_t T_cap,
+                              const int32_t* sel_ids, const int32_t* row_seq,
+                              const int64_t* row_pos, int32_t rows, float softmax_scale,
+                              void* out, float* out_lse, hipStream_t stream);
+
+/*
  * The fused projection of a full-attention layer: one product of the normed
  * hidden state with a weight whose rows are the attention's q, k, v and the
  * indexer's q, k, z and gate rows, written straight into seven outputs.

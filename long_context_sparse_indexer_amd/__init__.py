@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "Step5Error", "GEOM", "lib", "step5_status_str", "step5_index_summarize",
     "step5_index_append", "step5_index_score_topk", "step5_index_score_topk_workspace", "step5_sparse_attn",
-    "step5_sparse_attn_workspace", "attn_geom", "STEP5_Q_E4M3", "STEP5_APPEND_ONE_PER_SEQ",
+    "step5_sparse_attn_workspace", "step5_sparse_attn_noalloc", "attn_geom", "STEP5_Q_E4M3", "STEP5_APPEND_ONE_PER_SEQ",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libstep5.so")
@@ -87,6 +87,9 @@ def lib():
         L.step5_sparse_attn.restype = C.c_int
         L.step5_sparse_attn.argtypes = [G, P, I64, P, P, I64, I64, I64, I64, P, P, P, I32, F, P,
                                         P, P, SZ, P]
+        L.step5_sparse_attn_noalloc.restype = C.c_int
+        L.step5_sparse_attn_noalloc.argtypes = [G, P, I64, P, P, I64, I64, I64, I64, P, P, P, I32,
+                                                F, P, P, P]
         L.step5_sparse_attn_workspace.restype = SZ
         L.step5_sparse_attn_workspace.argtypes = [G, I32]
         L.step5_qkv_index_project.restype = C.c_int
@@ -309,14 +312,7 @@ def step5_index_append_score_topk(k_new: torch.Tensor, z_new: torch.Tensor, k_ri
     _check("step5_index_append_score_topk", st)
 
 
-def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
-                      sel_ids: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor,
-                      softmax_scale: float, out: torch.Tensor,
-                      out_lse: Optional[torch.Tensor] = None, *,
-                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Attention over selected regions plus the own region into out (bf16 [rows, Hq, D]).
-    The geometry comes from q: Hq query heads (16, 32 or 64: 4, 8 or 16 per KV
-    head) of D = 128 or 192 dims; k_cache, v_cache bf16 [B, T, 4, D]."""
+def _attn_checks(q, k_cache, v_cache, sel_ids, row_seq, row_pos, out, out_lse):
     rows = q.shape[0]
     _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.stride(2) == 1 and
           q.stride(1) == q.shape[2], "q must be bf16 [rows, Hq, D] with contiguous heads")
@@ -334,7 +330,18 @@ def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _need(out_lse.dtype == torch.float32 and tuple(out_lse.shape) == (rows, Hq) and
               out_lse.is_contiguous(), "out_lse must be fp32 [rows, Hq]")
     _need(row_seq.dtype == torch.int32 and row_pos.dtype == torch.int64, "row_seq int32, row_pos int64")
-    geom = attn_geom(Hq, D)
+    return rows, attn_geom(Hq, D)
+
+
+def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      sel_ids: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor,
+                      softmax_scale: float, out: torch.Tensor,
+                      out_lse: Optional[torch.Tensor] = None, *,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Attention over selected regions plus the own region into out (bf16 [rows, Hq, D]).
+    The geometry comes from q: Hq query heads (16, 32 or 64: 4, 8 or 16 per KV
+    head) of D = 128 or 192 dims; k_cache, v_cache bf16 [B, T, 4, D]."""
+    rows, geom = _attn_checks(q, k_cache, v_cache, sel_ids, row_seq, row_pos, out, out_lse)
     nbytes = int(lib().step5_sparse_attn_workspace(C.byref(geom), int(rows)))
     workspace = _workspace(nbytes, q.device, workspace)
     st = lib().step5_sparse_attn(
@@ -343,6 +350,21 @@ def step5_sparse_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _ptr(row_pos), rows, float(softmax_scale), _ptr(out), _ptr(out_lse), _ptr(workspace),
         nbytes, _stream(stream))
     _check("step5_sparse_attn", st)
+
+
+def step5_sparse_attn_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              sel_ids: torch.Tensor, row_seq: torch.Tensor, row_pos: torch.Tensor,
+                              softmax_scale: float, out: torch.Tensor,
+                              out_lse: Optional[torch.Tensor] = None, *, stream=None) -> None:
+    """step5_sparse_attn without a workspace: the library's static device
+    scratch holds the split states (no allocation, for graph capture and
+    serving loops). Calls that overlap on one GPU share that scratch."""
+    rows, geom = _attn_checks(q, k_cache, v_cache, sel_ids, row_seq, row_pos, out, out_lse)
+    st = lib().step5_sparse_attn_noalloc(
+        C.byref(geom), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+        k_cache.stride(0), k_cache.stride(1), k_cache.shape[1], _ptr(sel_ids), _ptr(row_seq),
+        _ptr(row_pos), rows, float(softmax_scale), _ptr(out), _ptr(out_lse), _stream(stream))
+    _check("step5_sparse_attn_noalloc", st)
 
 
 def proj_widths(gate_size: int = Q_HEADS, q_heads: int = Q_HEADS, head_dim: int = HEAD_DIM):

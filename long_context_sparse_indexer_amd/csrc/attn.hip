@@ -24,9 +24,12 @@
 //    loads (16 lanes cover a 256-byte row) and P from LDS.
 // Decode units are few (rows x 4), so they get many splits to spread the
 // gather over the GPU; prefill units are many and run unsplit.
+#include <atomic>
+
 #include "attn_tile.hpp"
 #include "device.hpp"
 #include "launch.hpp"
+#include "step5.h"
 
 namespace s5 {
 
@@ -361,6 +364,40 @@ size_t attn_workspace_bytes(int32_t rows) {
 #ifndef S5_ATTN_TILE_MAX_REGIONS
 #define S5_ATTN_TILE_MAX_REGIONS 5120
 #endif
+
+// Scratch of step5_sparse_attn_noalloc (callers that cannot allocate): the
+// split states of one call. Every GPU the library runs on holds its own copy
+// of the array until the process ends; host code never passes the array's
+// name to a kernel (on the host it is a stand-in, not a device address), only
+// the address hipGetSymbolAddress gives on each device, kept per device.
+// The split states are written in full before the merge reads them, so
+// nothing in it needs clearing; calls that overlap on one GPU race on it.
+__device__ __align__(256) unsigned char scratch[kAttnStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+int attn_static_scratch(hipStream_t stream, void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return STEP5_E_HIP;
+  if (dev >= kMaxDevices) return STEP5_E_UNSUPPORTED;
+  if (stream) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return STEP5_E_HIP;
+    if (sd != dev) return STEP5_E_INVALID;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return STEP5_E_HIP;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  *ptr = p;
+  return STEP5_OK;
+}
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   if (a.rows == 0) return hipSuccess;

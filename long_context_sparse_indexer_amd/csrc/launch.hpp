@@ -164,6 +164,13 @@ struct AttnArgs {
 };
 // qpk 4, head dim 128: attn_kernel (attn.hip); the rest: attn_mh_kernel (attn_mh.hip)
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+// The split-state scratch of step5_sparse_attn_noalloc: a file-scope device
+// array of kAttnStaticScratchBytes (attn.hip). attn_static_scratch gives its
+// address on the stream's device (which must be the current device; else
+// STEP5_E_INVALID), looked up once per device; STEP5_E_HIP if the lookup
+// fails.
+constexpr size_t kAttnStaticScratchBytes = (size_t)16 << 20;
+int attn_static_scratch(hipStream_t stream, void** ptr);
 hipError_t launch_attn_mh(const AttnArgs& a, hipStream_t stream);
 // the context sweep over tiles of 32 rows for contexts below maxr regions
 // (attn_tile.hip); tiles it does not take are left to attn_kernel

@@ -69,6 +69,9 @@ ScoreWs score_ws(int32_t rows, int64_t R_cap) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? STEP5_OK : STEP5_E_HIP; }
 
+static_assert(s5::kAttnStaticScratchBytes == STEP5_SPARSE_ATTN_STATIC_BYTES,
+              "the static attention scratch is the size the header states");
+
 }  // namespace
 
 STEP5_EXPORT const char* step5_status_str(int status) {
@@ -345,13 +348,13 @@ STEP5_EXPORT size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t 
   return b ? up(b) : 0;
 }
 
-STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_t q_stride_row,
-                                   const void* k_cache, const void* v_cache, int64_t B,
-                                   int64_t kv_stride_b, int64_t kv_stride_t, int64_t T_cap,
-                                   const int32_t* sel_ids, const int32_t* row_seq,
-                                   const int64_t* row_pos, int32_t rows, float softmax_scale,
-                                   void* out, float* out_lse, void* workspace, size_t ws_bytes,
-                                   hipStream_t stream) {
+// Checks the arguments of a sparse-attention call (all but the workspace) and
+// fills its launch arguments.
+static int attn_args(const step5_geom* geom, const void* q, int64_t q_stride_row,
+                     const void* k_cache, const void* v_cache, int64_t B, int64_t kv_stride_b,
+                     int64_t kv_stride_t, int64_t T_cap, const int32_t* sel_ids,
+                     const int32_t* row_seq, const int64_t* row_pos, int32_t rows,
+                     float softmax_scale, void* out, float* out_lse, s5::AttnArgs* a) {
   const int gs = check_geom(geom);
   if (gs) return gs;
   if (rows < 0) return STEP5_E_INVALID;
@@ -369,29 +372,65 @@ STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_
   if (!row_seq || !row_pos || !aligned(row_seq, 4) || !aligned(row_pos, 8)) return STEP5_E_INVALID;
   if (!std::isfinite(softmax_scale) || !(softmax_scale > 0.0f)) return STEP5_E_INVALID;
   if (!out || !aligned(out, 16) || (out_lse && !aligned(out_lse, 4))) return STEP5_E_INVALID;
+  a->q = q;
+  a->q_stride_row = q_stride_row;
+  a->k = k_cache;
+  a->v = v_cache;
+  a->B = B;
+  a->kv_sb = kv_stride_b;
+  a->kv_st = kv_stride_t;
+  a->T_cap = T_cap;
+  a->sel = sel_ids;
+  a->row_seq = row_seq;
+  a->row_pos = row_pos;
+  a->rows = rows;
+  a->qpk = geom->q_heads / geom->kv_heads;
+  a->head_dim = geom->head_dim;
+  a->scale = softmax_scale;
+  a->out = out;
+  a->lse = out_lse;
+  a->partial = nullptr;
+  return STEP5_OK;
+}
+
+STEP5_EXPORT int step5_sparse_attn(const step5_geom* geom, const void* q, int64_t q_stride_row,
+                                   const void* k_cache, const void* v_cache, int64_t B,
+                                   int64_t kv_stride_b, int64_t kv_stride_t, int64_t T_cap,
+                                   const int32_t* sel_ids, const int32_t* row_seq,
+                                   const int64_t* row_pos, int32_t rows, float softmax_scale,
+                                   void* out, float* out_lse, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  s5::AttnArgs a;
+  const int st = attn_args(geom, q, q_stride_row, k_cache, v_cache, B, kv_stride_b, kv_stride_t,
+                           T_cap, sel_ids, row_seq, row_pos, rows, softmax_scale, out, out_lse, &a);
+  if (st || rows == 0) return st;
   const size_t need = step5_sparse_attn_workspace(geom, rows);
   if (ws_bytes < need || (need && (!workspace || !aligned(workspace, kAlign))))
     return STEP5_E_WORKSPACE;
-
-  s5::AttnArgs a;
-  a.q = q;
-  a.q_stride_row = q_stride_row;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.B = B;
-  a.kv_sb = kv_stride_b;
-  a.kv_st = kv_stride_t;
-  a.T_cap = T_cap;
-  a.sel = sel_ids;
-  a.row_seq = row_seq;
-  a.row_pos = row_pos;
-  a.rows = rows;
-  a.qpk = geom->q_heads / geom->kv_heads;
-  a.head_dim = geom->head_dim;
-  a.scale = softmax_scale;
-  a.out = out;
-  a.lse = out_lse;
   a.partial = static_cast<float*>(workspace);
+  return from_hip(s5::launch_attn(a, stream));
+}
+
+STEP5_EXPORT int step5_sparse_attn_noalloc(const step5_geom* geom, const void* q,
+                                           int64_t q_stride_row, const void* k_cache,
+                                           const void* v_cache, int64_t B, int64_t kv_stride_b,
+                                           int64_t kv_stride_t, int64_t T_cap,
+                                           const int32_t* sel_ids, const int32_t* row_seq,
+                                           const int64_t* row_pos, int32_t rows,
+                                           float softmax_scale, void* out, float* out_lse,
+                                           hipStream_t stream) {
+  s5::AttnArgs a;
+  const int st = attn_args(geom, q, q_stride_row, k_cache, v_cache, B, kv_stride_b, kv_stride_t,
+                           T_cap, sel_ids, row_seq, row_pos, rows, softmax_scale, out, out_lse, &a);
+  if (st || rows == 0) return st;
+  const size_t need = step5_sparse_attn_workspace(geom, rows);
+  if (need > s5::kAttnStaticScratchBytes) return STEP5_E_WORKSPACE;
+  if (need) {
+    void* scratch = nullptr;
+    const int sst = s5::attn_static_scratch(stream, &scratch);
+    if (sst) return sst;
+    a.partial = static_cast<float*>(scratch);
+  }
   return from_hip(s5::launch_attn(a, stream));
 }
 

@@ -329,6 +329,42 @@ def test_sparse_attn_rejections(s5, over, code):
     assert _attn(s5, **over) == code
 
 
+@pytest.mark.parametrize("over,code", [
+    ({"rows": 0}, OK),
+    ({"rows": -3}, E_INVALID),
+    ({"q": None}, E_INVALID),
+    ({"qs": 2040}, E_INVALID),
+    ({"k": A + 2}, E_INVALID),
+    ({"T": 0}, E_INVALID),
+    ({"sel": None}, E_INVALID),
+    ({"scale": float("nan")}, E_INVALID),
+    ({"out": None}, E_INVALID),
+])
+def test_sparse_attn_noalloc_rejections(s5, over, code):
+    """The allocation-free attention call checks the same arguments before any
+    HIP call (here, with no GPU, a call that passed them would fail later)."""
+    g = over.pop("g", geom(s5))
+    rows = over.pop("rows", 16)
+    a = dict(q=A, qs=2048, k=A, v=A, B=16, kvb=4096 * 512, kvt=512, T=4096, sel=A, seq=A, pos=A,
+             scale=0.088, out=A, lse=None)
+    a.update(over)
+    assert s5.lib().step5_sparse_attn_noalloc(
+        C.byref(g), a["q"], a["qs"], a["k"], a["v"], a["B"], a["kvb"], a["kvt"], a["T"], a["sel"],
+        a["seq"], a["pos"], rows, a["scale"], a["out"], a["lse"], None) == code
+
+
+def test_sparse_attn_static_scratch_covers_every_geometry(s5):
+    """The static scratch (16 MiB) holds the split states of every accepted
+    geometry at every row count."""
+    L = s5.lib()
+    worst = 0
+    for hq, hd in ((16, 128), (32, 128), (64, 128), (16, 192), (32, 192), (64, 192)):
+        g = geom(s5, q_heads=hq, head_dim=hd)
+        for rows in list(range(1, 300)) + [1000, 4096, 65536]:
+            worst = max(worst, L.step5_sparse_attn_workspace(C.byref(g), rows))
+    assert 0 < worst <= 16 << 20
+
+
 def test_sparse_attn_geometry_strides_and_workspace(s5):
     """16 query heads per KV head of 192 dims: q rows need 64 x 192 elements,
     K/V token rows 4 x 192, and the split states grow with the heads and dims."""

@@ -181,7 +181,7 @@ def event_time_us(torch, fn, reps):
 def workspaces(torch, s5, rows, R_cap, dev):
     ws1 = torch.empty(s5.step5_index_score_topk_workspace(rows, R_cap) + 256, dtype=torch.uint8,
                       device=dev)
-    ws2 = torch.empty(max(1, s5.step5_sparse_attn_workspace(rows)) + 256, dtype=torch.uint8,
+    ws2 = torch.zeros(max(1, s5.step5_sparse_attn_workspace(rows)) + 256, dtype=torch.uint8,
                       device=dev)
     return ws1[(-ws1.data_ptr()) % 256:], ws2[(-ws2.data_ptr()) % 256:]
 
@@ -474,7 +474,7 @@ def attn_geometry(torch, s5):
             out = torch.empty((rows, Hq, D), dtype=torch.bfloat16, device=dev)
             lse = torch.empty((rows, Hq), dtype=torch.float32, device=dev)
             nb = s5.step5_sparse_attn_workspace(rows, Hq, D)
-            ws = torch.empty(max(1, nb) + 256, dtype=torch.uint8, device=dev)
+            ws = torch.zeros(max(1, nb) + 256, dtype=torch.uint8, device=dev)
             ws = ws[(-ws.data_ptr()) % 256:]
             layers = [[("attn", (lambda ids=ids: s5.step5_sparse_attn(
                 q, k, v, ids, seq, pos, 1.0 / math.sqrt(D), out, lse, workspace=ws)))]

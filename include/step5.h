@@ -286,7 +286,11 @@ int step5_index_append_score_topk(const step5_geom* geom, uint32_t flags,
  * out_lse     out, nullable: fp32 [rows, q_heads]: natural-log sum of
  *             exp(scale * q.k) over the row's tokens.
  * workspace   device scratch of at least step5_sparse_attn_workspace() bytes,
- *             256-byte aligned (may be null when that is 0).
+ *             256-byte aligned (may be null when that is 0). It must be all
+ *             zero before its first use by this call (it holds arrival
+ *             counters as well as split states); every call leaves the
+ *             counters zero again, so a workspace zeroed once can be reused by
+ *             any number of calls, one at a time.
  * Query head h reads KV head h / (q_heads / kv_heads).
  * rows == 0 is a successful no-op.
  */
@@ -309,13 +313,14 @@ size_t step5_sparse_attn_workspace(const step5_geom* geom, int32_t rows);
  * of the library, 16 MiB (STEP5_SPARSE_ATTN_STATIC_BYTES) per GPU, held from
  * the library's load until the process ends. The call allocates and frees
  * nothing; its first call on a device looks the array's address up once.
- * Calls whose step5_sparse_attn_workspace() exceeds the array return
+ * The array starts zero and every call leaves its counters zero. Calls
+ * whose step5_sparse_attn_workspace() exceeds the array return
  * STEP5_E_WORKSPACE (no accepted geometry needs more than about 12.7 MB);
  * a stream that belongs to another device than the current one returns
  * STEP5_E_INVALID. Every call on one GPU uses the same array: calls that
  * overlap on one GPU (different streams, or different host threads) race
  * and must be ordered by the caller. Nothing in the array needs to start
- * at any value.
+ * at any other value.
  */
 #define STEP5_SPARSE_ATTN_STATIC_BYTES ((size_t)16 << 20)
 int step5_sparse_attn_noalloc(const step5_geom* geom, const void* q, int64_t q_stride_row,

@@ -217,7 +217,8 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
     if nbytes == 0:
         return workspace
     if workspace is None:
-        workspace = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+        # zero-filled: the attention workspace's arrival counters start at zero
+        workspace = torch.zeros(nbytes + 256, dtype=torch.uint8, device=device)
         off = (-workspace.data_ptr()) % 256
         workspace = workspace[off:off + nbytes]
     _need(workspace.numel() >= nbytes, f"workspace needs {nbytes} bytes")

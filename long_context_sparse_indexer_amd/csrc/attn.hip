@@ -8,9 +8,11 @@
 // region first, then the 512 selected regions) is cut into splits of
 // `per_split` entries, one 256-thread workgroup each; inside a workgroup the
 // four waves take 4-entry chunks (32 tokens) in turn; wave states merge in
-// wave order, split states merge in split order (attn_mh_merge_kernel, one
-// workgroup per (unit, head)). Results are therefore independent of
-// scheduling.
+// wave order, split states merge in split order, by the unit's last split to
+// finish (an arrival counter per unit in the workspace; the split states are
+// written and read through device-coherent memory, so no cache write-back is
+// needed between workgroups on different dies). Results are therefore
+// independent of scheduling.
 //
 // Per 32-token chunk, per wave:
 //  - QK^T with the 16x16x32 bf16 MFMA: A = the unit's 4 query heads (MFMA
@@ -159,8 +161,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
     const uint16_t* __restrict__ vc, int64_t B, int64_t kv_sb, int64_t kv_st, int64_t T_cap,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ row_seq,
     const int64_t* __restrict__ row_pos, int32_t rows, int32_t sweep_maxr, float scale_log2,
-    int per_split, int nsplit, float* __restrict__ partial, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    int per_split, int nsplit, float* __restrict__ partial, unsigned* __restrict__ arrive,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ float4 p_lds[4][32];            // per wave: P of 32 tokens, 4 heads each
   __shared__ float o_lds[4][4][4][128];      // [wave][token slot][head][dim]
   __shared__ float ml_lds[4][2][4];          // [wave][m | l][head]
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     if (tl_tile_taken(row / TL_ROWS * TL_ROWS, rows, row_seq, row_pos, B, T_cap, sweep_maxr, &sq))
       return;
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, qd = lane >> 4;
 
   const int32_t seq = row_seq[row];
@@ -314,13 +316,47 @@ __global__ __launch_bounds__(256) void attn_kernel(
     O1 = O1 + f * s1;
   }
   if (nsplit > 1) {
+    // This split's state, stored with device-scope (write-through) stores and
+    // waited for; then one arrival per split at the unit's counter. The last
+    // split to arrive resets the counter (so the workspace is left as found)
+    // and merges every split's state, read with device-scope loads, in split
+    // order, as a merge kernel would.
+    __shared__ int sh_last;
     float* dst = partial + ((unit * nsplit + split) * 4 + r) * AT_PART;
     if (d0 == 0) {
-      dst[0] = M;
-      dst[1] = L;
+      __hip_atomic_store(dst, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    *reinterpret_cast<float2*>(dst + 2 + d0) = make_float2(O0, O1);
-    return;
+    __hip_atomic_store(dst + 2 + d0, O0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 3 + d0, O1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const unsigned old = __hip_atomic_fetch_add(&arrive[unit], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+      const bool last = old == (unsigned)nsplit - 1u;
+      if (last) __hip_atomic_store(&arrive[unit], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sh_last = last;
+    }
+    __syncthreads();
+    if (!sh_last) return;
+    const float* st = partial + (unit * nsplit * 4 + r) * AT_PART;
+    const int64_t sstride = 4 * AT_PART;  // between a head's states of consecutive splits
+    M = -INFINITY;
+    for (int sp = 0; sp < nsplit; ++sp)
+      M = fmaxf(M, __hip_atomic_load(st + sp * sstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    Mu = (M == -INFINITY) ? 0.f : M;
+    L = 0.f;
+    O0 = 0.f;
+    O1 = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float* ss = st + sp * sstride;
+      const float f = __builtin_amdgcn_exp2f(
+          __hip_atomic_load(ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mu);
+      L = L + f * __hip_atomic_load(ss + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      O0 = O0 + f * __hip_atomic_load(ss + 2 + d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      O1 = O1 + f * __hip_atomic_load(ss + 3 + d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const uint32_t packed = bf16_bits(O0 * inv) | (bf16_bits(O1 * inv) << 16);
@@ -336,6 +372,8 @@ __global__ __launch_bounds__(256) void attn_kernel(
 #endif
 AttnPlan attn_plan(int32_t rows) {
   const int64_t units = (int64_t)rows * 4;
+  // more than one split only for fewer than S5_ATTN_BLOCKS units (the
+  // workspace's counter region depends on it)
   int64_t ns = units > 0 ? (S5_ATTN_BLOCKS + units - 1) / units : 1;
   int64_t per = (AT_ENTRIES + ns - 1) / ns;
   per = (per + 15) / 16 * 16;
@@ -346,10 +384,16 @@ AttnPlan attn_plan(int32_t rows) {
   return a;
 }
 
+// Workspace of a split call: one arrival counter per unit in a region of
+// fixed size at the start (units are split only while there are fewer than
+// S5_ATTN_BLOCKS of them, so the counters of every split call lie in it and
+// no call's split states ever overlap them), then the split states.
+constexpr size_t AT_COUNTER_BYTES = ((size_t)S5_ATTN_BLOCKS * sizeof(unsigned) + 255) / 256 * 256;
+
 size_t attn_workspace_bytes(int32_t rows) {
   const AttnPlan a = attn_plan(rows);
   if (a.nsplit <= 1) return 0;
-  return (size_t)rows * 4 * a.nsplit * 4 * AT_PART * sizeof(float);
+  return AT_COUNTER_BYTES + (size_t)rows * 4 * a.nsplit * 4 * AT_PART * sizeof(float);
 }
 
 // Many rows (a prompt chunk) go to the context sweep, tile by tile, when the
@@ -416,15 +460,18 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   }
   const unsigned units = (unsigned)a.rows * 4u;
   const float scale_log2 = (float)((double)a.scale * 1.4426950408889634);
+  unsigned* arrive = nullptr;
+  float* states = nullptr;
+  if (pl.nsplit > 1) {
+    arrive = reinterpret_cast<unsigned*>(a.partial);
+    states = reinterpret_cast<float*>(reinterpret_cast<char*>(a.partial) + AT_COUNTER_BYTES);
+  }
   hipLaunchKernelGGL(attn_kernel, dim3(units, (unsigned)pl.nsplit), dim3(256), 0, stream,
                      (const uint16_t*)a.q, a.q_stride_row, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.B, a.kv_sb, a.kv_st, a.T_cap, a.sel, a.row_seq,
-                     a.row_pos, a.rows, maxr, scale_log2, pl.per_split, pl.nsplit, a.partial,
-                     (uint16_t*)a.out, a.lse);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.nsplit == 1) return e;
-  // the split states are laid out as attn_mh.hip's, 4 heads x 128 dims
-  return launch_attn_merge(a.partial, pl.nsplit, a.rows, 4, 128, a.out, a.lse, stream);
+                     a.row_pos, a.rows, maxr, scale_log2, pl.per_split, pl.nsplit, states,
+                     arrive, (uint16_t*)a.out, a.lse);
+  return hipGetLastError();
 }
 
 }  // namespace s5

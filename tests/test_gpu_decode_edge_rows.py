@@ -1,0 +1,78 @@
+"""GPU parity of the decode selection at shapes the workload tests do not
+reach: up to 64 rows over 5,000 and 16,384 regions, e4m3 query and summaries
+drawn directly. Ids and scores must equal the oracle's bit for bit (no
+near-tie excusal).
+
+Cases: rows with 0, 1, 511, 512, 513, 1,023, 1,024, 1,025 candidates and the
+full range, invalid rows (no sequence, a sequence past the batch, a position
+past the summary), every finite e4m3 code at random, and tie-heavy codes
+from {+-1/4 .. +-2} (many exact ties around the 512th score).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+import parity as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _draw(kind, g):
+    if kind == "random":
+        def draw(shape):
+            c = torch.randint(0, 0x7F, shape, generator=g, dtype=torch.int32)   # 0x7F is NaN
+            return (c | (torch.randint(0, 2, shape, generator=g, dtype=torch.int32) << 7)).to(torch.uint8)
+        return draw, torch.rand(16, generator=g)
+    tie = torch.tensor(W.TIE_CODES, dtype=torch.uint8)
+    return (lambda shape: tie[torch.randint(0, 8, shape, generator=g)],
+            torch.arange(1, 17, dtype=torch.float32) / 16)
+
+
+@pytest.mark.parametrize("kind", ["random", "tie_heavy"])
+def test_decode_select_edge_rows(kind):
+    B, R = 12, 5000
+    g = torch.Generator().manual_seed(7 if kind == "random" else 8)
+    draw, w = _draw(kind, g)
+    ncands = [0, 1, 511, 512, 513, 1023, 1024, 1025, 2777, 4999, 4999, 4999]
+    pos = [8 * c + (3 * i) % 8 for i, c in enumerate(ncands)]
+    seq = list(range(B))
+    # invalid rows: no sequence, a sequence past the batch, a position past the summary
+    seq += [-1, B, 3]
+    pos += [8 * 4000, 8 * 4000, 8 * R + 8]
+    rows = len(seq)
+    d = {"rows": rows, "q8": draw((rows, 16, 64)).to(DEV), "w_head": w.to(DEV),
+         "row_seq": torch.tensor(seq, dtype=torch.int32, device=DEV),
+         "row_pos": torch.tensor(pos, dtype=torch.int64, device=DEV)}
+    S = draw((B, R, 4, 64)).to(DEV)
+    P.say(f"[case] decode select {kind}: {rows} rows over {R} regions")
+    ids, sc = P.gpu_select(d, S)
+    torch.cuda.synchronize()
+    ids_h, sc_h = ids.cpu().numpy(), sc.cpu().numpy()
+    good = list(range(B))
+    osc = P.oracle_scores(d, P.host8(S), good)
+    ex = P.compare_selection(ids_h[good], sc_h[good], osc, np.array(pos)[good], exact=True)
+    assert ex == 0
+    for bad in range(B, rows):
+        assert np.all(ids_h[bad] == -1) and np.all(sc_h[bad] == 0), bad
+
+
+def test_decode_select_tie_heavy_16_rows_16384_regions():
+    """16 rows over 16,384 regions each, tie-heavy codes: many exact ties
+    around the 512th score, ordered by region id."""
+    rows, R = 16, 16384
+    g = torch.Generator().manual_seed(9)
+    draw, w = _draw("tie_heavy", g)
+    d = {"rows": rows, "q8": draw((rows, 16, 64)).to(DEV), "w_head": w.to(DEV),
+         "row_seq": torch.arange(rows, dtype=torch.int32, device=DEV),
+         "row_pos": torch.full((rows,), 8 * R - 1, dtype=torch.int64, device=DEV)}
+    S = draw((rows, R, 4, 64)).to(DEV)
+    P.say(f"[case] decode select tie-heavy: {rows} rows x {R} regions")
+    ids, sc = P.gpu_select(d, S)
+    torch.cuda.synchronize()
+    osc = P.oracle_scores(d, P.host8(S), list(range(rows)))
+    ex = P.compare_selection(ids.cpu().numpy(), sc.cpu().numpy(), osc,
+                             d["row_pos"].cpu().numpy(), exact=True)
+    assert ex == 0

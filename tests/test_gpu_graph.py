@@ -25,7 +25,7 @@ def test_graph_replays_match_eager(name):
     S = torch.zeros((B, R_cap, 4, 64), dtype=torch.uint8, device=dev)
     s5.step5_index_summarize(d["k_idx"], d["z_idx"], 0, d["ln_w"], d["ln_b"], P.EPS, d["rope"], S)
     ws1 = torch.empty(s5.step5_index_score_topk_workspace(rows, R_cap), dtype=torch.uint8, device=dev)
-    ws2 = torch.empty(max(1, s5.step5_sparse_attn_workspace(rows)), dtype=torch.uint8, device=dev)
+    ws2 = torch.zeros(max(1, s5.step5_sparse_attn_workspace(rows)), dtype=torch.uint8, device=dev)
     own0 = (T - 1) // 8 * 8
     ids = torch.empty((rows, 4, 512), dtype=torch.int32, device=dev)
     sc = torch.empty((rows, 4, 512), dtype=torch.float32, device=dev)

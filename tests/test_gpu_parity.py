@@ -411,3 +411,37 @@ def test_rejected_calls_write_nothing():
                                   q_eps=-1.0, rope=d["rope"].to(DEV))
     torch.cuda.synchronize()
     assert torch.all(S == 0x5A) and torch.all(ids == 7)
+
+
+def test_attention_workspace_reused_across_row_counts():
+    """One workspace, zeroed once, serves calls of 16, 5, 33 and again 16 rows
+    (different split plans): every call equals the same call on a fresh
+    workspace, bit for bit, so each call leaves the workspace's arrival
+    counters as it found them."""
+    import math
+    import long_context_sparse_indexer_amd as s5
+    g = torch.Generator(device=DEV)
+    g.manual_seed(12)
+    T = 6000
+    k = torch.randn((33, T, 4, 128), generator=g, device=DEV).to(torch.bfloat16)
+    v = torch.randn((33, T, 4, 128), generator=g, device=DEV).to(torch.bfloat16)
+    nb = max(s5.step5_sparse_attn_workspace(r) for r in (16, 5, 33))
+    ws = torch.zeros(nb + 256, dtype=torch.uint8, device=DEV)
+    ws = ws[(-ws.data_ptr()) % 256:]
+    for rows in (16, 5, 33, 16):
+        P.say(f"[case] attention workspace reuse, rows={rows}")
+        q = torch.randn((rows, 16, 128), generator=g, device=DEV).to(torch.bfloat16)
+        seq = torch.arange(rows, dtype=torch.int32, device=DEV)
+        pos = T - 1 - torch.randint(0, 9, (rows,), generator=g, device=DEV)
+        ids = torch.stack([torch.randperm(int(pos.min()) // 8, generator=g, device=DEV)[:512]
+                           for _ in range(rows * 4)]).to(torch.int32).view(rows, 4, 512).contiguous()
+        outs = []
+        for w in (ws, None):
+            out = torch.full((rows, 16, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+            lse = torch.full((rows, 16), float("nan"), dtype=torch.float32, device=DEV)
+            s5.step5_sparse_attn(q, k[:rows], v[:rows], ids, seq, pos, 1 / math.sqrt(128), out, lse,
+                                 workspace=w)
+            outs.append((out, lse))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16)), rows
+        assert torch.equal(outs[0][1], outs[1][1]), rows

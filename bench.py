@@ -1,9 +1,10 @@
 """Benchmark of the Step-5 sparse-indexer hot path on one MI355X.
 
 A step is one pass of the whole path over a batch of rows of one attention
-layer, with every input resident in HBM (each call captured as a HIP graph
-and replayed, so the step measures the GPU and not the Python launch path;
-the whole step is one graph, launched once per step):
+layer, with every input resident in HBM (the calls captured as HIP graphs and
+replayed, so the step measures the GPU and not the Python launch path; one
+graph holds one step per layer copy, as a decode pass captures all of a
+model's layers, and the one-graph-per-step figure is reported beside it):
   1. step5_index_append      decode: each row's new token into the k/z rings and
                              the region it completes summarised (prefill:
                              step5_index_summarize over the chunk)
@@ -75,6 +76,9 @@ def parse():
                     help="comma-separated extra lines to measure after the headline "
                          "(workload names, attn_geometry and/or hbm_copy; 'none' for none)")
     ap.add_argument("--eager", action="store_true", help="launch the calls directly, no HIP graphs")
+    ap.add_argument("--steps-per-graph", type=int, default=0,
+                    help="consecutive steps (one per layer copy) captured in one HIP graph; "
+                         "0: one step per layer copy (a decode pass over the layers)")
     ap.add_argument("--no-resident", action="store_true",
                     help="skip the per-call times on one layer copy (so that a profiled run holds "
                          "only launches that rotate over the copies)")
@@ -90,9 +94,11 @@ class Timer:
     the calls run on.
 
     layers: one list of (name, fn) per layer copy, the same names in the same
-    order. step(): each layer's whole step captured as ONE HIP graph (unless
-    eager); step i replays layer i mod L's graph, with a HIP event before
-    every replay. per_call(rotate): each call captured `reps` times back to
+    order. step(steps, per_graph): steps in turn on layer copy i mod L, with
+    per_graph consecutive steps (one per layer copy: a decode pass over the
+    model's layers) captured in ONE HIP graph and replayed (unless eager),
+    a HIP event before every replay; steps not filling a graph run in a
+    shorter one. per_call(rotate): each call captured `reps` times back to
     back in one graph, call k on layer k mod L (rotate) or on layer 0 every
     time (resident), replayed a few times; per-call time = event-timed replay
     / reps (what the call's kernels take, without the launch gap of a graph
@@ -104,17 +110,10 @@ class Timer:
         self.names = [n for n, _ in layers[0]]
         self.eager = eager
         self.stream = torch.cuda.current_stream()
+        self.graphs = {}
         for i in range(max(warmup, len(layers))):
             for _, f in layers[i % len(layers)]:
                 f()
-        torch.cuda.synchronize()
-        if eager:
-            self.step_fns = [(lambda calls=calls: [f() for _, f in calls]) for calls in layers]
-        else:
-            self.graphs = [self._capture([f for _, f in calls]) for calls in layers]
-            self.step_fns = [g.replay for g in self.graphs]
-        for i in range(max(warmup, len(layers))):
-            self.step_fns[i % len(layers)]()
         torch.cuda.synchronize()
 
     def _capture(self, fns):
@@ -124,20 +123,40 @@ class Timer:
                 f()
         return g
 
-    def step(self, steps):
+    def _runner(self, first, count):
+        """One run of `count` consecutive steps from layer copy `first`."""
+        L = len(self.layers)
+        fns = [f for i in range(count) for _, f in self.layers[(first + i) % L]]
+        if self.eager:
+            return lambda: [f() for f in fns]
+        key = (first % L, count)
+        if key not in self.graphs:
+            self.graphs[key] = self._capture(fns)
+        return self.graphs[key].replay
+
+    def step(self, steps, per_graph, warmup=2):
         torch = self.torch
-        L = len(self.step_fns)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        L = len(self.layers)
+        runs = []
+        i = 0
+        while i < steps:
+            n = min(per_graph, steps - i)
+            runs.append((self._runner(i, n), n))
+            i += n
+        for _ in range(warmup):
+            for run, _ in runs:
+                run()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(runs) + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(steps):
-            evs[i].record(self.stream)
-            self.step_fns[i % L]()
-        evs[steps].record(self.stream)
+        for j, (run, _) in enumerate(runs):
+            evs[j].record(self.stream)
+            run()
+        evs[len(runs)].record(self.stream)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        gpu_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-        return elapsed, sum(gpu_ms) / steps
+        gpu_ms = sum(evs[j].elapsed_time(evs[j + 1]) for j in range(len(runs)))
+        return elapsed, gpu_ms / steps
 
     def per_call(self, rotate, reps=None, rounds=5):
         torch = self.torch
@@ -330,9 +349,16 @@ def run_workload(name, args, torch, s5, W):
         return calls
 
     steps = args.steps if name == HEADLINE else max(5, min(args.steps, 20))
-    log(f"{name}: timing {steps} steps over {L} layer copies")
+    per_graph = L if args.steps_per_graph == 0 else args.steps_per_graph
+    log(f"{name}: timing {steps} steps over {L} layer copies, {per_graph} steps per graph")
     timer = Timer(torch, [layer_calls(lay) for lay in layers], args.warmup, args.eager)
-    elapsed, gpu_step_ms = timer.step(steps)
+    elapsed, gpu_step_ms = timer.step(steps, per_graph)
+    one_per_graph = None
+    if per_graph != 1 and not args.eager:
+        e1, g1 = timer.step(steps, 1)
+        one_per_graph = {"ms_per_step": round(e1 * 1000.0 / steps, 4),
+                         "gpu_ms_per_step": round(g1, 4),
+                         "rows_per_s": round(rows * steps / e1, 1)}
     log(f"{name}: per-call times (rotating, then resident)")
     per_call = timer.per_call(rotate=True)
     per_res = {} if args.no_resident else timer.per_call(rotate=False)
@@ -346,6 +372,8 @@ def run_workload(name, args, torch, s5, W):
     res.update({
         "layers": L,
         "layer_reuse_bytes": (L - 1) * step_bytes,
+        "steps_per_graph": per_graph,
+        "one_step_per_graph": one_per_graph,
         "steps": steps,
         "ms_per_step": round(ms_per_step, 4),
         "gpu_ms_per_step": round(gpu_step_ms, 4),

@@ -621,12 +621,18 @@ def main():
                    "candidates_per_row": head["candidates_per_row"][0], "topk": 512, "region": 8,
                    "idx_heads": 16, "kv_groups": 4, "q_heads": 16, "head_dim": 128,
                    "inputs": wl.dist, "layer_copies": head["layers"]},
-        "roofline": {"bound": "hbm",
-                     "kernel": "step5_sparse_attn (attn_kernel + attn_mh_merge_kernel)",
-                     "achieved": sa["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": sa["frac_hbm"], "traffic": attn_traffic(args.workload),
-                     "algorithmic_bytes_per_launch": sa["algorithmic_bytes"],
-                     "layer_copies": head["layers"]},
+        "roofline": ({"bound": "hbm",
+                      "kernel": "step5_sparse_attn (attn_kernel, split states merged in the launch)",
+                      "achieved": sa["GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": sa["frac_hbm"], "traffic": attn_traffic(args.workload),
+                      "algorithmic_bytes_per_launch": sa["algorithmic_bytes"],
+                      "layer_copies": head["layers"]} if "GBs" in sa else
+                     {"bound": "mfma",
+                      "kernel": "step5_sparse_attn (attn_tile_kernel, the context sweep)",
+                      "achieved": sa["TFLOPs"], "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": sa["frac_bf16_mfma"], "traffic": None,
+                      "algorithmic_flops_per_launch": sa["algorithmic_flops"],
+                      "layer_copies": head["layers"]}),
         "phases": {"graph_replay": not args.eager, **{k: v for k, v in head.items()
                                                       if k not in ("workload",)}},
     }

@@ -392,52 +392,60 @@ __device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int
 // ---------------------------------------------------------------------------
 constexpr int FUSED_MAX_N = 16 * TK_WAVES * TK_PER;  // 4,096
 
+// dword 3 of a raw buffer resource for 32-bit offsets (as attn_tile.hip's)
+constexpr int FK_RSRC3 = 0x00020000;
+
 __device__ inline int32_t fused_id(int tid, int k) {
   return 256 * k + 16 * (tid >> 6) + (tid & 15);
 }
 
-// The keys of candidate fused_id(tid, t): upper key in kh[t], lower key in
-// kl[fused_id] (LDS, for the rare cut by lower keys), absent ones 0; mx gets
-// the thread's 4 group maxima of lower keys. q8r: the row's prepared query
-// [16 heads][64]; Sg: the sequence's summary at group g (candidate stride
-// 256 B); N >= 1 candidates.
-__device__ inline void fused_keys(uint32_t (&kh)[TK_PER], uint32_t (&mx)[4], uint32_t* kl,
+// The keys of the thread's candidates fused_id(tid, t): upper and lower key
+// in kh[j] and kl[j] (LDS, by candidate id j; absent ones 0); mx gets the
+// thread's 4 group maxima of lower keys. The keys go to LDS rather than
+// registers (only lanes 0..15 hold any), so that four tiles fit in flight per
+// round trip to L2 within the selection's 64-register cap. q8r: the row's
+// prepared query [16 heads][64]; Sg: the sequence's summary at group g
+// (candidate stride 256 B); N >= 1 candidates.
+__device__ inline void fused_keys(uint32_t* kh, uint32_t (&mx)[4], uint32_t* kl,
                                   const uint8_t* __restrict__ q8r, const uint8_t* __restrict__ Sg,
                                   int g, int N, const float* w4, int tid) {
   const int lane = tid & 63, n = lane & 15, qd = lane >> 4;
   const int wave = tid >> 6;
-  // the query stays packed (widened per tile) and tiles go two at a time,
-  // within the selection's 64-register cap
+  // the query stays packed (widened per tile)
   uint4 araw = n < 4 ? ldg16(q8r + (4 * g + n) * 64 + 16 * qd) : make_uint4(0, 0, 0, 0);
   const uint32_t jmax = (uint32_t)(N - 1);
-#pragma unroll
-  for (int k = 0; k < TK_PER; ++k) kh[k] = 0u;
+  // summary loads through a buffer resource over the N candidates (a scalar
+  // base and a 32-bit offset per lane: no 64-bit address per lane to keep)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Sg, (short)0, (int)((uint32_t)N * 256u), FK_RSRC3);
 #pragma unroll
   for (int i = 0; i < 4; ++i) mx[i] = 0u;
 #pragma unroll
-  for (int b = 0; b < TK_PER / 2; ++b) {
-    if (2 * 256 * b >= N) break;  // block-uniform
-    // re-widened every pair of tiles, not hoisted out of the loop (16 more
-    // registers for the whole loop would spill)
+  for (int b = 0; b < TK_PER / 4; ++b) {
+    if (4 * 256 * b >= N) break;  // block-uniform
+    // re-widened every four tiles, not hoisted out of the loop
     asm volatile("" : "+v"(araw.x), "+v"(araw.y), "+v"(araw.z), "+v"(araw.w));
-    uint4 bq[2];
+    uint4 bq[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t j = min((uint32_t)(256 * (2 * b + u) + 16 * wave + n), jmax);
-      bq[u] = ldg16(Sg + j * 256u + 16 * qd);
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t j = min((uint32_t)(256 * (4 * b + u) + 16 * wave + n), jmax);
+      bq[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rs, (int)(j * 256u + 16 * qd), 0, 0));
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = 2 * b + u;
+    for (int u = 0; u < 4; ++u) {
+      const int t = 4 * b + u;
       f32x4 d, a;
       dot64(widen16(araw), widen16(bq[u]), d, a);
       const float2 iv = score_interval(d, a, w4);
       const int j = 256 * t + 16 * wave + n;
       const bool ok = qd == 0 && j < N;
       const uint32_t lo = ok ? ord_key(iv.x) : 0u;
-      kh[t] = ok ? ord_key(iv.y) : 0u;
-      mx[t & 3] = lo > mx[t & 3] ? lo : mx[t & 3];
-      if (ok) kl[j] = lo;
+      mx[u] = lo > mx[u] ? lo : mx[u];
+      if (ok) {
+        kl[j] = lo;
+        kh[j] = ord_key(iv.y);
+      }
     }
   }
 }
@@ -593,16 +601,17 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   uint32_t kh[TK_PER];
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
   uint32_t* const kl_lds = reinterpret_cast<uint32_t*>(sm.xb);  // fused: lower keys by id
+  // fused: upper keys by id, past the selection's LDS
+  uint32_t* const kh_lds = reinterpret_cast<uint32_t*>(smem + tk_smem_bytes(FUSED_MAX_N));
   if constexpr (FUSED) {
     unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
     N = (int)(ncand < FUSED_MAX_N ? ncand : FUSED_MAX_N);
     float w4[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
-#pragma unroll
-    for (int k = 0; k < TK_PER; ++k) kh[k] = 0u;
     if (N > 0)  // block-uniform
-      fused_keys(kh, mx, kl_lds, q8 + row * qs8, S + (int64_t)seq * ssb + g * 64, g, N, w4, tid);
+      fused_keys(kh_lds, mx, kl_lds, q8 + row * qs8, S + (int64_t)seq * ssb + g * 64, g, N, w4,
+                 tid);
   } else {
     const int nslot = (int)((R_cap - j0 < chunk) ? R_cap - j0 : chunk);
 #pragma unroll
@@ -641,6 +650,14 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
 #pragma unroll
     for (int w = 1; w < TK_WAVES; ++w) t = min(t, sm.misc[w]);
     tau = t > 1u ? t : 1u;
+  }
+  if constexpr (FUSED) {
+    // the thread's own upper keys back from LDS (it wrote them itself)
+#pragma unroll
+    for (int k = 0; k < TK_PER; ++k) {
+      const int j = fused_id(tid, k);
+      kh[k] = (lane < 16 && j < N) ? kh_lds[j] : 0u;
+    }
   }
   // 2. survivors: upper key >= tau, appended per wave (their order is free:
   //    the selection sorts by (key, id))
@@ -783,7 +800,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     napp = (unsigned)ap.rows;
   }
   if (a.fused) {
-    const size_t sm = tk_smem_bytes(FUSED_MAX_N);
+    const size_t sm = tk_smem_bytes(FUSED_MAX_N) + (size_t)FUSED_MAX_N * sizeof(uint32_t);
     hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel<TK_FUSED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;

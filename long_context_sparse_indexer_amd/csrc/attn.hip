@@ -8,11 +8,12 @@
 // region first, then the 512 selected regions) is cut into splits of
 // `per_split` entries, one 256-thread workgroup each; inside a workgroup the
 // four waves take 4-entry chunks (32 tokens) in turn; wave states merge in
-// wave order, split states merge in split order, by the unit's last split to
-// finish (an arrival counter per unit in the workspace; the split states are
-// written and read through device-coherent memory, so no cache write-back is
-// needed between workgroups on different dies). Results are therefore
-// independent of scheduling.
+// wave order, split states merge in split order: with up to 8 splits by the
+// unit's last split to finish (an arrival counter per unit in the workspace;
+// the split states are written and read through device-coherent memory, so no
+// cache write-back is needed between workgroups on different dies), with more
+// by a merge kernel (attn_mh_merge_kernel). Results are therefore independent
+// of scheduling.
 //
 // Per 32-token chunk, per wave:
 //  - QK^T with the 16x16x32 bf16 MFMA: A = the unit's 4 query heads (MFMA
@@ -37,6 +38,7 @@ namespace s5 {
 
 constexpr int AT_ENTRIES = 513;  // own region + 512 selections
 constexpr int AT_PART = 130;     // m, l, o[128] per head in a split state
+constexpr int AT_MERGE_MAX = 8;  // splits merged inside the attention launch
 
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -316,11 +318,13 @@ __global__ __launch_bounds__(256) void attn_kernel(
     O1 = O1 + f * s1;
   }
   if (nsplit > 1) {
-    // This split's state, stored with device-scope (write-through) stores and
-    // waited for; then one arrival per split at the unit's counter. The last
-    // split to arrive resets the counter (so the workspace is left as found)
-    // and merges every split's state, read with device-scope loads, in split
-    // order, as a merge kernel would.
+    // This split's state, stored with device-scope (write-through) stores. With
+    // few splits (AT_MERGE_MAX; `arrive` given) the unit's last split merges
+    // them: every thread waits for its stores, then one arrival per split at
+    // the unit's counter; the last split to arrive resets the counter (the
+    // workspace is left as found) and merges every split's state, read with
+    // device-scope loads all issued at once, in split order. With more splits
+    // attn_mh_merge_kernel merges them afterwards.
     __shared__ int sh_last;
     float* dst = partial + ((unit * nsplit + split) * 4 + r) * AT_PART;
     if (d0 == 0) {
@@ -329,6 +333,7 @@ __global__ __launch_bounds__(256) void attn_kernel(
     }
     __hip_atomic_store(dst + 2 + d0, O0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(dst + 3 + d0, O1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!arrive) return;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -342,20 +347,33 @@ __global__ __launch_bounds__(256) void attn_kernel(
     if (!sh_last) return;
     const float* st = partial + (unit * nsplit * 4 + r) * AT_PART;
     const int64_t sstride = 4 * AT_PART;  // between a head's states of consecutive splits
+    float mv[AT_MERGE_MAX], lv[AT_MERGE_MAX], ov0[AT_MERGE_MAX], ov1[AT_MERGE_MAX];
+#pragma unroll
+    for (int sp = 0; sp < AT_MERGE_MAX; ++sp) {
+      if (sp < nsplit) {
+        const float* ss = st + sp * sstride;
+        mv[sp] = __hip_atomic_load(ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        lv[sp] = __hip_atomic_load(ss + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ov0[sp] = __hip_atomic_load(ss + 2 + d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ov1[sp] = __hip_atomic_load(ss + 3 + d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
     M = -INFINITY;
-    for (int sp = 0; sp < nsplit; ++sp)
-      M = fmaxf(M, __hip_atomic_load(st + sp * sstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int sp = 0; sp < AT_MERGE_MAX; ++sp)
+      if (sp < nsplit) M = fmaxf(M, mv[sp]);
     Mu = (M == -INFINITY) ? 0.f : M;
     L = 0.f;
     O0 = 0.f;
     O1 = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float* ss = st + sp * sstride;
-      const float f = __builtin_amdgcn_exp2f(
-          __hip_atomic_load(ss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - Mu);
-      L = L + f * __hip_atomic_load(ss + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      O0 = O0 + f * __hip_atomic_load(ss + 2 + d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      O1 = O1 + f * __hip_atomic_load(ss + 3 + d0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int sp = 0; sp < AT_MERGE_MAX; ++sp) {
+      if (sp < nsplit) {
+        const float f = __builtin_amdgcn_exp2f(mv[sp] - Mu);
+        L = L + f * lv[sp];
+        O0 = O0 + f * ov0[sp];
+        O1 = O1 + f * ov1[sp];
+      }
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
@@ -463,7 +481,7 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   unsigned* arrive = nullptr;
   float* states = nullptr;
   if (pl.nsplit > 1) {
-    arrive = reinterpret_cast<unsigned*>(a.partial);
+    if (pl.nsplit <= AT_MERGE_MAX) arrive = reinterpret_cast<unsigned*>(a.partial);
     states = reinterpret_cast<float*>(reinterpret_cast<char*>(a.partial) + AT_COUNTER_BYTES);
   }
   hipLaunchKernelGGL(attn_kernel, dim3(units, (unsigned)pl.nsplit), dim3(256), 0, stream,
@@ -471,7 +489,12 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.v, a.B, a.kv_sb, a.kv_st, a.T_cap, a.sel, a.row_seq,
                      a.row_pos, a.rows, maxr, scale_log2, pl.per_split, pl.nsplit, states,
                      arrive, (uint16_t*)a.out, a.lse);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || pl.nsplit <= AT_MERGE_MAX) return e;
+  // many splits (one or two rows): a merge kernel with one workgroup per
+  // (unit, head) keeps every split's loads in flight; the states are laid out
+  // as attn_mh.hip's, 4 heads x 128 dims
+  return launch_attn_merge(states, pl.nsplit, a.rows, 4, 128, a.out, a.lse, stream);
 }
 
 }  // namespace s5

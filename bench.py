@@ -52,8 +52,8 @@ HBM_PEAK_GBS = 8000.0
 # profiles/sparse_attn_hbm_counters_decode16_ctx128k.md), each scaled by what
 # the counter reads for a 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).
 # Valid only for the attention source the counters were taken on.
-ATTN_TRAFFIC = {"source_sha256": "ef4e4fc315f463f7547b519935e05edc200a1f4595d7d35352148ede8fe7204c",
-                "bytes_per_launch": 136238464}
+ATTN_TRAFFIC = {"source_sha256": "8e005b4a8c294e774eb30f8fdc448595d2531ce6d2ac4ff6e0bcd9e93a535eb1",
+                "bytes_per_launch": 136713216}
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 METRIC = "sparse-attn decode rows/s at 128K ctx; indexer HBM GB/s as % of peak"

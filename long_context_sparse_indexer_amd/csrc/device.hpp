@@ -214,6 +214,14 @@ __device__ inline void unpack_bf16x8(const uint4 w, float* f) {
 
 __device__ inline uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// 32-bit key ordered like the float score (-0 first turned into +0 by adding
+// +0); every key but that of one negative NaN pattern is nonzero, and the
+// selection uses 0 for "no candidate"
+__device__ inline uint32_t ord_key(float s) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 // Arrival of a block at a per-unit counter after it has written its part of a
 // result to global memory; true in the one block that arrives last, which may
 // then read every other block's part. Each wave first waits until its own

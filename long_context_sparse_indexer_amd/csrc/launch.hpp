@@ -55,7 +55,9 @@ struct QPrepArgs {
   const int64_t* row_pos;
   uint8_t* q8;            // [rows, 16, 64] e4m3
   double* q64;            // [rows, 4 groups, 64 dims, 4 heads]: exact values of the e4m3 q
-  unsigned* arrivals;     // [rows*4] top-k arrival counters, zeroed here
+  unsigned* arrivals;     // [rows*8]: top-k arrival counters (zeroed by the q prep or the
+                          // exact scorer), then the exact path's survivor counts (zeroed
+                          // by the exact scorer)
 };
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream);
 
@@ -75,6 +77,8 @@ struct ScoreArgs {
   QPrepArgs prep;
   float2* bounds;         // [rows, 4, R_cap]: interval holding each exact score, or (exact)
                           // the exact scores as float [rows, 4, R_cap]
+  uint32_t* pool;         // exact mode, several selection chunks: [rows*4, blocks, 8] keys
+                          // for the selection's threshold (see topk_pool_bytes); else null
 };
 // Rows up to S5_EXACT_MAX_ROWS are scored exactly on the fp64 matrix cores,
 // the query prep fused in; more rows get their query prepped by its own
@@ -105,6 +109,9 @@ struct TopkPlan {
 };
 TopkPlan topk_plan(int32_t rows, int64_t R_cap);
 size_t topk_partial_bytes(int32_t rows, int64_t R_cap);
+// exact scores cut into several chunks: the scorer's threshold keys, 8 per
+// (row, group) and block of 256 candidates (0 bytes otherwise)
+size_t topk_pool_bytes(int32_t rows, int64_t R_cap);
 
 struct TopkArgs {
   const float2* bounds;  // [rows, 4, R_cap] from launch_score
@@ -124,7 +131,9 @@ struct TopkArgs {
   int64_t B;
   int64_t pos_limit;
   unsigned long long* partial;  // [rows*4, nchunks, 512] chunk lists when nchunks > 1
-  unsigned* arrivals;    // [rows*4], zero on entry (q prep zeroes them)
+  const uint32_t* pool;  // exact with nchunks > 1: the scorer's threshold keys
+  unsigned* arrivals;    // [rows*8]: arrival counters, then survivor counts; zero on
+                         // entry (the q prep or the exact scorer zeroes them)
   int32_t* sel_ids;
   float* sel_scores;
   // optional: the cache append of a call whose rows are of distinct

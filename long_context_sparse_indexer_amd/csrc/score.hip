@@ -333,7 +333,10 @@ __global__ __launch_bounds__(256) void score_kernel(
 // prep the row's 16 heads into LDS once per block (the same steps as
 // qprep_kernel); the first candidate block zeroes the row's top-k arrival
 // counters. The prep's loads are issued first, then each wave's first 8
-// quads of summary loads, then the prep's arithmetic.
+// quads of summary loads, then the prep's arithmetic. With `pool` (units cut
+// into several selection chunks) the block also leaves, per group, 8 keys
+// for the selection's threshold: each the best score key among 32 of its
+// candidates (lanes 4g + j and 4g + (j ^ 1) of a wave), 0 where none.
 // ---------------------------------------------------------------------------
 constexpr int SM_CB = 256;  // candidates per block
 
@@ -341,16 +344,23 @@ template <bool PREPARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_exact_mfma_kernel(
     const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
     const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
-    int64_t ssb, int64_t pos_limit, float* __restrict__ scores, QPrepArgs prep) {
+    int64_t ssb, int64_t pos_limit, float* __restrict__ scores, uint32_t* __restrict__ pool,
+    QPrepArgs prep) {
   __shared__ __align__(16) uint8_t q_lds[16 * 64];
+  __shared__ uint32_t pmax[4][8];  // pool: the best key of each 32 candidates (see below)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (threadIdx.x < 32) pmax[threadIdx.x >> 3][threadIdx.x & 7] = 0u;
   const int k = lane >> 4, g = (lane >> 2) & 3, ij = lane & 3;  // ij: head i (A) or candidate j (B)
   const int64_t row = blockIdx.y;
   const int32_t s = row_seq[row];
   const int64_t p = row_pos[row];
   const bool ok = s >= 0 && s < B && p >= 0 && p < pos_limit && (p >> 3) <= R_cap;
   const int64_t nc = ok ? (p >> 3) : 0;
-  if (blockIdx.x == 0 && threadIdx.x < 4) prep.arrivals[row * 4 + threadIdx.x] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < 4) {
+    // the selection's arrival counters and (pool selection) survivor counts
+    prep.arrivals[row * 4 + threadIdx.x] = 0u;
+    prep.arrivals[(int64_t)prep.rows * 4 + row * 4 + threadIdx.x] = 0u;
+  }
   if ((int64_t)blockIdx.x * SM_CB >= nc) return;  // block-uniform
   const int64_t cb0 = (int64_t)blockIdx.x * SM_CB + 64 * wave;
   const bool live = cb0 < nc;
@@ -392,7 +402,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   if (wave < 2) *reinterpret_cast<uint2*>(&q_lds[ph * 64 + pc * 8]) = pk;
   __syncthreads();
-  if (!live) return;
+  // pool: per (row, group) and block, 8 keys, entry 2 * wave + p the best
+  // key among the 32 candidates of lanes 4g + 2p and 4g + 2p + 1 (0 if
+  // none), gathered by LDS atomic max in pmax[wave][2g + p] (lane >> 1)
+  auto pool_put = [&]() {
+    if (lane < 8)
+      pool[((row * 4 + (lane >> 1)) * (int64_t)gridDim.x + blockIdx.x) * 8 + 2 * wave +
+           (lane & 1)] = pmax[wave][lane];
+  };
+  if (!live) {
+    if (pool) pool_put();
+    return;
+  }
   // A operand: head 4g + ij, dims 16k..16k+15 as packed e4m3, converted per use
   const uint4 qraw = *reinterpret_cast<const uint4*>(&q_lds[(4 * g + ij) * 64 + 16 * k]);
   const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
@@ -435,7 +456,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       sc = sc + t2;
       sc = sc + t3;
       const int64_t j = cb0 + 4 * (u0 + q) + ij;
-      if (lane < 16 && j < jend) out_g[j] = sc;
+      if (lane < 16 && j < jend) {
+        out_g[j] = sc;
+        if (pool) atomicMax(&pmax[wave][lane >> 1], ord_key(sc));
+      }
     }
   };
   load4(8, bC);
@@ -444,6 +468,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   quads4(4, bB);
   quads4(8, bC);
   quads4(12, bA);
+  if (pool) pool_put();  // the wave's own LDS atomics precede its reads
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
@@ -453,11 +478,11 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
     if (a.prep.prepared)
       hipLaunchKernelGGL(score_exact_mfma_kernel<true>, grid, dim3(256), 0, stream, a.w_head,
                          a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
+                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.pool, a.prep);
     else
       hipLaunchKernelGGL(score_exact_mfma_kernel<false>, grid, dim3(256), 0, stream, a.w_head,
                          a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.prep);
+                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.pool, a.prep);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));

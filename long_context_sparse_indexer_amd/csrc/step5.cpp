@@ -47,7 +47,7 @@ int check_geom(const step5_geom* g) {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 struct ScoreWs {
-  size_t q8 = 0, q64 = 0, bounds = 0, partial = 0, arrivals = 0, total = 0;
+  size_t q8 = 0, q64 = 0, bounds = 0, partial = 0, pool = 0, arrivals = 0, total = 0;
 };
 ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   ScoreWs w;
@@ -59,10 +59,12 @@ ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   w.bounds = off;  // score interval per (row, group, candidate), unless fused
   if (!s5::select_fused(rows, R_cap))
     off = up(off + (size_t)rows * kGroups * (size_t)R_cap * 2 * sizeof(float));
-  w.partial = off;
+  w.partial = off;  // chunk lists (or survivor lists) when units are cut into chunks
   off = up(off + s5::topk_partial_bytes(rows, R_cap));
-  w.arrivals = off;  // chunk arrival counters per (row, group)
-  off = up(off + (size_t)rows * kGroups * sizeof(unsigned));
+  w.pool = off;     // exact path with chunks: the scorer's threshold keys
+  off = up(off + s5::topk_pool_bytes(rows, R_cap));
+  w.arrivals = off;  // chunk arrival counters, then survivor counts, per (row, group)
+  off = up(off + (size_t)rows * kGroups * 2 * sizeof(unsigned));
   w.total = off;
   return w;
 }
@@ -274,6 +276,7 @@ static int score_topk(const step5_geom* geom, uint32_t flags, const void* q, int
   sa.pos_limit = q_ready ? INT64_MAX : rope_rows;
   sa.exact = exact;
   sa.bounds = reinterpret_cast<float2*>(ws + w.bounds);
+  sa.pool = s5::topk_pool_bytes(rows, R_cap) ? reinterpret_cast<uint32_t*>(ws + w.pool) : nullptr;
   const bool fused = s5::select_fused(rows, R_cap);
   if (!fused) {
     st = from_hip(s5::launch_score(sa, stream));
@@ -297,6 +300,7 @@ static int score_topk(const step5_geom* geom, uint32_t flags, const void* q, int
   ta.B = B;
   ta.pos_limit = sa.pos_limit;
   ta.partial = reinterpret_cast<unsigned long long*>(ws + w.partial);
+  ta.pool = sa.pool;
   ta.arrivals = qa.arrivals;
   ta.sel_ids = sel_ids;
   ta.sel_scores = sel_scores;

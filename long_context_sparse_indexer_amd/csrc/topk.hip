@@ -56,11 +56,6 @@ constexpr int TK_BINS = 2048;
 constexpr int TK_PER = (int)(TK_MAX_N / TK_THREADS);  // keys per thread in registers
 constexpr int TK_SORT = 1024;                           // survivors sorted directly up to this
 
-// 32-bit key ordered like the float (-0 first turned into +0 by adding +0)
-__device__ inline uint32_t ord_key(float s) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, s + 0.0f);
-  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-}
 __device__ inline float key_score(uint32_t k) {
   const uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
   return __builtin_bit_cast(float, u);
@@ -148,6 +143,7 @@ __device__ inline uint32_t block_excl_scan(uint32_t v, uint32_t* misc, uint32_t*
 
 struct Boundary {
   uint32_t P, mask, need;
+  uint32_t cnt;  // keys with (k & mask) == P (>= need)
 };
 
 // Radix select over keys[0..N), 1 <= K <= N: keys with (k & mask) > P are
@@ -202,13 +198,21 @@ __device__ Boundary radix_boundary(const TkShared& sm, int N, int K, int passes 
   bd.P = P;
   bd.mask = mask;
   bd.need = need;
+  bd.cnt = sm.misc[50];
+  __syncthreads();
   return bd;
 }
 
-// keys/ids[0..N) -> sm.out[0..K): the best K (any order), N > K >= 1
+// keys/ids[0..N) -> sm.out[0..K): the best K by (key, then smaller id), in
+// any order, N > K >= 1. Keys above the boundary are all taken; when more
+// keys equal the K-th best key than are needed, a second radix select over
+// their ids (as ~id) takes the smallest ids. sm.keys is overwritten.
 __device__ void collect_best(const TkShared& sm, int N, int K) {
   const int tid = threadIdx.x;
   const Boundary bd = radix_boundary(sm, N, K);
+  // the passes ran to the full key (mask all ones) unless the boundary bin
+  // was taken whole, so only then can equal keys outnumber the need
+  const bool tie = bd.cnt > bd.need;
   const int seg = (N + TK_THREADS - 1) / TK_THREADS;
   const int i0 = min(N, tid * seg), i1 = min(N, i0 + seg);
   uint32_t ngt = 0, neq = 0;
@@ -227,9 +231,27 @@ __device__ void collect_best(const TkShared& sm, int N, int K) {
     if (m < bd.P) continue;
     if (m > bd.P) {
       sm.out[gt_off++] = compose(k, sm.ids[i]);
-    } else {
-      if (eq_off < bd.need) sm.out[eq_base + eq_off] = compose(k, sm.ids[i]);
-      ++eq_off;
+    } else if (!tie) {
+      sm.out[eq_base + eq_off++] = compose(k, sm.ids[i]);
+    }
+  }
+  if (tie) {  // block-uniform
+    // keys equal to P = the K-th best key: rank them by ~id (ids are
+    // distinct, so the select ends exact); every other entry drops out as 0
+    __syncthreads();
+    for (int i = i0; i < i1; ++i)
+      sm.keys[i] = sm.keys[i] == bd.P ? ~(uint32_t)sm.ids[i] : 0u;
+    __syncthreads();
+    const Boundary b2 = radix_boundary(sm, N, (int)bd.need);
+    uint32_t nsel = 0;
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = sm.keys[i];
+      nsel += k != 0u && (k & b2.mask) >= b2.P;
+    }
+    uint32_t off = block_excl_scan(nsel, sm.misc, &tot);
+    for (int i = i0; i < i1; ++i) {
+      const uint32_t k = sm.keys[i];
+      if (k != 0u && (k & b2.mask) >= b2.P) sm.out[eq_base + off++] = compose(bd.P, (int32_t)~k);
     }
   }
   __syncthreads();
@@ -453,16 +475,17 @@ __device__ inline void fused_keys(uint32_t* kh, uint32_t (&mx)[4], uint32_t* kl,
 // Appends the candidates whose key reaches t to sm.ids (and, with keys, the
 // key to sm.keys), per wave in ballot order; misc[56] holds the count, zero
 // on entry. Returns the total (a barrier comes first). Key k of thread tid is
-// candidate j0 + tid + 1024 k, or with FUSED the candidate fused_id gives.
+// candidate j0 + tid + 1024 k, or with FUSED the candidate fused_id gives;
+// slots k >= nk are not looked at.
 template <bool FUSED = false>
 __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_PER], uint32_t t,
-                                   int64_t j0, bool keys) {
+                                   int64_t j0, bool keys, int nk = TK_PER) {
   const int tid = threadIdx.x, lane = tid & 63;
   unsigned long long msk[TK_PER];
   uint32_t wt = 0;
 #pragma unroll
   for (int k = 0; k < TK_PER; ++k) {
-    msk[k] = __ballot(key[k] >= t);
+    msk[k] = k < nk ? __ballot(key[k] >= t) : 0ull;  // nk: slots in use (block-uniform)
     wt += (uint32_t)__popcll(msk[k]);
   }
   uint32_t base = 0;
@@ -561,6 +584,72 @@ __device__ inline void rescore_survivors(const TkShared& sm, int M, const double
 // one block per CU and 1.6x the time.
 enum { TK_EXACT = 0, TK_INTERVAL = 1, TK_FUSED = 2 };
 
+// Mode 2 (exact scores, a unit cut into chunks, the scorer's threshold keys
+// at hand): the chunk's survivors sm.keys/ids[0..M) all reach a bound of the
+// unit's 512th best, so the unit's best 512 lie among the union of every
+// chunk's survivors, and among the best 512 of each chunk's. Each chunk
+// appends those (at most 512) to the unit's list in `partial`, counted in
+// arrivals[nunits + unit]; the last chunk to arrive sorts the list and
+// writes the unit's selection. (The arrival counters are zeroed by the
+// scorer of the same call.)
+__device__ void pool_select_tail(const TkShared& sm, int M, int64_t unit, int nchunks,
+                                 int64_t ncand, unsigned long long* __restrict__ partial,
+                                 unsigned* __restrict__ arrivals, int64_t nunits,
+                                 int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores) {
+  const int tid = threadIdx.x;
+  unsigned long long v = 0ull;
+  const int Mo = M < TK ? M : TK;
+  if (M <= TK) {
+    v = tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull;
+  } else if (M <= TK_SORT) {
+    v = sort_desc<TK_SORT>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
+  } else {
+    collect_best(sm, M, TK);
+    v = tid < TK ? sm.out[tid] : 0ull;
+  }
+  unsigned* const cnt = arrivals + nunits + unit;
+  unsigned long long* const list = partial + unit * (int64_t)nchunks * TK;
+  __shared__ unsigned sh_base;
+  __shared__ int sh_last;
+  if (tid == 0) sh_base = Mo ? atomicAdd(cnt, (unsigned)Mo) : 0u;
+  __syncthreads();
+  // device-scope stores (written through to where every die sees them), each
+  // thread waits for its own, then one arrival per chunk: no release fence,
+  // which would write back the die's whole L2 once per chunk
+  if (tid < Mo)
+    __hip_atomic_store(&list[sh_base + tid], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    sh_last = __hip_atomic_fetch_add(&arrivals[unit], 1u, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT) == (unsigned)nchunks - 1u;
+  __syncthreads();
+  if (!sh_last) return;
+  // every chunk's part is in (read with device-scope loads, which miss the
+  // die's own cache): L >= the unit's K entries, all distinct
+  const int L = (int)__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int K = ncand < TK ? (int)ncand : TK;
+  auto ld = [&](int i) {
+    return __hip_atomic_load(&list[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  unsigned long long w;
+  if (L <= TK) {
+    w = sort_desc<TK>(tid < L ? ld(tid) : 0ull, sm);
+  } else if (L <= TK_SORT) {
+    w = sort_desc<TK_SORT>(tid < L ? ld(tid) : 0ull, sm);
+  } else {
+    for (int i = tid; i < L; i += TK_THREADS) {
+      const unsigned long long c = ld(i);
+      sm.keys[i] = (uint32_t)(c >> 32);
+      sm.ids[i] = (int32_t)~(uint32_t)c;
+    }
+    __syncthreads();
+    collect_best(sm, L, K);
+    w = sort_desc<TK>(tid < K ? sm.out[tid] : 0ull, sm);
+  }
+  write_rank(w, K, unit, sel_ids, sel_scores);
+}
+
 template <int KIND>
 __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_chunk_kernel(
     int mode, const float2* __restrict__ bounds, const uint8_t* __restrict__ q8, int64_t qs8,
@@ -568,8 +657,9 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int64_t B,
     int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
     int64_t w_stride, const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
-    unsigned long long* __restrict__ partial, unsigned* __restrict__ arrivals,
-    int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores, int64_t nunits, AppendArgs ap) {
+    unsigned long long* __restrict__ partial, const uint32_t* __restrict__ pool,
+    unsigned* __restrict__ arrivals, int32_t* __restrict__ sel_ids,
+    float* __restrict__ sel_scores, int64_t nunits, AppendArgs ap) {
   constexpr bool EXACT = KIND == TK_EXACT;
   constexpr bool FUSED = KIND == TK_FUSED;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -585,7 +675,9 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   const int c = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const TkShared sm = carve(smem, (int)chunk);
+  // mode 2 gathers up to nchunks x 512 survivors in the last block's LDS
+  const TkShared sm =
+      carve(smem, (int)(mode == 2 && (int64_t)nchunks * TK > chunk ? (int64_t)nchunks * TK : chunk));
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
   const int64_t j0 = (int64_t)c * chunk;
@@ -600,6 +692,9 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   // the thread's keys (absent candidates 0) and its 4 group maxima
   uint32_t kh[TK_PER];
   uint32_t mx[4] = {0u, 0u, 0u, 0u};
+  // mode 2: maxima of the unit's threshold keys from the scorer, entries
+  // tid + 1024 (s + 4 i) in slot s
+  uint32_t pv[4] = {0u, 0u, 0u, 0u};
   uint32_t* const kl_lds = reinterpret_cast<uint32_t*>(sm.xb);  // fused: lower keys by id
   // fused: upper keys by id, past the selection's LDS
   uint32_t* const kh_lds = reinterpret_cast<uint32_t*>(smem + tk_smem_bytes(FUSED_MAX_N));
@@ -627,8 +722,34 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
         }
       }
     }
+    // the unit's threshold keys, entry 64 wave + lane + 1024 (s + 4 i) in
+    // slot s (coalesced; with at least 4,096 keys every wave gets as many)
+    const int64_t npool = ((R_cap + 255) >> 8) * 8;
+    const uint32_t* const pu = (EXACT && mode == 2) ? pool + unit * npool : nullptr;
+    const int64_t pe0 = tid;
+    if (EXACT && mode == 2) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int64_t e = pe0 + TK_THREADS * s;
+        if (e < npool) pv[s] = pu[e];
+      }
+    }
     unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
     if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
+    if (EXACT && mode == 2) {
+      // only the blocks that hold the row's candidates wrote their keys
+      const int64_t nvalid = ((ncand + 255) >> 8) * 8;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (pe0 + TK_THREADS * s >= nvalid) pv[s] = 0u;
+      for (int64_t e0 = pe0 + 4 * TK_THREADS; e0 < nvalid; e0 += 4 * TK_THREADS) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int64_t e = e0 + TK_THREADS * s;
+          if (e < nvalid) pv[s] = pu[e] > pv[s] ? pu[e] : pv[s];
+        }
+      }
+    }
 #pragma unroll
     for (int k = 0; k < TK_PER; ++k) {
       const bool have = tid + TK_THREADS * k < N;
@@ -639,8 +760,13 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   }
   const int K = N < TK ? N : TK;
   // 1. tau = least over the waves of the wave's 32nd largest group maximum
-  //    (at least 1: absent candidates, key 0, never survive)
-  const uint32_t tw = wave_kth_largest4(mx, TK / TK_WAVES);
+  //    (at least 1: absent candidates, key 0, never survive). Mode 2 takes
+  //    the same bound over the scorer's threshold keys instead: at least 512
+  //    distinct candidates of the whole unit reach it (each slot a maximum
+  //    over disjoint candidates), so the unit's 512th best does too.
+  // (mode 2 takes the pool's bound alone: its chunks are small enough that
+  // their own bound would be far below it)
+  const uint32_t tw = wave_kth_largest4((EXACT && mode == 2) ? pv : mx, TK / TK_WAVES);
   if (lane == 0) sm.misc[wave] = tw;
   if (tid == 0) sm.misc[56] = 0u;
   __syncthreads();
@@ -661,7 +787,8 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   }
   // 2. survivors: upper key >= tau, appended per wave (their order is free:
   //    the selection sorts by (key, id))
-  int M = compact_keys<FUSED>(sm, kh, tau, j0, EXACT);
+  int M = compact_keys<FUSED>(sm, kh, tau, j0, EXACT,
+                             FUSED ? TK_PER : (int)((chunk + TK_THREADS - 1) / TK_THREADS));
   if constexpr (!EXACT) {
     if (M > TK_SORT) {
       // too many to sort directly: cut by T from the lower keys >= tau
@@ -687,6 +814,13 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     // 3. exact scores of the survivors (matrix cores)
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
     rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)seq * ssb + g * 64, wl, tid);
+  }
+  if constexpr (EXACT) {
+    if (mode == 2) {
+      pool_select_tail(sm, M, unit, nchunks, ncand, partial, arrivals, nunits, sel_ids,
+                       sel_scores);
+      return;
+    }
   }
   // 4. exact best K of the survivors (M >= K), sorted: thread t < 512 gets rank t
   unsigned long long v;
@@ -758,7 +892,23 @@ __device__ void merge_lists(const unsigned long long* __restrict__ src, int nchu
 #define S5_TOPK_MIN_CHUNK 16384
 #endif
 
+// exact scores over more than one chunk's worth of candidates: chunks of
+// this many (more when 32 of them do not cover the summary), each keeping
+// only what reaches the scorer's threshold bound
+#ifndef S5_TOPK_POOL_CHUNK
+#define S5_TOPK_POOL_CHUNK 4096
+#endif
+
 TopkPlan topk_plan(int32_t rows, int64_t R_cap) {
+  if (score_exact_mode(rows) && R_cap > TK_MAX_N) {
+    int64_t ch = S5_TOPK_POOL_CHUNK;
+    if (ch * 32 < R_cap) ch = (R_cap + 31) / 32;
+    ch = (ch + 63) / 64 * 64;
+    TopkPlan p;
+    p.chunk = ch;
+    p.nchunks = (int32_t)((R_cap + ch - 1) / ch);
+    return p;
+  }
   // at most 16,384 candidates per chunk; a batch too small to fill the GPU
   // (rows * 4 units) is cut further, into chunks of at least
   // S5_TOPK_MIN_CHUNK, up to 16
@@ -786,6 +936,11 @@ size_t topk_partial_bytes(int32_t rows, int64_t R_cap) {
   return (size_t)rows * 4 * p.nchunks * TK * sizeof(unsigned long long);
 }
 
+size_t topk_pool_bytes(int32_t rows, int64_t R_cap) {
+  if (!score_exact_mode(rows) || topk_plan(rows, R_cap).nchunks <= 1) return 0;
+  return (size_t)rows * 4 * (size_t)((R_cap + 255) / 256) * 8 * sizeof(uint32_t);
+}
+
 // the append's LDS (z and e, e*k of 8 tokens x 32 lanes) fits in every
 // selection launch's dynamic LDS
 static_assert(8 * 32 * 16 + 8 * 32 * 64 <= TK * 8 + 2 * TK_SORT * 8, "append LDS");
@@ -807,32 +962,38 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(topk_chunk_kernel<TK_FUSED>, dim3(units + napp, 1), dim3(TK_THREADS), sm,
                        stream, 0, nullptr, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos,
                        a.B, a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb,
-                       (int64_t)FUSED_MAX_N, 1, a.partial, a.arrivals, a.sel_ids, a.sel_scores,
-                       (int64_t)units, ap);
+                       (int64_t)FUSED_MAX_N, 1, a.partial, nullptr, a.arrivals, a.sel_ids,
+                       a.sel_scores, (int64_t)units, ap);
     return hipGetLastError();
   }
   const TopkPlan p = topk_plan(a.rows, a.R_cap);
+  // mode 0: one chunk per unit; 1: chunk lists merged by the last chunk;
+  // 2 (exact scores with the scorer's threshold keys): survivor lists
+  const int mode = p.nchunks == 1 ? 0 : (a.exact && a.pool ? 2 : 1);
   size_t sm = tk_smem_bytes((int)p.chunk);
-  const size_t sm_merge = (size_t)(p.nchunks + 4) * TK * sizeof(unsigned long long);
-  if (p.nchunks > 1 && sm_merge > sm) sm = sm_merge;
+  if (mode == 1) {
+    const size_t sm_merge = (size_t)(p.nchunks + 4) * TK * sizeof(unsigned long long);
+    if (sm_merge > sm) sm = sm_merge;
+  } else if (mode == 2 && (int64_t)p.nchunks * TK > p.chunk) {
+    sm = tk_smem_bytes(p.nchunks * TK);
+  }
   const void* fn = a.exact ? (const void*)topk_chunk_kernel<TK_EXACT>
                            : (const void*)topk_chunk_kernel<TK_INTERVAL>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
-  const int mode = p.nchunks == 1 ? 0 : 1;
   const dim3 grid(units + napp, (unsigned)p.nchunks);
   if (a.exact)
     hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
-                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores, (int64_t)units,
-                       ap);
+                       p.nchunks, a.partial, a.pool, a.arrivals, a.sel_ids, a.sel_scores,
+                       (int64_t)units, ap);
   else
     hipLaunchKernelGGL(topk_chunk_kernel<TK_INTERVAL>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
-                       p.nchunks, a.partial, a.arrivals, a.sel_ids, a.sel_scores, (int64_t)units,
-                       ap);
+                       p.nchunks, a.partial, nullptr, a.arrivals, a.sel_ids, a.sel_scores,
+                       (int64_t)units, ap);
   return hipGetLastError();
 }
 

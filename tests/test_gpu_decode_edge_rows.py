@@ -76,3 +76,31 @@ def test_decode_select_tie_heavy_16_rows_16384_regions():
     ex = P.compare_selection(ids.cpu().numpy(), sc.cpu().numpy(), osc,
                              d["row_pos"].cpu().numpy(), exact=True)
     assert ex == 0
+
+
+@pytest.mark.parametrize("R", [16384, 40000])
+def test_decode_select_zero_score_ties(R):
+    """Many candidates tie at the 512th score: candidates whose dots are all
+    negative score exactly 0 after relu. Rows with 400 positive scores among
+    2,000 candidates, none among all R, and 600 among all R: more than 1,024
+    candidates reach the threshold, and the 0-score ties must go by smaller
+    id (one selection chunk at 16,384 regions, several at 40,000)."""
+    g = torch.Generator().manual_seed(12)
+    npos = [(2000, 400), (R - 1, 0), (R - 1, 600)]
+    rows = len(npos)
+    S = (0x81 + torch.randint(0, 0x7E - 0x00, (rows, R, 4, 64), generator=g)).to(torch.uint8)
+    for r, (nc, npositive) in enumerate(npos):
+        pick = torch.randperm(nc, generator=g)[:npositive]
+        S[r, pick] = (1 + torch.randint(0, 0x7E, (npositive, 4, 64), generator=g)).to(torch.uint8)
+    d = {"rows": rows, "q8": torch.full((rows, 16, 64), 0x38, dtype=torch.uint8).to(DEV),
+         "w_head": (torch.rand(16, generator=g) + 0.5).to(DEV),
+         "row_seq": torch.arange(rows, dtype=torch.int32, device=DEV),
+         "row_pos": torch.tensor([8 * nc + 7 for nc, _ in npos], dtype=torch.int64, device=DEV)}
+    S = S.to(DEV)
+    P.say(f"[case] decode select, zero-score ties: {rows} rows over {R} regions")
+    ids, sc = P.gpu_select(d, S)
+    torch.cuda.synchronize()
+    osc = P.oracle_scores(d, P.host8(S), list(range(rows)))
+    ex = P.compare_selection(ids.cpu().numpy(), sc.cpu().numpy(), osc,
+                             d["row_pos"].cpu().numpy(), exact=True)
+    assert ex == 0

@@ -338,15 +338,16 @@ __global__ __launch_bounds__(256) void score_kernel(
 // for the selection's threshold: each the best score key among 32 of its
 // candidates (lanes 4g + j and 4g + (j ^ 1) of a wave), 0 where none.
 // ---------------------------------------------------------------------------
-constexpr int SM_CB = 256;  // candidates per block
-
-template <bool PREPARED>
+// NQ quads of 4 candidates per wave: 16 (256 candidates per block), or 8
+// (128) when a batch has too few rows for 1,024 blocks of 256
+template <bool PREPARED, int NQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_exact_mfma_kernel(
     const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
     const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
     int64_t ssb, int64_t pos_limit, float* __restrict__ scores, uint32_t* __restrict__ pool,
     QPrepArgs prep) {
   __shared__ __align__(16) uint8_t q_lds[16 * 64];
+  constexpr int CW = 4 * NQ, CB = 4 * CW;  // candidates per wave, per block
   __shared__ uint32_t pmax[4][8];  // pool: the best key of each 32 candidates (see below)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (threadIdx.x < 32) pmax[threadIdx.x >> 3][threadIdx.x & 7] = 0u;
@@ -361,10 +362,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     prep.arrivals[row * 4 + threadIdx.x] = 0u;
     prep.arrivals[(int64_t)prep.rows * 4 + row * 4 + threadIdx.x] = 0u;
   }
-  if ((int64_t)blockIdx.x * SM_CB >= nc) return;  // block-uniform
-  const int64_t cb0 = (int64_t)blockIdx.x * SM_CB + 64 * wave;
+  if ((int64_t)blockIdx.x * CB >= nc) return;  // block-uniform
+  const int64_t cb0 = (int64_t)blockIdx.x * CB + CW * wave;
   const bool live = cb0 < nc;
-  const int64_t jend = live ? (cb0 + 64 < nc ? cb0 + 64 : nc) : 0;
+  const int64_t jend = live ? (cb0 + CW < nc ? cb0 + CW : nc) : 0;
   // The query prep's loads go out first (every wave loads the heads of wave
   // & 1, waves 0 and 1 store the result), then the summary loads, so that
   // the prep waits for its own loads only.
@@ -402,13 +403,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   if (wave < 2) *reinterpret_cast<uint2*>(&q_lds[ph * 64 + pc * 8]) = pk;
   __syncthreads();
-  // pool: per (row, group) and block, 8 keys, entry 2 * wave + p the best
-  // key among the 32 candidates of lanes 4g + 2p and 4g + 2p + 1 (0 if
-  // none), gathered by LDS atomic max in pmax[wave][2g + p] (lane >> 1)
+  // pool: per (row, group), one key per 32 candidates, the best (0 if none),
+  // gathered by LDS atomic max. NQ = 16: entry 8 b + 2 wave + p from lanes
+  // 4g + 2p and 4g + 2p + 1 (pmax[wave][2g + p]); NQ = 8: entry 4 b + wave
+  // from the group's 4 lanes (pmax[wave][g]). A unit's keys start every
+  // 8 * ceil(R_cap / 256) entries.
+  constexpr int PSH = NQ == 16 ? 1 : 2;  // lane >> PSH: the lane's pmax slot
   auto pool_put = [&]() {
-    if (lane < 8)
-      pool[((row * 4 + (lane >> 1)) * (int64_t)gridDim.x + blockIdx.x) * 8 + 2 * wave +
-           (lane & 1)] = pmax[wave][lane];
+    const int64_t ustride = ((R_cap + 255) >> 8) * 8;
+    if (NQ == 16 && lane < 8)
+      pool[(row * 4 + (lane >> 1)) * ustride + 8 * (int64_t)blockIdx.x + 2 * wave + (lane & 1)] =
+          pmax[wave][lane];
+    if (NQ == 8 && lane < 4)
+      pool[(row * 4 + lane) * ustride + 4 * (int64_t)blockIdx.x + wave] = pmax[wave][lane];
   };
   if (!live) {
     if (pool) pool_put();
@@ -458,31 +465,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const int64_t j = cb0 + 4 * (u0 + q) + ij;
       if (lane < 16 && j < jend) {
         out_g[j] = sc;
-        if (pool) atomicMax(&pmax[wave][lane >> 1], ord_key(sc));
+        if (pool) atomicMax(&pmax[wave][lane >> PSH], ord_key(sc));
       }
     }
   };
-  load4(8, bC);
-  quads4(0, bA);
-  load4(12, bA);
-  quads4(4, bB);
-  quads4(8, bC);
-  quads4(12, bA);
+  if constexpr (NQ == 16) {
+    load4(8, bC);
+    quads4(0, bA);
+    load4(12, bA);
+    quads4(4, bB);
+    quads4(8, bC);
+    quads4(12, bA);
+  } else {
+    quads4(0, bA);
+    quads4(4, bB);
+  }
   if (pool) pool_put();  // the wave's own LDS atomics precede its reads
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
   if (a.rows == 0 || a.R_cap == 0) return hipSuccess;
   if (a.exact) {
-    const dim3 grid((unsigned)((a.R_cap + SM_CB - 1) / SM_CB), (unsigned)a.rows);
-    if (a.prep.prepared)
-      hipLaunchKernelGGL(score_exact_mfma_kernel<true>, grid, dim3(256), 0, stream, a.w_head,
-                         a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.pool, a.prep);
-    else
-      hipLaunchKernelGGL(score_exact_mfma_kernel<false>, grid, dim3(256), 0, stream, a.w_head,
-                         a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B, a.R_cap, a.ssb,
-                         a.pos_limit, reinterpret_cast<float*>(a.bounds), a.pool, a.prep);
+    // half-size blocks when 256-candidate blocks would not reach 1,024
+    const bool half = (int64_t)a.rows * ((a.R_cap + 255) / 256) < 1024;
+    const int64_t cb = half ? 128 : 256;
+    const dim3 grid((unsigned)((a.R_cap + cb - 1) / cb), (unsigned)a.rows);
+    float* const sc = reinterpret_cast<float*>(a.bounds);
+    if (a.prep.prepared) {
+      if (half)
+        hipLaunchKernelGGL((score_exact_mfma_kernel<true, 8>), grid, dim3(256), 0, stream,
+                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
+                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
+      else
+        hipLaunchKernelGGL((score_exact_mfma_kernel<true, 16>), grid, dim3(256), 0, stream,
+                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
+                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
+    } else {
+      if (half)
+        hipLaunchKernelGGL((score_exact_mfma_kernel<false, 8>), grid, dim3(256), 0, stream,
+                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
+                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
+      else
+        hipLaunchKernelGGL((score_exact_mfma_kernel<false, 16>), grid, dim3(256), 0, stream,
+                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
+                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
+    }
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((a.R_cap + SC_CB - 1) / SC_CB), (unsigned)((a.rows + 3) / 4));

@@ -737,8 +737,9 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
     if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
     if (EXACT && mode == 2) {
-      // only the blocks that hold the row's candidates wrote their keys
-      const int64_t nvalid = ((ncand + 255) >> 8) * 8;
+      // keys of the first ceil(ncand / 32) entries were written by this call
+      // (one per 32 candidates, 0 for those with none)
+      const int64_t nvalid = (ncand + 31) >> 5;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         if (pe0 + TK_THREADS * s >= nvalid) pv[s] = 0u;

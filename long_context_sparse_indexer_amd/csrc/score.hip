@@ -339,8 +339,9 @@ __global__ __launch_bounds__(256) void score_kernel(
 // candidates (lanes 4g + j and 4g + (j ^ 1) of a wave), 0 where none.
 // ---------------------------------------------------------------------------
 // NQ quads of 4 candidates per wave: 16 (256 candidates per block), or 8
-// (128) when a batch has too few rows for 1,024 blocks of 256
-template <bool PREPARED, int NQ>
+// (128) when a batch has too few rows for 1,024 blocks of 256; POOL: `pool`
+// is given (the threshold keys are written)
+template <bool PREPARED, int NQ, bool POOL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) void score_exact_mfma_kernel(
     const float* __restrict__ w_head, int64_t w_stride, const int32_t* __restrict__ row_seq,
     const int64_t* __restrict__ row_pos, const uint8_t* __restrict__ S, int64_t B, int64_t R_cap,
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       pool[(row * 4 + lane) * ustride + 4 * (int64_t)blockIdx.x + wave] = pmax[wave][lane];
   };
   if (!live) {
-    if (pool) pool_put();
+    if (POOL) pool_put();
     return;
   }
   // A operand: head 4g + ij, dims 16k..16k+15 as packed e4m3, converted per use
@@ -465,7 +466,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       const int64_t j = cb0 + 4 * (u0 + q) + ij;
       if (lane < 16 && j < jend) {
         out_g[j] = sc;
-        if (pool) atomicMax(&pmax[wave][lane >> PSH], ord_key(sc));
+        if (POOL) atomicMax(&pmax[wave][lane >> PSH], ord_key(sc));
       }
     }
   };
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     quads4(0, bA);
     quads4(4, bB);
   }
-  if (pool) pool_put();  // the wave's own LDS atomics precede its reads
+  if (POOL) pool_put();  // the wave's own LDS atomics precede its reads
 }
 
 hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
@@ -491,24 +492,18 @@ hipError_t launch_score(const ScoreArgs& a, hipStream_t stream) {
     const int64_t cb = half ? 128 : 256;
     const dim3 grid((unsigned)((a.R_cap + cb - 1) / cb), (unsigned)a.rows);
     float* const sc = reinterpret_cast<float*>(a.bounds);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a.w_head, a.w_stride_row, a.row_seq,
+                         a.row_pos, a.summary, a.B, a.R_cap, a.ssb, a.pos_limit, sc, a.pool,
+                         a.prep);
+    };
+    const bool pl = a.pool != nullptr;
     if (a.prep.prepared) {
-      if (half)
-        hipLaunchKernelGGL((score_exact_mfma_kernel<true, 8>), grid, dim3(256), 0, stream,
-                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
-                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
-      else
-        hipLaunchKernelGGL((score_exact_mfma_kernel<true, 16>), grid, dim3(256), 0, stream,
-                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
-                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
+      if (half) pl ? go(score_exact_mfma_kernel<true, 8, true>) : go(score_exact_mfma_kernel<true, 8, false>);
+      else pl ? go(score_exact_mfma_kernel<true, 16, true>) : go(score_exact_mfma_kernel<true, 16, false>);
     } else {
-      if (half)
-        hipLaunchKernelGGL((score_exact_mfma_kernel<false, 8>), grid, dim3(256), 0, stream,
-                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
-                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
-      else
-        hipLaunchKernelGGL((score_exact_mfma_kernel<false, 16>), grid, dim3(256), 0, stream,
-                           a.w_head, a.w_stride_row, a.row_seq, a.row_pos, a.summary, a.B,
-                           a.R_cap, a.ssb, a.pos_limit, sc, a.pool, a.prep);
+      if (half) pl ? go(score_exact_mfma_kernel<false, 8, true>) : go(score_exact_mfma_kernel<false, 8, false>);
+      else pl ? go(score_exact_mfma_kernel<false, 16, true>) : go(score_exact_mfma_kernel<false, 16, false>);
     }
     return hipGetLastError();
   }

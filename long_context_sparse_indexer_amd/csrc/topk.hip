@@ -577,12 +577,16 @@ __device__ inline void rescore_survivors(const TkShared& sm, int M, const double
 // output; mode 1: partial list, merged by the unit's last block.
 // KIND: TK_EXACT reads exact scores from `bounds` (as float), TK_INTERVAL
 // reads intervals, TK_FUSED computes the intervals itself (fused_intervals;
-// one chunk of at most FUSED_MAX_N candidates) from q8 (row stride qs8).
+// one chunk of at most FUSED_MAX_N candidates) from q8 (row stride qs8),
+// TK_POOLED reads exact scores and the scorer's threshold keys (`pool`)
+// and appends survivors to the unit's list (pool_select_tail; mode 2). The
+// pooled path is its own instance so that the one-chunk kernel carries
+// none of its code.
 // Registers are capped for 8 waves per SIMD, so that two 1024-thread blocks
 // share a CU when the chunk's LDS allows it (prefill-sized chunks of 4,096
 // candidates): uncapped, the interval variant's scalar registers held it to
 // one block per CU and 1.6x the time.
-enum { TK_EXACT = 0, TK_INTERVAL = 1, TK_FUSED = 2 };
+enum { TK_EXACT = 0, TK_INTERVAL = 1, TK_FUSED = 2, TK_POOLED = 3 };
 
 // Mode 2 (exact scores, a unit cut into chunks, the scorer's threshold keys
 // at hand): the chunk's survivors sm.keys/ids[0..M) all reach a bound of the
@@ -660,7 +664,8 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     unsigned long long* __restrict__ partial, const uint32_t* __restrict__ pool,
     unsigned* __restrict__ arrivals, int32_t* __restrict__ sel_ids,
     float* __restrict__ sel_scores, int64_t nunits, AppendArgs ap) {
-  constexpr bool EXACT = KIND == TK_EXACT;
+  constexpr bool POOLED = KIND == TK_POOLED;
+  constexpr bool EXACT = KIND == TK_EXACT || POOLED;
   constexpr bool FUSED = KIND == TK_FUSED;
   extern __shared__ __align__(16) unsigned char smem[];
   if ((int64_t)blockIdx.x >= nunits) {
@@ -677,7 +682,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // mode 2 gathers up to nchunks x 512 survivors in the last block's LDS
   const TkShared sm =
-      carve(smem, (int)(mode == 2 && (int64_t)nchunks * TK > chunk ? (int64_t)nchunks * TK : chunk));
+      carve(smem, (int)(POOLED && (int64_t)nchunks * TK > chunk ? (int64_t)nchunks * TK : chunk));
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
   const int64_t j0 = (int64_t)c * chunk;
@@ -725,9 +730,9 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     // the unit's threshold keys, entry 64 wave + lane + 1024 (s + 4 i) in
     // slot s (coalesced; with at least 4,096 keys every wave gets as many)
     const int64_t npool = ((R_cap + 255) >> 8) * 8;
-    const uint32_t* const pu = (EXACT && mode == 2) ? pool + unit * npool : nullptr;
+    const uint32_t* const pu = POOLED ? pool + unit * npool : nullptr;
     const int64_t pe0 = tid;
-    if (EXACT && mode == 2) {
+    if constexpr (POOLED) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int64_t e = pe0 + TK_THREADS * s;
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     }
     unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
     if (j0 < ncand) N = (int)((ncand - j0 < chunk) ? ncand - j0 : chunk);
-    if (EXACT && mode == 2) {
+    if constexpr (POOLED) {
       // keys of the first ceil(ncand / 32) entries were written by this call
       // (one per 32 candidates, 0 for those with none)
       const int64_t nvalid = (ncand + 31) >> 5;
@@ -767,7 +772,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   //    over disjoint candidates), so the unit's 512th best does too.
   // (mode 2 takes the pool's bound alone: its chunks are small enough that
   // their own bound would be far below it)
-  const uint32_t tw = wave_kth_largest4((EXACT && mode == 2) ? pv : mx, TK / TK_WAVES);
+  const uint32_t tw = wave_kth_largest4(POOLED ? pv : mx, TK / TK_WAVES);
   if (lane == 0) sm.misc[wave] = tw;
   if (tid == 0) sm.misc[56] = 0u;
   __syncthreads();
@@ -789,7 +794,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   // 2. survivors: upper key >= tau, appended per wave (their order is free:
   //    the selection sorts by (key, id))
   int M = compact_keys<FUSED>(sm, kh, tau, j0, EXACT,
-                             FUSED ? TK_PER : (int)((chunk + TK_THREADS - 1) / TK_THREADS));
+                              POOLED ? (int)((chunk + TK_THREADS - 1) / TK_THREADS) : TK_PER);
   if constexpr (!EXACT) {
     if (M > TK_SORT) {
       // too many to sort directly: cut by T from the lower keys >= tau
@@ -816,12 +821,10 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
     rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)seq * ssb + g * 64, wl, tid);
   }
-  if constexpr (EXACT) {
-    if (mode == 2) {
-      pool_select_tail(sm, M, unit, nchunks, ncand, partial, arrivals, nunits, sel_ids,
-                       sel_scores);
-      return;
-    }
+  if constexpr (POOLED) {
+    pool_select_tail(sm, M, unit, nchunks, ncand, partial, arrivals, nunits, sel_ids,
+                     sel_scores);
+    return;
   }
   // 4. exact best K of the survivors (M >= K), sorted: thread t < 512 gets rank t
   unsigned long long v;
@@ -978,16 +981,23 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   } else if (mode == 2 && (int64_t)p.nchunks * TK > p.chunk) {
     sm = tk_smem_bytes(p.nchunks * TK);
   }
-  const void* fn = a.exact ? (const void*)topk_chunk_kernel<TK_EXACT>
-                           : (const void*)topk_chunk_kernel<TK_INTERVAL>;
+  const void* fn = mode == 2  ? (const void*)topk_chunk_kernel<TK_POOLED>
+                   : a.exact ? (const void*)topk_chunk_kernel<TK_EXACT>
+                             : (const void*)topk_chunk_kernel<TK_INTERVAL>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
   if (e != hipSuccess) return e;
   const dim3 grid(units + napp, (unsigned)p.nchunks);
-  if (a.exact)
-    hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
+  if (mode == 2)
+    hipLaunchKernelGGL(topk_chunk_kernel<TK_POOLED>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
                        p.nchunks, a.partial, a.pool, a.arrivals, a.sel_ids, a.sel_scores,
+                       (int64_t)units, ap);
+  else if (a.exact)
+    hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
+                       a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
+                       p.nchunks, a.partial, nullptr, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);
   else
     hipLaunchKernelGGL(topk_chunk_kernel<TK_INTERVAL>, grid, dim3(TK_THREADS), sm, stream, mode,

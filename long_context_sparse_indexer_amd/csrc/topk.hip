@@ -401,83 +401,17 @@ __device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int
   if ((int)threadIdx.x < TK) write_rank_at(v, threadIdx.x, K, unit, sel_ids, sel_scores);
 }
 
-// ---------------------------------------------------------------------------
-// Fused intervals (prefill-sized units, up to FUSED_MAX_N candidates): the
-// workgroup of a (row, group) computes its candidates' score intervals on
-// the bf16 matrix cores instead of reading them from memory. A = the row's 4
-// query heads of the group (MFMA rows 0..3, the rest zero), B = 16
-// candidates; output lane n (of the first 16) then holds the 4 head dots of
-// column n, and its interval. Tile t of wave w covers candidates
-// 256 t + 16 w + n: the waves interleave, so that with at least 512
-// candidates every wave holds 32 groups (lane, t mod 4) with one, as the
-// threshold step needs. Keys stay in lanes 0..15, 16 per lane.
-// ---------------------------------------------------------------------------
+// Units of the fused interval selection hold at most this many candidates
+// (summaries of up to 4,096 regions; topk_fused4_kernel below).
 constexpr int FUSED_MAX_N = 16 * TK_WAVES * TK_PER;  // 4,096
 
 // dword 3 of a raw buffer resource for 32-bit offsets (as attn_tile.hip's)
 constexpr int FK_RSRC3 = 0x00020000;
 
-__device__ inline int32_t fused_id(int tid, int k) {
-  return 256 * k + 16 * (tid >> 6) + (tid & 15);
-}
-
-// The keys of the thread's candidates fused_id(tid, t): upper and lower key
-// in kh[j] and kl[j] (LDS, by candidate id j; absent ones 0); mx gets the
-// thread's 4 group maxima of lower keys. The keys go to LDS rather than
-// registers (only lanes 0..15 hold any), so that four tiles fit in flight per
-// round trip to L2 within the selection's 64-register cap. q8r: the row's
-// prepared query [16 heads][64]; Sg: the sequence's summary at group g
-// (candidate stride 256 B); N >= 1 candidates.
-__device__ inline void fused_keys(uint32_t* kh, uint32_t (&mx)[4], uint32_t* kl,
-                                  const uint8_t* __restrict__ q8r, const uint8_t* __restrict__ Sg,
-                                  int g, int N, const float* w4, int tid) {
-  const int lane = tid & 63, n = lane & 15, qd = lane >> 4;
-  const int wave = tid >> 6;
-  // the query stays packed (widened per tile)
-  uint4 araw = n < 4 ? ldg16(q8r + (4 * g + n) * 64 + 16 * qd) : make_uint4(0, 0, 0, 0);
-  const uint32_t jmax = (uint32_t)(N - 1);
-  // summary loads through a buffer resource over the N candidates (a scalar
-  // base and a 32-bit offset per lane: no 64-bit address per lane to keep)
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)Sg, (short)0, (int)((uint32_t)N * 256u), FK_RSRC3);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mx[i] = 0u;
-#pragma unroll
-  for (int b = 0; b < TK_PER / 4; ++b) {
-    if (4 * 256 * b >= N) break;  // block-uniform
-    // re-widened every four tiles, not hoisted out of the loop
-    asm volatile("" : "+v"(araw.x), "+v"(araw.y), "+v"(araw.z), "+v"(araw.w));
-    uint4 bq[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t j = min((uint32_t)(256 * (4 * b + u) + 16 * wave + n), jmax);
-      bq[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            rs, (int)(j * 256u + 16 * qd), 0, 0));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = 4 * b + u;
-      f32x4 d, a;
-      dot64(widen16(araw), widen16(bq[u]), d, a);
-      const float2 iv = score_interval(d, a, w4);
-      const int j = 256 * t + 16 * wave + n;
-      const bool ok = qd == 0 && j < N;
-      const uint32_t lo = ok ? ord_key(iv.x) : 0u;
-      mx[u] = lo > mx[u] ? lo : mx[u];
-      if (ok) {
-        kl[j] = lo;
-        kh[j] = ord_key(iv.y);
-      }
-    }
-  }
-}
-
 // Appends the candidates whose key reaches t to sm.ids (and, with keys, the
 // key to sm.keys), per wave in ballot order; misc[56] holds the count, zero
 // on entry. Returns the total (a barrier comes first). Key k of thread tid is
-// candidate j0 + tid + 1024 k, or with FUSED the candidate fused_id gives;
-// slots k >= nk are not looked at.
-template <bool FUSED = false>
+// candidate j0 + tid + 1024 k; slots k >= nk are not looked at.
 __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_PER], uint32_t t,
                                    int64_t j0, bool keys, int nk = TK_PER) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -496,7 +430,7 @@ __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_
     if (msk[k]) {
       if (lane_in(msk[k])) {
         const uint32_t pos = base + lanes_below(msk[k]);
-        sm.ids[pos] = FUSED ? fused_id(tid, k) : (int32_t)(j0 + tid + TK_THREADS * k);
+        sm.ids[pos] = (int32_t)(j0 + tid + TK_THREADS * k);
         if (keys) sm.keys[pos] = key[k];
       }
       base += (uint32_t)__popcll(msk[k]);
@@ -576,8 +510,7 @@ __device__ inline void rescore_survivors(const TkShared& sm, int M, const double
 // rescoring (intervals), exact selection. mode 0: the whole range, final
 // output; mode 1: partial list, merged by the unit's last block.
 // KIND: TK_EXACT reads exact scores from `bounds` (as float), TK_INTERVAL
-// reads intervals, TK_FUSED computes the intervals itself (fused_intervals;
-// one chunk of at most FUSED_MAX_N candidates) from q8 (row stride qs8),
+// reads intervals (the fused interval selection is topk_fused4_kernel),
 // TK_POOLED reads exact scores and the scorer's threshold keys (`pool`)
 // and appends survivors to the unit's list (pool_select_tail; mode 2). The
 // pooled path is its own instance so that the one-chunk kernel carries
@@ -586,7 +519,7 @@ __device__ inline void rescore_survivors(const TkShared& sm, int M, const double
 // share a CU when the chunk's LDS allows it (prefill-sized chunks of 4,096
 // candidates): uncapped, the interval variant's scalar registers held it to
 // one block per CU and 1.6x the time.
-enum { TK_EXACT = 0, TK_INTERVAL = 1, TK_FUSED = 2, TK_POOLED = 3 };
+enum { TK_EXACT = 0, TK_INTERVAL = 1, TK_POOLED = 3 };
 
 // Mode 2 (exact scores, a unit cut into chunks, the scorer's threshold keys
 // at hand): the chunk's survivors sm.keys/ids[0..M) all reach a bound of the
@@ -656,8 +589,7 @@ __device__ void pool_select_tail(const TkShared& sm, int M, int64_t unit, int nc
 
 template <int KIND>
 __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_chunk_kernel(
-    int mode, const float2* __restrict__ bounds, const uint8_t* __restrict__ q8, int64_t qs8,
-    int64_t R_cap,
+    int mode, const float2* __restrict__ bounds, int64_t R_cap,
     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int64_t B,
     int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
     int64_t w_stride, const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
@@ -666,7 +598,6 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     float* __restrict__ sel_scores, int64_t nunits, AppendArgs ap) {
   constexpr bool POOLED = KIND == TK_POOLED;
   constexpr bool EXACT = KIND == TK_EXACT || POOLED;
-  constexpr bool FUSED = KIND == TK_FUSED;
   extern __shared__ __align__(16) unsigned char smem[];
   if ((int64_t)blockIdx.x >= nunits) {
     // workgroups past the units: the cache append of one decode row each
@@ -686,7 +617,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   const int64_t row = unit >> 2;
   const int g = (int)(unit & 3);
   const int64_t j0 = (int64_t)c * chunk;
-  // keys of candidates tid + 1024 k (fused: fused_id) in registers. The
+  // keys of candidates tid + 1024 k in registers. The
   // chunk's slots of the score buffer are read before the row's candidate
   // count is known (it only masks them), all loads in flight at once; a lane
   // past the chunk's end reads its last slot again.
@@ -700,19 +631,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   // mode 2: maxima of the unit's threshold keys from the scorer, entries
   // tid + 1024 (s + 4 i) in slot s
   uint32_t pv[4] = {0u, 0u, 0u, 0u};
-  uint32_t* const kl_lds = reinterpret_cast<uint32_t*>(sm.xb);  // fused: lower keys by id
-  // fused: upper keys by id, past the selection's LDS
-  uint32_t* const kh_lds = reinterpret_cast<uint32_t*>(smem + tk_smem_bytes(FUSED_MAX_N));
-  if constexpr (FUSED) {
-    unit_row(row_seq, row_pos, B, R_cap, pos_limit, row, &seq, &ncand);
-    N = (int)(ncand < FUSED_MAX_N ? ncand : FUSED_MAX_N);
-    float w4[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w4[i] = w_head[row * w_stride + 4 * g + i];
-    if (N > 0)  // block-uniform
-      fused_keys(kh_lds, mx, kl_lds, q8 + row * qs8, S + (int64_t)seq * ssb + g * 64, g, N, w4,
-                 tid);
-  } else {
+  {
     const int nslot = (int)((R_cap - j0 < chunk) ? R_cap - j0 : chunk);
 #pragma unroll
     for (int k = 0; k < TK_PER; ++k) {
@@ -783,39 +702,26 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     for (int w = 1; w < TK_WAVES; ++w) t = min(t, sm.misc[w]);
     tau = t > 1u ? t : 1u;
   }
-  if constexpr (FUSED) {
-    // the thread's own upper keys back from LDS (it wrote them itself)
-#pragma unroll
-    for (int k = 0; k < TK_PER; ++k) {
-      const int j = fused_id(tid, k);
-      kh[k] = (lane < 16 && j < N) ? kh_lds[j] : 0u;
-    }
-  }
   // 2. survivors: upper key >= tau, appended per wave (their order is free:
   //    the selection sorts by (key, id))
-  int M = compact_keys<FUSED>(sm, kh, tau, j0, EXACT,
-                              POOLED ? (int)((chunk + TK_THREADS - 1) / TK_THREADS) : TK_PER);
+  int M = compact_keys(sm, kh, tau, j0, EXACT,
+                       POOLED ? (int)((chunk + TK_THREADS - 1) / TK_THREADS) : TK_PER);
   if constexpr (!EXACT) {
     if (M > TK_SORT) {
       // too many to sort directly: cut by T from the lower keys >= tau
       uint32_t kl[TK_PER];
 #pragma unroll
       for (int k = 0; k < TK_PER; ++k) {
-        if constexpr (FUSED) {
-          const int j = fused_id(tid, k);
-          kl[k] = (lane < 16 && j < N) ? kl_lds[j] : 0u;
-        } else {
-          kl[k] = tid + TK_THREADS * k < N ? ord_key(raw[k].x) : 0u;
-        }
+        kl[k] = tid + TK_THREADS * k < N ? ord_key(raw[k].x) : 0u;
       }
       if (tid == 0) sm.misc[56] = 0u;
       __syncthreads();
-      M = compact_keys<FUSED>(sm, kl, tau, j0, true);
+      M = compact_keys(sm, kl, tau, j0, true);
       const Boundary bd = radix_boundary(sm, M, K, 2);
       const uint32_t T = bd.P > 1u ? bd.P : 1u;
       if (tid == 0) sm.misc[56] = 0u;
       __syncthreads();
-      M = compact_keys<FUSED>(sm, kh, T, j0, false);
+      M = compact_keys(sm, kh, T, j0, false);
     }
     // 3. exact scores of the survivors (matrix cores)
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
@@ -844,6 +750,206 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
   if (!block_arrive_last(&arrivals[unit], (unsigned)nchunks, &sh_last)) return;
   merge_lists(partial + unit * (int64_t)nchunks * TK, nchunks, ncand, unit, smem, sel_ids,
               sel_scores);
+}
+
+// ---------------------------------------------------------------------------
+// Fused intervals for four rows at once (prefill chunks): one workgroup per
+// 4 consecutive rows and KV group g. When the rows share a sequence, the
+// interval MFMA takes A = the 4 rows x the group's 4 heads (every MFMA row
+// used) and B = 16 candidates, so each summary tile loaded serves all four
+// rows; rows of different sequences get a pass each (A = one row's heads).
+// Lane (n, qd) of the output then holds row qd's 4 head dots of candidate n
+// and makes its interval. The intervals go to LDS as 16-bit key prefixes,
+// rounded outward (lower key down to its prefix, upper key up to the
+// prefix's last value), which keeps every bound below valid: the threshold
+// is taken at 16-bit resolution anyway. Then the four units are selected
+// one after another by the whole workgroup, 4 candidates a thread
+// (t + 1024 k): threshold, survivors, the cut when more than 1,024 survive,
+// exact rescoring and the sort, as in topk_chunk_kernel. One workgroup per
+// CU (64 KB of keys beside the selection's LDS), so the register cap is
+// that of 4 waves per SIMD.
+// ---------------------------------------------------------------------------
+constexpr int F4_KEYS = 4 * FUSED_MAX_N;  // u16 prefixes per array (4 rows)
+
+// element i of a 4-array, i known only at run time (no dynamic indexing of
+// a private array, which would go to scratch)
+template <typename T>
+__device__ inline T sel4(int i, T a, T b, T c, T d) {
+  return i < 2 ? (i == 0 ? a : b) : (i == 2 ? c : d);
+}
+
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void
+topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
+                   const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
+                   int64_t B, int64_t pos_limit, const double* __restrict__ q64,
+                   const float* __restrict__ w_head, int64_t w_stride,
+                   const uint8_t* __restrict__ S, int64_t ssb, int32_t rows, int64_t nwg,
+                   int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores, AppendArgs ap) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if ((int64_t)blockIdx.x >= nwg) {
+    // workgroups past the units: the cache append of one decode row each
+    append_row_block(ap, (int64_t)blockIdx.x - nwg, reinterpret_cast<uint4(*)[32]>(smem),
+                     reinterpret_cast<float4(*)[32][4]>(smem + 8 * 32 * 16));
+    return;
+  }
+  const int64_t r0 = (blockIdx.x >> 2) * 4;
+  const int g = (int)(blockIdx.x & 3);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, qd = lane >> 4;
+  const TkShared sm = carve(smem, FUSED_MAX_N);
+  uint16_t* const kl16 = reinterpret_cast<uint16_t*>(smem + tk_smem_bytes(FUSED_MAX_N));
+  uint16_t* const kh16 = kl16 + F4_KEYS;
+  // the four rows (uniform): sequence (-1: no row / invalid) and candidates
+  int32_t sq0, sq1, sq2, sq3;
+  int64_t nc0, nc1, nc2, nc3;
+  auto row_of = [&](int i, int32_t& si, int64_t& ni) {
+    si = -1;
+    ni = 0;
+    if (r0 + i < rows) unit_row(row_seq, row_pos, B, R_cap, pos_limit, r0 + i, &si, &ni);
+    if (ni > FUSED_MAX_N) ni = FUSED_MAX_N;  // (R_cap <= FUSED_MAX_N on this path)
+  };
+  row_of(0, sq0, nc0);
+  row_of(1, sq1, nc1);
+  row_of(2, sq2, nc2);
+  row_of(3, sq3, nc3);
+  auto SQ = [&](int i) { return sel4(i, sq0, sq1, sq2, sq3); };
+  auto NC = [&](int i) { return sel4(i, nc0, nc1, nc2, nc3); };
+  int32_t s0 = -1;
+  bool shared = true;
+  int nmax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t si = SQ(i);
+    const int64_t ni = NC(i);
+    if (si < 0 || ni == 0) continue;
+    if (s0 < 0) s0 = si;
+    shared = shared && si == s0;
+    nmax = max(nmax, (int)ni);
+  }
+  // this lane's output row qd: its weights and candidate count
+  float w4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w4[i] = r0 + qd < rows ? w_head[(r0 + qd) * w_stride + 4 * g + i] : 0.f;
+  // ---- intervals: one pass for rows sharing a sequence, else a pass per row
+  const int npass = shared ? (s0 >= 0 ? 1 : 0) : 4;
+  for (int ps = 0; ps < npass; ++ps) {
+    const int prow = shared ? -1 : ps;  // the pass's row (per-row passes)
+    const int32_t pseq = shared ? s0 : SQ(ps);
+    const int pn = shared ? nmax : (int)NC(ps);
+    if (pseq < 0 || pn == 0) continue;  // uniform
+    // A: MFMA row n = 4 rl + h (shared) or h = n < 4 of the pass's row
+    const int arow = shared ? (n >> 2) : prow;
+    const int ah = shared ? (n & 3) : n;
+    uint4 araw = make_uint4(0, 0, 0, 0);
+    if (ah < 4 && SQ(arow) >= 0 && NC(arow) > 0)
+      araw = ldg16(q8 + (r0 + arow) * qs8 + (4 * g + ah) * 64 + 16 * qd);
+    const Bf16x16 aq = widen16(araw);
+    // output row of this lane's D, and whether the lane holds one
+    const int orow = shared ? qd : prow;
+    const bool olane = shared || qd == 0;
+    float wo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wo[i] = shared ? w4[i] : w_head[(r0 + prow) * w_stride + 4 * g + i];
+    const int on = (int)NC(orow);
+    const uint8_t* Sg = S + (int64_t)pseq * ssb + g * 64;
+    const uint32_t jmax = (uint32_t)(pn - 1);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)Sg, (short)0, (int)((uint32_t)pn * 256u), FK_RSRC3);
+    // tile t of wave w: candidates 256 t + 16 w + n; 8 tiles per round trip
+#pragma unroll 1
+    for (int b = 0; b < FUSED_MAX_N / 256; b += 8) {
+      if (256 * b >= pn) break;  // uniform
+      uint4 bq[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t j = min((uint32_t)(256 * (b + u) + 16 * wave + n), jmax);
+        bq[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rs, (int)(j * 256u + 16 * qd), 0, 0));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        f32x4 d, a;
+        dot64(aq, widen16(bq[u]), d, a);
+        const float2 iv = score_interval(d, a, wo);
+        const int j = 256 * (b + u) + 16 * wave + n;
+        if (olane && j < on) {
+          kl16[orow * FUSED_MAX_N + j] = (uint16_t)(ord_key(iv.x) >> 16);
+          kh16[orow * FUSED_MAX_N + j] = (uint16_t)(ord_key(iv.y) >> 16);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // ---- the four units, one after another
+#pragma unroll 1
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = r0 + u;
+    if (row >= rows) break;  // uniform
+    const int64_t unit = row * 4 + g;
+    const int N = (int)NC(u);
+    const int32_t useq = SQ(u);
+    const int K = N < TK ? N : TK;
+    // keys of candidates tid + 1024 k (absent 0): lower prefix rounded down,
+    // upper prefix rounded up to its last value
+    uint32_t kh[TK_PER], mx[4];
+#pragma unroll
+    for (int k = 0; k < TK_PER; ++k) kh[k] = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int j = tid + TK_THREADS * k;
+      const bool have = j < N;
+      mx[k] = have ? (uint32_t)kl16[u * FUSED_MAX_N + j] << 16 : 0u;
+      kh[k] = have ? ((uint32_t)kh16[u * FUSED_MAX_N + j] << 16) | 0xffffu : 0u;
+    }
+    // 1. tau: least over the waves of the wave's 32nd largest lower key
+    const uint32_t tw = wave_kth_largest4(mx, TK / TK_WAVES);
+    if (lane == 0) sm.misc[wave] = tw;
+    if (tid == 0) sm.misc[56] = 0u;
+    __syncthreads();
+    uint32_t tau;
+    {
+      uint32_t t = sm.misc[0];
+#pragma unroll
+      for (int w = 1; w < TK_WAVES; ++w) t = min(t, sm.misc[w]);
+      tau = t > 1u ? t : 1u;
+    }
+    // 2. survivors: upper key >= tau
+    int M = compact_keys(sm, kh, tau, 0, false, 4);
+    if (M > TK_SORT) {
+      // too many to sort directly: cut by T from the lower keys >= tau
+      uint32_t kl[TK_PER];
+#pragma unroll
+      for (int k = 0; k < TK_PER; ++k) kl[k] = k < 4 ? mx[k] : 0u;
+      if (tid == 0) sm.misc[56] = 0u;
+      __syncthreads();
+      M = compact_keys(sm, kl, tau, 0, true, 4);
+      const Boundary bd = radix_boundary(sm, M, K, 2);
+      const uint32_t T = bd.P > 1u ? bd.P : 1u;
+      if (tid == 0) sm.misc[56] = 0u;
+      __syncthreads();
+      M = compact_keys(sm, kh, T, 0, false, 4);
+    }
+    // 3. exact scores of the survivors (matrix cores)
+    const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
+    if (M > 0)
+      rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)useq * ssb + g * 64, wl,
+                        tid);
+    // 4. exact best K, sorted
+    unsigned long long v;
+    if (M <= TK) {
+      v = sort_desc<TK>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
+    } else if (M <= TK_SORT) {
+      v = sort_desc<TK_SORT>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
+    } else {
+      collect_best(sm, M, K);
+      v = sort_desc<TK>(tid < K ? sm.out[tid] : 0ull, sm);
+    }
+    write_rank(v, K, unit, sel_ids, sel_scores);
+    __syncthreads();
+  }
 }
 
 // Merge of the chunk lists of one (row, group): each list holds its chunk's
@@ -959,15 +1065,15 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     napp = (unsigned)ap.rows;
   }
   if (a.fused) {
-    const size_t sm = tk_smem_bytes(FUSED_MAX_N) + (size_t)FUSED_MAX_N * sizeof(uint32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)topk_chunk_kernel<TK_FUSED>,
+    const size_t sm = tk_smem_bytes(FUSED_MAX_N) + (size_t)2 * F4_KEYS * sizeof(uint16_t);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_fused4_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_chunk_kernel<TK_FUSED>, dim3(units + napp, 1), dim3(TK_THREADS), sm,
-                       stream, 0, nullptr, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos,
-                       a.B, a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb,
-                       (int64_t)FUSED_MAX_N, 1, a.partial, nullptr, a.arrivals, a.sel_ids,
-                       a.sel_scores, (int64_t)units, ap);
+    const int64_t nwg = ((int64_t)a.rows + 3) / 4 * 4;
+    hipLaunchKernelGGL(topk_fused4_kernel, dim3((unsigned)(nwg + napp)), dim3(TK_THREADS), sm,
+                       stream, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, a.rows, nwg,
+                       a.sel_ids, a.sel_scores, ap);
     return hipGetLastError();
   }
   const TopkPlan p = topk_plan(a.rows, a.R_cap);
@@ -989,19 +1095,19 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   const dim3 grid(units + napp, (unsigned)p.nchunks);
   if (mode == 2)
     hipLaunchKernelGGL(topk_chunk_kernel<TK_POOLED>, grid, dim3(TK_THREADS), sm, stream, mode,
-                       a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
                        p.nchunks, a.partial, a.pool, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);
   else if (a.exact)
     hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
-                       a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
                        p.nchunks, a.partial, nullptr, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);
   else
     hipLaunchKernelGGL(topk_chunk_kernel<TK_INTERVAL>, grid, dim3(TK_THREADS), sm, stream, mode,
-                       a.bounds, nullptr, (int64_t)0, a.R_cap, a.row_seq, a.row_pos, a.B,
+                       a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B,
                        a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
                        p.nchunks, a.partial, nullptr, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);

@@ -104,3 +104,48 @@ def test_decode_select_zero_score_ties(R):
     ex = P.compare_selection(ids.cpu().numpy(), sc.cpu().numpy(), osc,
                              d["row_pos"].cpu().numpy(), exact=True)
     assert ex == 0
+
+
+def test_fused_select_mixed_row_blocks():
+    """More than 64 rows over at most 4,096 regions take the fused interval
+    selection, which scores 4 consecutive rows at once when they share a
+    sequence and row by row otherwise. 70 rows (the last block of 4 is
+    partial): blocks of one sequence at consecutive positions (as a prompt
+    chunk), blocks mixing sequences, rows with 0, 1, 511, 512 and 513
+    candidates, and invalid rows (no sequence, a sequence past the batch, a
+    position past the summary). Ids and scores equal the oracle's."""
+    B, R = 6, 3000
+    g = torch.Generator().manual_seed(13)
+    draw, w = _draw("random", g)
+    seq, pos = [], []
+    for b in range(8):              # blocks of one sequence, consecutive positions
+        s = b % 4
+        p0 = 8 * (1200 + 150 * b) + 3
+        seq += [s] * 4
+        pos += [p0 + i for i in range(4)]
+    for b in range(6):              # blocks mixing sequences and candidate counts
+        seq += [4, 5, b % 4, (b + 1) % 4]
+        pos += [8 * 2999 + 2, 8 * (100 * b + 7), 8 * 512 + b, 8 * (2000 + b) + 7]
+    seq += [0, 1, 2, 3, 4, 5, 0, 1, 2, 3, 2, 5]  # edge counts, then invalid rows
+    pos += [0, 8 * 1, 8 * 511 + 5, 8 * 512, 8 * 513 + 7, 8 * 2999 + 7, 8 * 2800, 8 * 17, 8 * 2000,
+            8 * 640, 8 * 1500 + 1, 8 * 300]
+    seq += [-1, B]
+    pos += [8 * 1000, 8 * 1000]
+    seq[-4], pos[-4] = 3, 8 * R + 8   # a position past the summary
+    rows = len(seq)
+    assert rows == 70
+    d = {"rows": rows, "q8": draw((rows, 16, 64)).to(DEV), "w_head": w.to(DEV),
+         "row_seq": torch.tensor(seq, dtype=torch.int32, device=DEV),
+         "row_pos": torch.tensor(pos, dtype=torch.int64, device=DEV)}
+    S = draw((B, R, 4, 64)).to(DEV)
+    P.say(f"[case] fused selection, mixed 4-row blocks: {rows} rows over {R} regions")
+    ids, sc = P.gpu_select(d, S)
+    torch.cuda.synchronize()
+    ids_h, sc_h = ids.cpu().numpy(), sc.cpu().numpy()
+    bad = [r for r in range(rows) if not (0 <= seq[r] < B and pos[r] // 8 <= R)]
+    good = [r for r in range(rows) if r not in bad]
+    osc = P.oracle_scores(d, P.host8(S), good)
+    ex = P.compare_selection(ids_h[good], sc_h[good], osc, np.array(pos)[good], exact=True)
+    assert ex == 0
+    for r in bad:
+        assert np.all(ids_h[r] == -1) and np.all(sc_h[r] == 0), r

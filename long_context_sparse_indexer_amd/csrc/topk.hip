@@ -764,12 +764,91 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
 // prefix's last value), which keeps every bound below valid: the threshold
 // is taken at 16-bit resolution anyway. Then the four units are selected
 // one after another by the whole workgroup, 4 candidates a thread
-// (t + 1024 k): threshold, survivors, the cut when more than 1,024 survive,
-// exact rescoring and the sort, as in topk_chunk_kernel. One workgroup per
-// CU (64 KB of keys beside the selection's LDS), so the register cap is
-// that of 4 waves per SIMD.
+// (t + 1024 k): threshold, survivors, the cut when more than 1,024 survive
+// and exact rescoring, as in topk_chunk_kernel; each unit's (at most 1,024)
+// composites are set aside, and the four units are sorted at the end at
+// once, four waves each (one sort alone leaves a quarter of the block
+// busy; four side by side keep every SIMD at four waves). One workgroup
+// per CU (64 KB of keys and 32 KB of composites beside the selection's
+// LDS), so the register cap is that of 4 waves per SIMD.
 // ---------------------------------------------------------------------------
 constexpr int F4_KEYS = 4 * FUSED_MAX_N;  // u16 prefixes per array (4 rows)
+
+// The bitonic network over 1,024 composites held four per thread by a group
+// of 256 threads (four waves): element 4t + e in v[e], t the thread's index
+// in the group. Partners one or two apart are in the thread, 4..255 apart in
+// the wave (lane t ^ J/4, as above); the three stages with partners in
+// another wave of the group go through xb, the group's 1,024 slots, in
+// place (each thread writes its own four, a barrier, reads its partner's,
+// a barrier). All groups of the block run it together (the barriers).
+struct Bitonic4Ctx {
+  int t;                   // the thread's index in its group
+  int iw;                  // index of the wave's lane 0 in the group (wave-uniform)
+  unsigned long long* xb;  // the group's 1,024 slots
+};
+template <int K, int J>
+__device__ inline void bitonic4_stage(unsigned long long (&v)[4], const Bitonic4Ctx& c) {
+  if constexpr (J < 4) {
+    // elements e and e | J of the thread; descending where (i & K) == 0
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((e & J) != 0) continue;
+      bool desc;
+      if constexpr (K < 4) desc = (e & K) == 0;
+      else desc = (c.t & (K >> 2)) == 0;
+      const unsigned long long a = v[e], b = v[e | J];
+      const bool keep = (a > b) == desc;  // the larger stays first where descending
+      v[e] = keep ? a : b;
+      v[e | J] = keep ? b : a;
+    }
+  } else if constexpr (J < 256) {
+    constexpr int L = J >> 2;  // lane distance 1..32
+    unsigned long long tm;     // lanes that keep the larger
+    if constexpr ((K >> 2) < 64) tm = lanes_agree(L, K >> 2);
+    else tm = ((c.iw & (K >> 2)) == 0) ? lanes_clear(L) : ~lanes_clear(L);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const unsigned long long p = ((unsigned long long)lane_xor<L>((uint32_t)(v[e] >> 32)) << 32) |
+                                   lane_xor<L>((uint32_t)v[e]);
+      v[e] = lane_in(~(__ballot(v[e] > p) ^ tm)) ? v[e] : p;
+    }
+  } else {
+    constexpr int L = J >> 2;  // 64 or 128: another wave of the group
+    ulonglong2* b = reinterpret_cast<ulonglong2*>(c.xb);
+    b[2 * c.t] = make_ulonglong2(v[0], v[1]);
+    b[2 * c.t + 1] = make_ulonglong2(v[2], v[3]);
+    __syncthreads();
+    const ulonglong2 p01 = b[2 * (c.t ^ L)], p23 = b[2 * (c.t ^ L) + 1];
+    __syncthreads();
+    const unsigned long long p[4] = {p01.x, p01.y, p23.x, p23.y};
+    // wave-uniform: K / 4 and L are both at least 64
+    const bool larger = ((c.t & (K >> 2)) == 0) == ((c.t & L) == 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = ((v[e] > p[e]) == larger) ? v[e] : p[e];
+  }
+}
+template <int K, int J>
+struct Bitonic4Merge {
+  __device__ static inline void run(unsigned long long (&v)[4], const Bitonic4Ctx& c) {
+    bitonic4_stage<K, J>(v, c);
+    Bitonic4Merge<K, J / 2>::run(v, c);
+  }
+};
+template <int K>
+struct Bitonic4Merge<K, 0> {
+  __device__ static inline void run(unsigned long long (&)[4], const Bitonic4Ctx&) {}
+};
+template <int K>
+struct Bitonic4Sort {
+  __device__ static inline void run(unsigned long long (&v)[4], const Bitonic4Ctx& c) {
+    Bitonic4Sort<K / 2>::run(v, c);
+    Bitonic4Merge<K, K / 2>::run(v, c);
+  }
+};
+template <>
+struct Bitonic4Sort<1> {
+  __device__ static inline void run(unsigned long long (&)[4], const Bitonic4Ctx&) {}
+};
 
 // element i of a 4-array, i known only at run time (no dynamic indexing of
 // a private array, which would go to scratch)
@@ -800,6 +879,8 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
   const TkShared sm = carve(smem, FUSED_MAX_N);
   uint16_t* const kl16 = reinterpret_cast<uint16_t*>(smem + tk_smem_bytes(FUSED_MAX_N));
   uint16_t* const kh16 = kl16 + F4_KEYS;
+  // the four units' composites for the final sort, [4][1,024]
+  unsigned long long* const fin = reinterpret_cast<unsigned long long*>(kh16 + F4_KEYS);
   // the four rows (uniform): sequence (-1: no row / invalid) and candidates
   int32_t sq0, sq1, sq2, sq3;
   int64_t nc0, nc1, nc2, nc3;
@@ -888,7 +969,6 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
   for (int u = 0; u < 4; ++u) {
     const int64_t row = r0 + u;
     if (row >= rows) break;  // uniform
-    const int64_t unit = row * 4 + g;
     const int N = (int)NC(u);
     const int32_t useq = SQ(u);
     const int K = N < TK ? N : TK;
@@ -937,18 +1017,40 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
     if (M > 0)
       rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)useq * ssb + g * 64, wl,
                         tid);
-    // 4. exact best K, sorted
-    unsigned long long v;
-    if (M <= TK) {
-      v = sort_desc<TK>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
-    } else if (M <= TK_SORT) {
-      v = sort_desc<TK_SORT>(tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull, sm);
+    // 4. the unit's composites for the sort below: the survivors (at most
+    //    1,024), or the best K of them when more survive (collect_best)
+    unsigned long long* const fu = fin + u * TK_SORT;
+    if (M <= TK_SORT) {
+      fu[tid] = tid < M ? compose(sm.keys[tid], sm.ids[tid]) : 0ull;
     } else {
       collect_best(sm, M, K);
-      v = sort_desc<TK>(tid < K ? sm.out[tid] : 0ull, sm);
+      fu[tid] = tid < K ? sm.out[tid] : 0ull;
     }
-    write_rank(v, K, unit, sel_ids, sel_scores);
     __syncthreads();
+  }
+  // ---- the four units sorted at once, 256 threads (four waves) each,
+  //      best first; thread t < 128 of a group writes ranks 4t .. 4t+3
+  {
+    const int us = tid >> 8, t = tid & 255;
+    Bitonic4Ctx c;
+    c.t = t;
+    c.iw = __builtin_amdgcn_readfirstlane(t & ~63);
+    c.xb = fin + us * TK_SORT;
+    unsigned long long v[4];
+    const ulonglong2* src = reinterpret_cast<const ulonglong2*>(c.xb);
+    const ulonglong2 v01 = src[2 * t], v23 = src[2 * t + 1];
+    v[0] = v01.x;
+    v[1] = v01.y;
+    v[2] = v23.x;
+    v[3] = v23.y;
+    Bitonic4Sort<TK_SORT>::run(v, c);
+    const int64_t row = r0 + us;
+    if (row < rows && t < TK / 4) {
+      const int N = (int)NC(us);
+      const int K = N < TK ? N : TK;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) write_rank_at(v[e], 4 * t + e, K, row * 4 + g, sel_ids, sel_scores);
+    }
   }
 }
 
@@ -1065,7 +1167,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     napp = (unsigned)ap.rows;
   }
   if (a.fused) {
-    const size_t sm = tk_smem_bytes(FUSED_MAX_N) + (size_t)2 * F4_KEYS * sizeof(uint16_t);
+    const size_t sm = tk_smem_bytes(FUSED_MAX_N) + (size_t)2 * F4_KEYS * sizeof(uint16_t) +
+                      (size_t)4 * TK_SORT * sizeof(unsigned long long);
     hipError_t e = hipFuncSetAttribute((const void*)topk_fused4_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm);
     if (e != hipSuccess) return e;

@@ -964,7 +964,65 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
     }
   }
   __syncthreads();
-  // ---- the four units, one after another
+  // ---- thresholds and survivors of the four units side by side, four waves
+  //      (256 threads) each: thread t of unit ua's group holds candidates
+  //      t + 256 k (k < 16), grouped by k % 4. tau = the least over the
+  //      group's waves of the wave's 128th largest group maximum of the lower
+  //      keys (at least 1): at least 512 distinct candidates reach it. The
+  //      survivors (upper key >= tau) go to the unit's composite slots as
+  //      ids (low words); misc[60 + ua] counts them (past 1,024 the unit is
+  //      redone one unit at a time below).
+  if (tid < 4) sm.misc[60 + tid] = 0u;
+  __syncthreads();
+  uint32_t* const fw = reinterpret_cast<uint32_t*>(fin);
+  {
+    const int ua = tid >> 8, t = tid & 255;
+    const int Na = (int)NC(ua);
+    uint32_t kha[16], mxa[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int j = t + 256 * k;
+      const bool have = j < Na;
+      const uint32_t lo = have ? (uint32_t)kl16[ua * FUSED_MAX_N + j] << 16 : 0u;
+      kha[k] = have ? ((uint32_t)kh16[ua * FUSED_MAX_N + j] << 16) | 0xffffu : 0u;
+      mxa[k & 3] = lo > mxa[k & 3] ? lo : mxa[k & 3];
+    }
+    const uint32_t twa = wave_kth_largest4(mxa, TK / 4);
+    if (lane == 0) sm.misc[wave] = twa;
+    __syncthreads();
+    uint32_t taua;
+    {
+      const int w0 = 4 * ua;
+      const uint32_t m =
+          min(min(sm.misc[w0], sm.misc[w0 + 1]), min(sm.misc[w0 + 2], sm.misc[w0 + 3]));
+      taua = m > 1u ? m : 1u;
+    }
+    unsigned long long msk[16];
+    uint32_t wt = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      msk[k] = __ballot(kha[k] >= taua);
+      wt += (uint32_t)__popcll(msk[k]);
+    }
+    uint32_t base = 0;
+    if (lane == 0 && wt) base = atomicAdd(&sm.misc[60 + ua], wt);
+    base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (msk[k]) {
+        if (lane_in(msk[k])) {
+          const uint32_t pos = base + lanes_below(msk[k]);
+          if (pos < (uint32_t)TK_SORT) fw[2 * (ua * TK_SORT + pos)] = (uint32_t)(t + 256 * k);
+        }
+        base += (uint32_t)__popcll(msk[k]);
+      }
+    }
+  }
+  __syncthreads();
+  const int Ma[4] = {(int)sm.misc[60], (int)sm.misc[61], (int)sm.misc[62], (int)sm.misc[63]};
+  // ---- the four units' rescoring, one after another (a unit with more than
+  //      1,024 survivors: its threshold, survivors and cut again here, the
+  //      whole workgroup on it)
 #pragma unroll 1
   for (int u = 0; u < 4; ++u) {
     const int64_t row = r0 + u;
@@ -972,6 +1030,13 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
     const int N = (int)NC(u);
     const int32_t useq = SQ(u);
     const int K = N < TK ? N : TK;
+    int M;
+    const int Mu = sel4(u, Ma[0], Ma[1], Ma[2], Ma[3]);
+    if (Mu <= TK_SORT) {
+      M = Mu;
+      if (tid < M) sm.ids[tid] = (int32_t)fw[2 * (u * TK_SORT + tid)];
+      __syncthreads();
+    } else {
     // keys of candidates tid + 1024 k (absent 0): lower prefix rounded down,
     // upper prefix rounded up to its last value
     uint32_t kh[TK_PER], mx[4];
@@ -997,7 +1062,7 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
       tau = t > 1u ? t : 1u;
     }
     // 2. survivors: upper key >= tau
-    int M = compact_keys(sm, kh, tau, 0, false, 4);
+    M = compact_keys(sm, kh, tau, 0, false, 4);
     if (M > TK_SORT) {
       // too many to sort directly: cut by T from the lower keys >= tau
       uint32_t kl[TK_PER];
@@ -1011,6 +1076,7 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
       if (tid == 0) sm.misc[56] = 0u;
       __syncthreads();
       M = compact_keys(sm, kh, T, 0, false, 4);
+    }
     }
     // 3. exact scores of the survivors (matrix cores)
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];

@@ -149,3 +149,39 @@ def test_fused_select_mixed_row_blocks():
     assert ex == 0
     for r in bad:
         assert np.all(ids_h[r] == -1) and np.all(sc_h[r] == 0), r
+
+
+@pytest.mark.parametrize("kind", ["every_score_equal", "tie_heavy"])
+def test_fused_select_many_survivors(kind):
+    """The fused interval selection when one unit's survivors outnumber
+    1,024: every score equal (all 2,999 candidates of a row tie at the
+    threshold, so the unit is redone by the whole workgroup, cut and radix
+    selected, and keeps regions 0..511), and tie-heavy codes (8 distinct
+    values). 68 rows of 4 sequences over 3,000 regions, rows of one block
+    sharing a sequence. Ids and scores equal the oracle's."""
+    B, R, rows = 4, 3000, 68
+    g = torch.Generator().manual_seed(17)
+    seq = [(r // 4) % B for r in range(rows)]
+    pos = [8 * 2999 + (r % 8) for r in range(rows)]
+    if kind == "every_score_equal":
+        code = 0x38  # 1.0 in e4m3
+        q8 = torch.full((rows, 16, 64), code, dtype=torch.uint8)
+        S = torch.full((B, R, 4, 64), code, dtype=torch.uint8)
+        w = torch.arange(1, 17, dtype=torch.float32) / 16
+    else:
+        draw, w = _draw("tie_heavy", g)
+        q8, S = draw((rows, 16, 64)), draw((B, R, 4, 64))
+    d = {"rows": rows, "q8": q8.to(DEV), "w_head": w.to(DEV),
+         "row_seq": torch.tensor(seq, dtype=torch.int32, device=DEV),
+         "row_pos": torch.tensor(pos, dtype=torch.int64, device=DEV)}
+    S = S.to(DEV)
+    P.say(f"[case] fused selection, many survivors ({kind}): {rows} rows over {R} regions")
+    ids, sc = P.gpu_select(d, S)
+    torch.cuda.synchronize()
+    ids_h, sc_h = ids.cpu().numpy(), sc.cpu().numpy()
+    if kind == "every_score_equal":
+        assert np.array_equal(ids_h, np.tile(np.arange(512, dtype=np.int32), (rows, 4, 1)))
+    good = list(range(rows))
+    osc = P.oracle_scores(d, P.host8(S), good)
+    ex = P.compare_selection(ids_h, sc_h, osc, np.array(pos), exact=True)
+    assert ex == 0

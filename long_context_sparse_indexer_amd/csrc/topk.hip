@@ -454,11 +454,9 @@ __device__ inline int compact_keys(const TkShared& sm, const uint32_t (&key)[TK_
 // 64-register cap without spills). xb holds the query meanwhile (it is free
 // until the sort).
 constexpr int RS_Q = 3;
-__device__ inline void rescore_survivors(const TkShared& sm, int M, const double* __restrict__ qg,
-                                         const uint8_t* __restrict__ Sg, float wl, int tid) {
-  double* qs = reinterpret_cast<double*>(sm.xb);
-  if (tid < 256) qs[tid] = qg[tid];
-  __syncthreads();
+// qs: the query in LDS, [64 dims][4 heads] (a barrier since it was written)
+__device__ inline void rescore_survivors_lds(const TkShared& sm, int M, const double* qs,
+                                             const uint8_t* __restrict__ Sg, float wl, int tid) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int kk = lane >> 4, c16 = lane & 15, i = lane & 3;
   const int ngrp = (M + 15) >> 4;
@@ -504,6 +502,13 @@ __device__ inline void rescore_survivors(const TkShared& sm, int M, const double
     }
   }
   __syncthreads();
+}
+__device__ inline void rescore_survivors(const TkShared& sm, int M, const double* __restrict__ qg,
+                                         const uint8_t* __restrict__ Sg, float wl, int tid) {
+  double* qs = reinterpret_cast<double*>(sm.xb);
+  if (tid < 256) qs[tid] = qg[tid];
+  __syncthreads();
+  rescore_survivors_lds(sm, M, qs, Sg, wl, tid);
 }
 
 // One chunk of a (row, group)'s candidates: threshold, survivors, exact
@@ -896,6 +901,10 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
   row_of(3, sq3, nc3);
   auto SQ = [&](int i) { return sel4(i, sq0, sq1, sq2, sq3); };
   auto NC = [&](int i) { return sel4(i, nc0, nc1, nc2, nc3); };
+  // the four units' exact queries for the rescoring (thread t: entry t % 256
+  // of unit t / 256), loaded now and kept in LDS (sm.xb, [4][256]) once the
+  // intervals are done, so that their latency hides behind the intervals
+  const double qpre = NC(tid >> 8) > 0 ? q64[(r0 * 4 + g + 4 * (tid >> 8)) * 256 + (tid & 255)] : 0.0;
   int32_t s0 = -1;
   bool shared = true;
   int nmax = 0;
@@ -973,6 +982,7 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
   //      ids (low words); misc[60 + ua] counts them (past 1,024 the unit is
   //      redone one unit at a time below).
   if (tid < 4) sm.misc[60 + tid] = 0u;
+  reinterpret_cast<double*>(sm.xb)[tid] = qpre;
   __syncthreads();
   uint32_t* const fw = reinterpret_cast<uint32_t*>(fin);
   {
@@ -1081,8 +1091,8 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
     // 3. exact scores of the survivors (matrix cores)
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
     if (M > 0)
-      rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)useq * ssb + g * 64, wl,
-                        tid);
+      rescore_survivors_lds(sm, M, reinterpret_cast<const double*>(sm.xb) + 256 * u,
+                            S + (int64_t)useq * ssb + g * 64, wl, tid);
     // 4. the unit's composites for the sort below: the survivors (at most
     //    1,024), or the best K of them when more survive (collect_best)
     unsigned long long* const fu = fin + u * TK_SORT;

@@ -40,6 +40,10 @@
 // all taken and `need` keys with prefix P are taken in list order; the
 // passes stop early when the boundary bin is taken whole. The bins are
 // scanned by all threads at once (two bins each, a block-wide scan).
+//
+// Prompt chunks take topk_fused4_kernel (below): four units per workgroup,
+// their intervals computed in place, thresholds, survivors and sorts done
+// for the four units side by side.
 #include "device.hpp"
 #include "exact.hpp"
 #include "interval.hpp"
@@ -767,15 +771,15 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
 // and makes its interval. The intervals go to LDS as 16-bit key prefixes,
 // rounded outward (lower key down to its prefix, upper key up to the
 // prefix's last value), which keeps every bound below valid: the threshold
-// is taken at 16-bit resolution anyway. Then the four units are selected
-// one after another by the whole workgroup, 4 candidates a thread
-// (t + 1024 k): threshold, survivors, the cut when more than 1,024 survive
-// and exact rescoring, as in topk_chunk_kernel; each unit's (at most 1,024)
-// composites are set aside, and the four units are sorted at the end at
-// once, four waves each (one sort alone leaves a quarter of the block
-// busy; four side by side keep every SIMD at four waves). One workgroup
-// per CU (64 KB of keys and 32 KB of composites beside the selection's
-// LDS), so the register cap is that of 4 waves per SIMD.
+// is taken at 16-bit resolution anyway. Then: thresholds and survivors of
+// the four units side by side, four waves each (16 candidates a thread);
+// exact rescoring one unit after another by the whole workgroup (a unit
+// with more than 1,024 survivors is redone here as in topk_chunk_kernel,
+// cut and radix selected); the four sorts side by side, four waves each
+// (one sort alone leaves a quarter of the block busy; four keep every
+// SIMD at four waves). One workgroup per CU (64 KB of keys and 32 KB of
+// composites beside the selection's LDS), so the register cap is that of
+// 4 waves per SIMD.
 // ---------------------------------------------------------------------------
 constexpr int F4_KEYS = 4 * FUSED_MAX_N;  // u16 prefixes per array (4 rows)
 

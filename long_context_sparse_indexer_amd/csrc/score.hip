@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) void score_kernel(
 // quads of summary loads, then the prep's arithmetic. With `pool` (units cut
 // into several selection chunks) the block also leaves, per group, 8 keys
 // for the selection's threshold: each the best score key among 32 of its
-// candidates (lanes 4g + j and 4g + (j ^ 1) of a wave), 0 where none.
+// candidates (candidates j and j ^ 1 of a wave's 16 quads), 0 where none.
 // ---------------------------------------------------------------------------
 // NQ quads of 4 candidates per wave: 16 (256 candidates per block), or 8
 // (128) when a batch has too few rows for 1,024 blocks of 256; POOL: `pool`
@@ -405,11 +405,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   if (wave < 2) *reinterpret_cast<uint2*>(&q_lds[ph * 64 + pc * 8]) = pk;
   __syncthreads();
   // pool: per (row, group), one key per 32 candidates, the best (0 if none),
-  // gathered by LDS atomic max. NQ = 16: entry 8 b + 2 wave + p from lanes
-  // 4g + 2p and 4g + 2p + 1 (pmax[wave][2g + p]); NQ = 8: entry 4 b + wave
-  // from the group's 4 lanes (pmax[wave][g]). A unit's keys start every
+  // gathered by LDS atomic max. NQ = 16: entry 8 b + 2 wave + p from the
+  // lanes of candidates 2p and 2p + 1 of group g (pmax[wave][2g + p]); NQ = 8:
+  // entry 4 b + wave from all of the group's lanes (pmax[wave][g]). A unit's keys start every
   // 8 * ceil(R_cap / 256) entries.
-  constexpr int PSH = NQ == 16 ? 1 : 2;  // lane >> PSH: the lane's pmax slot
+  constexpr int PSH = NQ == 16 ? 1 : 2;  // (lane & 15) >> PSH: the lane's pmax slot
   auto pool_put = [&]() {
     const int64_t ustride = ((R_cap + 255) >> 8) * 8;
     if (NQ == 16 && lane < 8)
@@ -453,21 +453,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         for (int q = 0; q < 4; ++q)
           acc[q] = __builtin_amdgcn_mfma_f64_4x4x4f64(qa[e], sv[q][e], acc[q], 0, 0, 0);
     }
-    // D lane 16i + 4g + j: dot of head 4g + i with candidate j. The score
-    // sums the heads' weighted relu terms in head order, gathered into the
-    // lanes of head 0 (16 apart).
+    // D lane 16i + 4g + j: dot of head 4g + i with candidate j of quad q.
+    // Each lane weighs its relu term, then a 4 x 4 transpose over (lane row
+    // i, quad q), two 32-lane and two 16-lane swaps, leaves in lane
+    // 16r + 4g + j the four heads' terms of quad r's candidate j, which it
+    // sums in head order.
+    uint32_t t[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float t = relu0((float)acc[q]) * wl;
-      const float t1 = __shfl_down(t, 16, 64), t2 = __shfl_down(t, 32, 64), t3 = __shfl_down(t, 48, 64);
-      float sc = t + t1;
-      sc = sc + t2;
-      sc = sc + t3;
-      const int64_t j = cb0 + 4 * (u0 + q) + ij;
-      if (lane < 16 && j < jend) {
-        out_g[j] = sc;
-        if (POOL) atomicMax(&pmax[wave][lane >> PSH], ord_key(sc));
-      }
+    for (int q = 0; q < 4; ++q) t[q] = __float_as_uint(relu0((float)acc[q]) * wl);
+    {
+      // upper half of t0 (t1) <-> lower half of t2 (t3): rows 0-1 of quads
+      // 0 and 2 (1 and 3) in t0 (t1), rows 2-3 in t2 (t3)
+      const auto a = __builtin_amdgcn_permlane32_swap(t[0], t[2], false, false);
+      const auto b = __builtin_amdgcn_permlane32_swap(t[1], t[3], false, false);
+      // odd rows of the first <-> even rows of the second: row r of each
+      // result then holds quad r, heads 0, 1 (c) and 2, 3 (d)
+      const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+      const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+      t[0] = c[0];
+      t[1] = c[1];
+      t[2] = d[0];
+      t[3] = d[1];
+    }
+    float sc = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+    sc = sc + __uint_as_float(t[2]);
+    sc = sc + __uint_as_float(t[3]);
+    const int64_t j = cb0 + 4 * (u0 + k) + ij;
+    if (j < jend) {
+      out_g[j] = sc;
+      if (POOL) atomicMax(&pmax[wave][(lane & 15) >> PSH], ord_key(sc));
     }
   };
   if constexpr (NQ == 16) {

@@ -89,9 +89,6 @@ struct TlRegs {
   u32x2 va, vb;
 };
 
-// word 3 of a raw buffer resource on gfx9 parts (32-bit data format; no
-// swizzle, no stride): out-of-range reads return zero
-constexpr int TL_RSRC3 = 0x00020000;
 
 }  // namespace
 
@@ -241,9 +238,9 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
     const int64_t left = rec_end - off;
     const int nrec = left > 0 ? (int)left : 0;
     const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, nrec, TL_RSRC3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), (short)0, nrec, RAW_RSRC3);
     const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, nrec, TL_RSRC3);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), (short)0, nrec, RAW_RSRC3);
     TlRegs R;
     R.k = __builtin_amdgcn_raw_buffer_load_b128(rk, (int)ko, 0, 0);
     R.va = __builtin_amdgcn_raw_buffer_load_b64(rv, (int)vo0, 0, 0);

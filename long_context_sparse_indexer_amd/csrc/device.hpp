@@ -214,6 +214,10 @@ __device__ inline void unpack_bf16x8(const uint4 w, float* f) {
 
 __device__ inline uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// word 3 of a raw buffer resource on gfx9 parts (32-bit data format; no
+// swizzle, no stride): reads at offsets from the record count on return zero
+constexpr int RAW_RSRC3 = 0x00020000;
+
 // 32-bit key ordered like the float score (-0 first turned into +0 by adding
 // +0); every key but that of one negative NaN pattern is nonzero, and the
 // selection uses 0 for "no candidate"

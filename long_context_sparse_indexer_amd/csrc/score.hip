@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ __align__(16) uint8_t q_lds[16 * 64];
   constexpr int CW = 4 * NQ, CB = 4 * CW;  // candidates per wave, per block
   __shared__ uint32_t pmax[4][8];  // pool: the best key of each 32 candidates (see below)
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (threadIdx.x < 32) pmax[threadIdx.x >> 3][threadIdx.x & 7] = 0u;
   const int k = lane >> 4, g = (lane >> 2) & 3, ij = lane & 3;  // ij: head i (A) or candidate j (B)
   const int64_t row = blockIdx.y;
@@ -380,17 +380,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     pin = qprep8_load(static_cast<const uint16_t*>(prep.q), prep.q_stride_row, row, ph, pc,
                       prep.w, static_cast<const uint16_t*>(prep.rope), qprep_pos(p, prep.rope_rows));
   // this lane's 16 summary bytes of quad u: candidate cb0 + 4u + ij, group
-  // g, dims 16k..16k+15 (candidates past jend load jend - 1 again; a wave
-  // past the row's candidates loads region 0 and stops after the prep).
-  // Quads are loaded four at a time, two groups ahead of the one computed.
+  // g, dims 16k..16k+15, through a buffer resource over exactly the wave's
+  // jend - cb0 summaries: loads of candidates past jend return zeros (not
+  // stored; a wave past the row's candidates has none and stops after the
+  // prep). Quads are loaded four at a time, two groups ahead of the one
+  // computed.
   const uint8_t* Sw = S + (int64_t)s * ssb + (live ? cb0 * 256 : 0);
-  const uint32_t jlast = live ? (uint32_t)(jend - cb0 - 1) : 0u;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)Sw, (short)0, (int)(live ? (uint32_t)(jend - cb0) * 256u : 0u), RAW_RSRC3);
+  const uint32_t lo = (uint32_t)(ij * 256 + g * 64 + 16 * k);
   auto load4 = [&](int u0, uint4 (&dst)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t jo = min((uint32_t)(4 * (u0 + q) + ij), jlast);
-      dst[q] = ldg16(Sw + (jo * 256u + (uint32_t)(g * 64 + 16 * k)));
-    }
+    for (int q = 0; q < 4; ++q)
+      dst[q] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(lo + 1024u * (u0 + q)), 0, 0));
   };
   uint4 bA[4], bB[4], bC[4];
   load4(0, bA);

@@ -409,8 +409,6 @@ __device__ inline void write_rank(unsigned long long v, int K, int64_t unit, int
 // (summaries of up to 4,096 regions; topk_fused4_kernel below).
 constexpr int FUSED_MAX_N = 16 * TK_WAVES * TK_PER;  // 4,096
 
-// dword 3 of a raw buffer resource for 32-bit offsets (as attn_tile.hip's)
-constexpr int FK_RSRC3 = 0x00020000;
 
 // Appends the candidates whose key reaches t to sm.ids (and, with keys, the
 // key to sm.keys), per wave in ballot order; misc[56] holds the count, zero
@@ -951,7 +949,7 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
     const uint8_t* Sg = S + (int64_t)pseq * ssb + g * 64;
     const uint32_t jmax = (uint32_t)(pn - 1);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)Sg, (short)0, (int)((uint32_t)pn * 256u), FK_RSRC3);
+        (void*)Sg, (short)0, (int)((uint32_t)pn * 256u), RAW_RSRC3);
     // tile t of wave w: candidates 256 t + 16 w + n; 8 tiles per round trip
 #pragma unroll 1
     for (int b = 0; b < FUSED_MAX_N / 256; b += 8) {

@@ -217,6 +217,9 @@ __device__ inline uint4 ldg16(const void* p) { return *reinterpret_cast<const ui
 // word 3 of a raw buffer resource on gfx9 parts (32-bit data format; no
 // swizzle, no stride): reads at offsets from the record count on return zero
 constexpr int RAW_RSRC3 = 0x00020000;
+// a byte offset past every record count the kernels give a resource
+// (at most a few hundred MB): a store there is dropped
+constexpr uint32_t RAW_PAST_END = 0x7ffffff0u;
 
 // 32-bit key ordered like the float score (-0 first turned into +0 by adding
 // +0); every key but that of one negative NaN pattern is nonzero, and the

@@ -430,7 +430,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
   // this lane's weight for the epilogue: head 4g + i with i = lane >> 4 (the D row)
   const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
-  float* out_g = scores + (row * 4 + g) * R_cap;
+  // the row's 4 x R_cap scores as one buffer resource; lane offset of its
+  // group's candidate cb0
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(scores + row * 4 * R_cap), (short)0, (int)(16 * R_cap), RAW_RSRC3);
+  const uint32_t obase = (uint32_t)((g * R_cap + cb0) * 4);
+  const uint32_t nw = (uint32_t)(jend - cb0);
   auto quads4 = [&](int u0, const uint4 (&bq)[4]) {
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -481,11 +486,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     float sc = __uint_as_float(t[0]) + __uint_as_float(t[1]);
     sc = sc + __uint_as_float(t[2]);
     sc = sc + __uint_as_float(t[3]);
-    const int64_t j = cb0 + 4 * (u0 + k) + ij;
-    if (j < jend) {
-      out_g[j] = sc;
-      if (POOL) atomicMax(&pmax[wave][(lane & 15) >> PSH], ord_key(sc));
-    }
+    // candidate cb0 + jw; lanes past jend store to an offset beyond the
+    // resource's records (dropped) and put a 0 key, so no lane branches
+    const uint32_t jw = (uint32_t)(4 * (u0 + k) + ij);
+    const bool in = jw < nw;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), ro,
+                                          (int)(in ? obase + 4u * jw : RAW_PAST_END), 0, 0);
+    if (POOL) atomicMax(&pmax[wave][(lane & 15) >> PSH], in ? ord_key(sc) : 0u);
   };
   if constexpr (NQ == 16) {
     load4(8, bC);

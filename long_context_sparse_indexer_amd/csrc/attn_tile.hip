@@ -289,7 +289,7 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
 
   // S^T of the chunk in buffer bf: lane (n, qd), acc[st][r] = score of MFMA
   // row n with token 16 st + 4 qd + r (region 2 st + qd/2 of the chunk, token
-  // 4 (qd & 1) + r in it)
+  // 4 (qd & 1) + r in it); the two 4-MFMA chains alternate
   auto scores = [&](int bf, f32x4 (&acc)[2]) {
     const uint4* kl = kbuf + bf * 512;
     uint4 kf[2][4];
@@ -297,12 +297,12 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int u = 0; u < 4; ++u) kf[st][u] = kl[(16 * st + n) * 16 + ((4 * u + qd) ^ n)];
+    acc[0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    acc[1] = acc[0];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      acc[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[st] = tl_mfma(kf[st][u], qb[u], acc[st]);
-    }
+      for (int st = 0; st < 2; ++st) acc[st] = tl_mfma(kf[st][u], qb[u], acc[st]);
   };
   // t = scale*log2(e)*score - ms where the row attends the token, else -inf:
   // in the sweep, the row's selected regions (whole regions)
@@ -433,7 +433,10 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
     if (ci + 1 < nch) {
       // the two waves sharing a SIMD (w and w + 4) take the matrix work and
       // the softmax in opposite orders, so one feeds the MFMA unit while the
-      // other runs vector instructions
+      // other runs vector instructions. In the matrix work the scores' 8
+      // operand reads from LDS are issued together, then their 8 MFMAs,
+      // then the output's 8 reads and 16 MFMAs (the scheduling groups below:
+      // left alone, the compiler reuses a few registers and waits on each read)
       f32x4 acc2[2];
       float t[2][4];
       uint4 nhi, nlo;
@@ -444,9 +447,17 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
         __builtin_amdgcn_sched_barrier(0);
         scores(B2, acc2);  // chunk ci+2 (unused past the last chunk)
         pv(B0, phi, plo);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
       } else {
         scores(B2, acc2);
         pv(B0, phi, plo);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
         __builtin_amdgcn_sched_barrier(0);
         masked_sel(mb1, acc1, t);
         ps = probs(t, nhi, nlo);

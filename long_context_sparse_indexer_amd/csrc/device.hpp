@@ -221,6 +221,22 @@ constexpr int RAW_RSRC3 = 0x00020000;
 // (at most a few hundred MB): a store there is dropped
 constexpr uint32_t RAW_PAST_END = 0x7ffffff0u;
 
+// A 4 x 4 transpose over (16-lane row of the wave, register) with gfx950's
+// lane swaps: on return t[i] in lane 16r + c holds what t[r] held in lane
+// 16i + c. (The 32-lane swap exchanges the upper half of its first operand
+// with the lower half of its second; the 16-lane swap exchanges the odd
+// rows of its first operand with the even rows of its second.)
+__device__ inline void transpose_rows4(uint32_t (&t)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(t[0], t[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(t[1], t[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  t[0] = c[0];
+  t[1] = c[1];
+  t[2] = d[0];
+  t[3] = d[1];
+}
+
 // 32-bit key ordered like the float score (-0 first turned into +0 by adding
 // +0); every key but that of one negative NaN pattern is nonzero, and the
 // selection uses 0 for "no candidate"

@@ -469,20 +469,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     uint32_t t[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) t[q] = __float_as_uint(relu0((float)acc[q]) * wl);
-    {
-      // upper half of t0 (t1) <-> lower half of t2 (t3): rows 0-1 of quads
-      // 0 and 2 (1 and 3) in t0 (t1), rows 2-3 in t2 (t3)
-      const auto a = __builtin_amdgcn_permlane32_swap(t[0], t[2], false, false);
-      const auto b = __builtin_amdgcn_permlane32_swap(t[1], t[3], false, false);
-      // odd rows of the first <-> even rows of the second: row r of each
-      // result then holds quad r, heads 0, 1 (c) and 2, 3 (d)
-      const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-      const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-      t[0] = c[0];
-      t[1] = c[1];
-      t[2] = d[0];
-      t[3] = d[1];
-    }
+    transpose_rows4(t);  // t[i] in lane 16r + 4g + j: head i, quad r
     float sc = __uint_as_float(t[0]) + __uint_as_float(t[1]);
     sc = sc + __uint_as_float(t[2]);
     sc = sc + __uint_as_float(t[3]);

@@ -404,14 +404,24 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
   uint32_t umR = 0;  // token mask of the chunk in R
   uint4 phi, plo;
   f32x4 acc1[2];
-  // chunk ids from registers: lane i of clv0 holds the id of list entry
-  // 64 clb + i, clv1 those of the next 64 (no LDS round trip per step)
-  uint32_t clv0 = 0, clv1 = 0;
+  // chunk ids and token masks from registers: lane i of clv0 (clu0) holds
+  // the id (token mask) of list entry 64 clb + i, clv1 (clu1) those of the
+  // next 64 (no LDS round trip, and no wait for one, per step)
+  uint32_t clv0 = 0, clv1 = 0, clu0 = 0, clu1 = 0;
   int clb = 0;
   auto cl_fetch = [&](int blk) { const int i = 64 * blk + lane; return i < nch ? (uint32_t)clist[i] : 0u; };
+  auto cu_fetch = [&](int blk) {
+    const int i = 64 * blk + lane;
+    return i < nch ? umask[clist[i]] : 0u;
+  };
   auto cid = [&](int i) {
     const int a = __builtin_amdgcn_readlane((int)clv0, i & 63);
     const int b = __builtin_amdgcn_readlane((int)clv1, i & 63);
+    return (i >> 6) == clb ? a : b;
+  };
+  auto cum = [&](int i) {
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)clu0, i & 63);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)clu1, i & 63);
     return (i >> 6) == clb ? a : b;
   };
   uint32_t mb1 = 0;  // this row's region bits in chunk ci+1 (read a step ahead)
@@ -421,14 +431,15 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
     if ((ci & 63) == 0 && ci > 0) {
       clv0 = clv1;
       clv1 = cl_fetch((ci >> 6) + 1);
+      clu0 = clu1;
+      clu1 = cu_fetch((ci >> 6) + 1);
       clb = ci >> 6;
     }
     const uint32_t mb2 = mask_bits(cid(min(ci + 2, nch - 1)));
     if (ci + 3 < nch) {
       write(R, umR, B3);
-      const int c4 = cid(min(ci + 4, nch - 1));
-      R = load_chunk(c4);
-      umR = umask[c4];
+      R = load_chunk(cid(min(ci + 4, nch - 1)));
+      umR = cum(min(ci + 4, nch - 1));
     }
     if (ci + 1 < nch) {
       // the two waves sharing a SIMD (w and w + 4) take the matrix work and
@@ -475,6 +486,8 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
   if (nch > 0) {
     clv0 = cl_fetch(0);
     clv1 = cl_fetch(1);
+    clu0 = cu_fetch(0);
+    clu1 = cu_fetch(1);
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
       const int c = cid(min(i, nch - 1));

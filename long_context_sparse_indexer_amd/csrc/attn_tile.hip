@@ -139,14 +139,19 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
   if (tid < 16 + 2 * TL_ROWS) misc[tid] = 0u;  // counters, own chunks, own token masks
   for (int w = tid; w < TL_ROWS * mw + (int)L.tw; w += TL_THREADS) rmask[w] = 0u;  // and umask
   __syncthreads();
-  for (int x = tid; x < TL_ROWS * 512; x += TL_THREADS) {
-    const int i = x >> 9;
-    const int64_t p = rp[i];
-    if (p < 0) continue;
-    const int32_t j = sel[((r0 + i) * 4 + g) * 512 + (x & 511)];
-    if (j >= 0 && j < (p >> 3)) {
-      atomicOr(&rmask[i * mw + (j >> 5)], 1u << (j & 31));
-      atomicOr(&umask[j >> 2], 0xffu << (8 * (j & 3)));
+  {
+    // the rows' region bits: thread tid takes entry tid of every row's
+    // selection (all 32 loads issued first), set by LDS atomics
+    static_assert(TL_THREADS == 512, "one selection entry per thread and row");
+    int32_t jr[TL_ROWS];
+#pragma unroll
+    for (int k = 0; k < TL_ROWS; ++k)
+      jr[k] = r0 + k < rows ? sel[((r0 + k) * 4 + g) * 512 + tid] : -1;
+#pragma unroll
+    for (int k = 0; k < TL_ROWS; ++k) {
+      const int64_t p = rp[k];
+      const int32_t j = jr[k];
+      if (p >= 0 && j >= 0 && j < (p >> 3)) atomicOr(&rmask[k * mw + (j >> 5)], 1u << (j & 31));
     }
   }
   if (tid < TL_ROWS && rp[tid] >= 0) {
@@ -155,6 +160,18 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
     atomicMax(&misc[2], (uint32_t)p + 1u);
   }
   __syncthreads();
+  // the tile's token mask per chunk: the union of the rows' region bits
+  // (region word w holds chunks 8w .. 8w+7), each region's bit spread to its
+  // 8 tokens (bit r of a nibble to byte r)
+  for (int w = tid; w < mw; w += TL_THREADS) {
+    uint32_t o = 0u;
+    for (int k = 0; k < TL_ROWS; ++k) o |= rmask[k * mw + w];
+#pragma unroll
+    for (int c4 = 0; c4 < 8; ++c4) {
+      const int c = 8 * w + c4;
+      if (c < (int)L.tw) umask[c] = ((((o >> (4 * c4)) & 15u) * 0x00204081u) & 0x01010101u) * 0xffu;
+    }
+  }
   // the distinct chunks holding the rows' own regions (attended after the
   // sweep): row i's chunk unless an earlier row has it
   if (wave == 0) {
@@ -179,6 +196,7 @@ __global__ __launch_bounds__(TL_THREADS) void attn_tile_kernel(
       atomicOr(&misc[16 + TL_ROWS + k], ((2u << (pi & 7)) - 1u) << (8 * (jo & 3)));
     }
   }
+  __syncthreads();
   // the chunks holding some row's selected regions, in order
   const int nch_all = (int)((misc[0] + 3u) >> 2);
   for (int base = 0; base < nch_all; base += TL_THREADS) {

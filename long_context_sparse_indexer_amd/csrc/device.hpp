@@ -137,38 +137,6 @@ __device__ inline uint32_t dppu(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
 
-// the 64-bit value of lane ^ J (J = 1, 2, 4, 8 within 16-lane rows by DPP;
-// 16 and 32 through the cross-lane permute)
-template <int J>
-__device__ inline unsigned long long lane_xor64(unsigned long long v, int lane) {
-  if constexpr (J >= 16) {
-    return __shfl_xor(v, J, 64);
-  } else {
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-    uint32_t a, b;
-    if constexpr (J == 1) {
-      a = dppu<DPP_QUAD_XOR1>(lo);
-      b = dppu<DPP_QUAD_XOR1>(hi);
-    } else if constexpr (J == 2) {
-      a = dppu<DPP_QUAD_XOR2>(lo);
-      b = dppu<DPP_QUAD_XOR2>(hi);
-    } else if constexpr (J == 4) {
-      // row_ror:n reads lane (i - n) mod 16 of the row: lane i ^ 4 is lane
-      // i - 4 (ror 4) where bit 2 is set and i + 4 (ror 12) where it is clear
-      const bool up = (lane & 4) != 0;
-      const uint32_t a4 = dppu<DPP_ROW_ROR4>(lo), a12 = dppu<DPP_ROW_ROR12>(lo);
-      const uint32_t b4 = dppu<DPP_ROW_ROR4>(hi), b12 = dppu<DPP_ROW_ROR12>(hi);
-      a = up ? a4 : a12;
-      b = up ? b4 : b12;
-    } else {
-      static_assert(J == 8, "lane_xor64: J must be a power of two up to 32");
-      a = dppu<DPP_ROW_ROR8>(lo);  // rotating a 16-lane row by 8 is lane ^ 8
-      b = dppu<DPP_ROW_ROR8>(hi);
-    }
-    return ((unsigned long long)b << 32) | a;
-  }
-}
-
 template <int CTRL>
 __device__ inline float dpp(float v) {
   return __builtin_bit_cast(

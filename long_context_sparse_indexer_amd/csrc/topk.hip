@@ -309,8 +309,12 @@ __device__ inline uint32_t lane_xor(uint32_t v) {
   } else if constexpr (J == 16) {
     return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (16 << 10));   // xor 16
   } else {
+    // gfx950's 32-lane swap of the value with itself: the first result holds
+    // the lower half twice, the second the upper half twice (no LDS round
+    // trip, unlike a bpermute)
     static_assert(J == 32, "lane_xor: J must be a power of two below 64");
-    return (uint32_t)__shfl_xor((int)v, 32, 64);
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() >> 5) ? s[0] : s[1];
   }
 }
 

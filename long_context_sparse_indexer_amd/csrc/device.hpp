@@ -189,6 +189,11 @@ constexpr int RAW_RSRC3 = 0x00020000;
 // (at most a few hundred MB): a store there is dropped
 constexpr uint32_t RAW_PAST_END = 0x7ffffff0u;
 
+// the exact value of an e4m3 code (every e4m3 value is an fp32 value)
+__device__ inline double e4m3_f64(uint8_t b) {
+  return (double)__builtin_amdgcn_cvt_f32_fp8((int)b, 0);
+}
+
 // A 4 x 4 transpose over (16-lane row of the wave, register) with gfx950's
 // lane swaps: on return t[i] in lane 16r + c holds what t[r] held in lane
 // 16i + c. (The 32-lane swap exchanges the upper half of its first operand

@@ -54,7 +54,6 @@ struct QPrepArgs {
   int64_t rope_rows;
   const int64_t* row_pos;
   uint8_t* q8;            // [rows, 16, 64] e4m3
-  double* q64;            // [rows, 4 groups, 64 dims, 4 heads]: exact values of the e4m3 q
   unsigned* arrivals;     // [rows*8]: top-k arrival counters (zeroed by the q prep or the
                           // exact scorer), then the exact path's survivor counts (zeroed
                           // by the exact scorer)
@@ -117,9 +116,8 @@ struct TopkArgs {
   const float2* bounds;  // [rows, 4, R_cap] from launch_score
   bool exact;            // bounds holds exact scores (see ScoreArgs)
   bool fused;            // select_fused: no bounds; intervals computed from q8
-  const uint8_t* q8;     // from launch_qprep, [rows, 16, 64] (fused)
+  const uint8_t* q8;     // from launch_qprep, [rows, 16, 64] (intervals, rescoring)
   int64_t q8_stride_row; // bytes
-  const double* q64;     // exact query, for rescoring
   const float* w_head;
   int64_t w_stride_row;
   const uint8_t* summary;

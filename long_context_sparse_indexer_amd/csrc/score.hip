@@ -146,17 +146,6 @@ __device__ inline uint2 qprep8(int mode, const void* __restrict__ qin, int64_t q
   return qprep8_math(in, c, lane, eps);
 }
 
-// exact values of 8 packed e4m3 codes (every e4m3 value is an fp32 value)
-__device__ inline void e4m3x8_f64(uint2 pk, double (&out)[8]) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.x, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.x, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.y, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)pk.y, true);
-  const float f[8] = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = (double)f[i];
-}
-
 // q prep kernel: one 8-lane group per (row, head)
 __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __restrict__ qin,
                                                     int64_t qs, int32_t rows,
@@ -165,7 +154,6 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
                                                     int64_t rope_rows,
                                                     const int64_t* __restrict__ row_pos,
                                                     uint8_t* __restrict__ q8,
-                                                    double* __restrict__ q64,
                                                     unsigned* __restrict__ arrivals) {
   const int lane = threadIdx.x & 63;
   const int c = threadIdx.x & 7;
@@ -180,11 +168,6 @@ __global__ __launch_bounds__(256) void qprep_kernel(int mode, const void* __rest
   const int h = (int)(vec & 15);
   const uint2 pk = qprep8(mode, qin, qs, r, h, c, lane, w, eps, rope, rope_rows, row_pos);
   *reinterpret_cast<uint2*>(q8 + vec * 64 + c * 8) = pk;
-  double vals[8];
-  e4m3x8_f64(pk, vals);
-  double* dst = q64 + ((r * 4 + (h >> 2)) * 64 + c * 8) * 4 + (h & 3);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) dst[i * 4] = vals[i];
 }
 
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream) {
@@ -192,7 +175,7 @@ hipError_t launch_qprep(const QPrepArgs& a, hipStream_t stream) {
   if (vecs == 0) return hipSuccess;
   hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)((vecs + 31) / 32)), dim3(256), 0, stream,
                      a.prepared ? 1 : 0, a.q, a.q_stride_row, a.rows, a.w, a.eps,
-                     (const uint16_t*)a.rope, a.rope_rows, a.row_pos, a.q8, a.q64, a.arrivals);
+                     (const uint16_t*)a.rope, a.rope_rows, a.row_pos, a.q8, a.arrivals);
   return hipGetLastError();
 }
 

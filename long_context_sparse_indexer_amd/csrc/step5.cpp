@@ -47,15 +47,13 @@ int check_geom(const step5_geom* g) {
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 struct ScoreWs {
-  size_t q8 = 0, q64 = 0, bounds = 0, partial = 0, pool = 0, arrivals = 0, total = 0;
+  size_t q8 = 0, bounds = 0, partial = 0, pool = 0, arrivals = 0, total = 0;
 };
 ScoreWs score_ws(int32_t rows, int64_t R_cap) {
   ScoreWs w;
   size_t off = 0;
   w.q8 = off;   // prepared e4m3 query, [rows, idx_heads, idx_dim]
   off = up(off + (size_t)rows * kIdxHeads * kIdxDim);
-  w.q64 = off;  // its exact fp64 values, [rows, groups, idx_dim, heads per group]
-  off = up(off + (size_t)rows * kIdxHeads * kIdxDim * sizeof(double));
   w.bounds = off;  // score interval per (row, group, candidate), unless fused
   if (!s5::select_fused(rows, R_cap))
     off = up(off + (size_t)rows * kGroups * (size_t)R_cap * 2 * sizeof(float));
@@ -242,7 +240,6 @@ static int score_topk(const step5_geom* geom, uint32_t flags, const void* q, int
   if (ws_bytes < w.total || !workspace || !aligned(workspace, kAlign)) return STEP5_E_WORKSPACE;
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  double* q64 = reinterpret_cast<double*>(ws + w.q64);
   uint8_t* q8 = ws + w.q8;
   s5::QPrepArgs qa;
   qa.prepared = q_ready;
@@ -255,7 +252,6 @@ static int score_topk(const step5_geom* geom, uint32_t flags, const void* q, int
   qa.rope_rows = q_ready ? 0 : rope_rows;
   qa.row_pos = row_pos;
   qa.q8 = q8;
-  qa.q64 = q64;
   qa.arrivals = reinterpret_cast<unsigned*>(ws + w.arrivals);
   const bool exact = s5::score_exact_mode(rows);
   int st = exact ? STEP5_OK : from_hip(s5::launch_qprep(qa, stream));
@@ -288,7 +284,6 @@ static int score_topk(const step5_geom* geom, uint32_t flags, const void* q, int
   ta.fused = fused;
   ta.q8 = q8;
   ta.q8_stride_row = sa.q8_stride_row;
-  ta.q64 = q64;
   ta.w_head = w_head;
   ta.w_stride_row = w_stride_row;
   ta.summary = static_cast<const uint8_t*>(summary);

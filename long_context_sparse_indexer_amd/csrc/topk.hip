@@ -509,10 +509,12 @@ __device__ inline void rescore_survivors_lds(const TkShared& sm, int M, const do
   }
   __syncthreads();
 }
-__device__ inline void rescore_survivors(const TkShared& sm, int M, const double* __restrict__ qg,
+// qg: the row's e4m3 query for the group's 4 heads ([4 heads][64 dims]),
+// staged in LDS as exact fp64 [64 dims][4 heads]
+__device__ inline void rescore_survivors(const TkShared& sm, int M, const uint8_t* __restrict__ qg,
                                          const uint8_t* __restrict__ Sg, float wl, int tid) {
   double* qs = reinterpret_cast<double*>(sm.xb);
-  if (tid < 256) qs[tid] = qg[tid];
+  if (tid < 256) qs[tid] = e4m3_f64(qg[(tid & 3) * 64 + (tid >> 2)]);
   __syncthreads();
   rescore_survivors_lds(sm, M, qs, Sg, wl, tid);
 }
@@ -602,7 +604,7 @@ template <int KIND>
 __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_chunk_kernel(
     int mode, const float2* __restrict__ bounds, int64_t R_cap,
     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos, int64_t B,
-    int64_t pos_limit, const double* __restrict__ q64, const float* __restrict__ w_head,
+    int64_t pos_limit, const uint8_t* __restrict__ q8, int64_t qs8, const float* __restrict__ w_head,
     int64_t w_stride, const uint8_t* __restrict__ S, int64_t ssb, int64_t chunk, int nchunks,
     unsigned long long* __restrict__ partial, const uint32_t* __restrict__ pool,
     unsigned* __restrict__ arrivals, int32_t* __restrict__ sel_ids,
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(8, 8
     }
     // 3. exact scores of the survivors (matrix cores)
     const float wl = w_head[row * w_stride + 4 * g + (lane >> 4)];
-    rescore_survivors(sm, M, q64 + (row * 4 + g) * 256, S + (int64_t)seq * ssb + g * 64, wl, tid);
+    rescore_survivors(sm, M, q8 + row * qs8 + g * 256, S + (int64_t)seq * ssb + g * 64, wl, tid);
   }
   if constexpr (POOLED) {
     pool_select_tail(sm, M, unit, nchunks, ncand, partial, arrivals, nunits, sel_ids,
@@ -871,8 +873,7 @@ __device__ inline T sel4(int i, T a, T b, T c, T d) {
 __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
                    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_pos,
-                   int64_t B, int64_t pos_limit, const double* __restrict__ q64,
-                   const float* __restrict__ w_head, int64_t w_stride,
+                   int64_t B, int64_t pos_limit, const float* __restrict__ w_head, int64_t w_stride,
                    const uint8_t* __restrict__ S, int64_t ssb, int32_t rows, int64_t nwg,
                    int32_t* __restrict__ sel_ids, float* __restrict__ sel_scores, AppendArgs ap) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -910,7 +911,10 @@ topk_fused4_kernel(const uint8_t* __restrict__ q8, int64_t qs8, int64_t R_cap,
   // the four units' exact queries for the rescoring (thread t: entry t % 256
   // of unit t / 256), loaded now and kept in LDS (sm.xb, [4][256]) once the
   // intervals are done, so that their latency hides behind the intervals
-  const double qpre = NC(tid >> 8) > 0 ? q64[(r0 * 4 + g + 4 * (tid >> 8)) * 256 + (tid & 255)] : 0.0;
+  const double qpre =
+      NC(tid >> 8) > 0
+          ? e4m3_f64(q8[(r0 + (tid >> 8)) * qs8 + g * 256 + (tid & 3) * 64 + ((tid & 255) >> 2)])
+          : 0.0;
   int32_t s0 = -1;
   bool shared = true;
   int nmax = 0;
@@ -1257,7 +1261,7 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
     const int64_t nwg = ((int64_t)a.rows + 3) / 4 * 4;
     hipLaunchKernelGGL(topk_fused4_kernel, dim3((unsigned)(nwg + napp)), dim3(TK_THREADS), sm,
                        stream, a.q8, a.q8_stride_row, a.R_cap, a.row_seq, a.row_pos, a.B,
-                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, a.rows, nwg,
+                       a.pos_limit, a.w_head, a.w_stride_row, a.summary, a.ssb, a.rows, nwg,
                        a.sel_ids, a.sel_scores, ap);
     return hipGetLastError();
   }
@@ -1281,19 +1285,22 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t stream) {
   if (mode == 2)
     hipLaunchKernelGGL(topk_chunk_kernel<TK_POOLED>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B,
-                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
+                       a.pos_limit, a.q8, a.q8_stride_row, a.w_head, a.w_stride_row, a.summary,
+                       a.ssb, p.chunk,
                        p.nchunks, a.partial, a.pool, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);
   else if (a.exact)
     hipLaunchKernelGGL(topk_chunk_kernel<TK_EXACT>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B,
-                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
+                       a.pos_limit, a.q8, a.q8_stride_row, a.w_head, a.w_stride_row, a.summary,
+                       a.ssb, p.chunk,
                        p.nchunks, a.partial, nullptr, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);
   else
     hipLaunchKernelGGL(topk_chunk_kernel<TK_INTERVAL>, grid, dim3(TK_THREADS), sm, stream, mode,
                        a.bounds, a.R_cap, a.row_seq, a.row_pos, a.B,
-                       a.pos_limit, a.q64, a.w_head, a.w_stride_row, a.summary, a.ssb, p.chunk,
+                       a.pos_limit, a.q8, a.q8_stride_row, a.w_head, a.w_stride_row, a.summary,
+                       a.ssb, p.chunk,
                        p.nchunks, a.partial, nullptr, a.arrivals, a.sel_ids, a.sel_scores,
                        (int64_t)units, ap);
   return hipGetLastError();

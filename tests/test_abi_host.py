@@ -277,16 +277,17 @@ def test_workspace_sizes(s5):
     assert L.step5_index_score_topk_workspace(C.byref(g), 0, 100) == 0
     assert L.step5_index_score_topk_workspace(C.byref(g), 4, 0) == 0
     assert L.step5_index_score_topk_workspace(C.byref(geom(s5, groups=2)), 4, 64) == 0
-    # q8 (rows*1024) + q64 (rows*8192) + bounds (rows*4*R_cap*8), 256-aligned, plus chunk lists;
-    # more than 64 rows over at most 4,096 regions select with fused intervals: no bounds
+    # q8 (rows*1024) + bounds (rows*4*R_cap*8), 256-aligned, plus chunk lists and
+    # counters; more than 64 rows over at most 4,096 regions select with fused
+    # intervals: no bounds
     w1 = L.step5_index_score_topk_workspace(C.byref(g), 2048, 4096)
-    assert 2048 * 9216 <= w1 < 2048 * 9216 + 2048 * 4 * 8 + 4096
+    assert 2048 * 1024 <= w1 < 2048 * 1024 + 2048 * 4 * 8 + 4096
     w2 = L.step5_index_score_topk_workspace(C.byref(g), 2048, 4097)
-    assert w2 >= 2048 * 9216 + 2048 * 4 * 4097 * 8
+    assert w2 >= 2048 * 1024 + 2048 * 4 * 4097 * 8
     w4 = L.step5_index_score_topk_workspace(C.byref(g), 16, 16384)
-    assert w4 >= 16 * 9216 + 16 * 4 * 16384 * 8                       # one pass: no chunk lists
+    assert w4 >= 16 * 1024 + 16 * 4 * 16384 * 8                       # one pass: no chunk lists
     w5 = L.step5_index_score_topk_workspace(C.byref(g), 1, 131072)
-    assert w5 >= 9216 + 4 * 131072 * 8 + 4 * 8 * 512 * 8               # 8 chunk lists of 512
+    assert w5 >= 1024 + 4 * 131072 * 8 + 4 * 8 * 512 * 8               # 8 chunk lists of 512
     assert L.step5_sparse_attn_workspace(C.byref(g), 2048) == 0          # prefill: unsplit
     assert L.step5_sparse_attn_workspace(C.byref(g), 16) > 0             # decode: split states
     assert L.step5_sparse_attn_workspace(C.byref(g), 0) == 0

@@ -211,11 +211,11 @@ def test_fp8_products_exhaustive_through_scores():
 
 def _scores_view(ws, rows, R_cap, exact):
     """The candidate scores inside step5_index_score_topk's workspace
-    (white-box: e4m3 q [rows*1024 B], fp64 q [rows*8192 B], then per (row,
-    group, candidate) the exact score as float, or an interval as float2;
-    each part 256-byte aligned)."""
+    (white-box: e4m3 q [rows*1024 B], then per (row, group, candidate) the
+    exact score as float, or an interval as float2; each part 256-byte
+    aligned)."""
     up = lambda x: (x + 255) // 256 * 256
-    off = up(up(rows * 1024) + rows * 8192)
+    off = up(rows * 1024)
     k = 1 if exact else 2
     n = rows * 4 * R_cap * k
     return ws[off:off + n * 4].view(torch.float32).view(rows, 4, R_cap, k)

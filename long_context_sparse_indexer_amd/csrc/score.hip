@@ -392,9 +392,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __syncthreads();
   // pool: per (row, group), one key per 32 candidates, the best (0 if none),
   // gathered by LDS atomic max. NQ = 16: entry 8 b + 2 wave + p from the
-  // lanes of candidates 2p and 2p + 1 of group g (pmax[wave][2g + p]); NQ = 8:
-  // entry 4 b + wave from all of the group's lanes (pmax[wave][g]). A unit's keys start every
-  // 8 * ceil(R_cap / 256) entries.
+  // lanes of candidates 2p and 2p + 1 of group g (pmax[wave][2g + p]);
+  // NQ = 8: entry 4 b + wave from all of the group's lanes (pmax[wave][g]).
+  // A unit's keys start every 8 * ceil(R_cap / 256) entries.
   constexpr int PSH = NQ == 16 ? 1 : 2;  // (lane & 15) >> PSH: the lane's pmax slot
   auto pool_put = [&]() {
     const int64_t ustride = ((R_cap + 255) >> 8) * 8;

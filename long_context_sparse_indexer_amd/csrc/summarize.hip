@@ -29,6 +29,16 @@
 
 namespace s5 {
 
+// out[t] = v of lane 8 (i / 8) + t (t < 4), for the lanes i of every 8-lane
+// group (ds_swizzle in its bit-mask mode: and-mask 0x18 keeps the group,
+// or-mask t)
+template <int T>
+__device__ inline void bcast4_of8(float v, float (&out)[4]) {
+  out[T] = __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x18 | (T << 5)));
+  if constexpr (T < 3) bcast4_of8<T + 1>(v, out);
+}
+
 __global__ __launch_bounds__(256) void summarize_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ z, int64_t nreg, int64_t total,
     int64_t t0, int64_t sb, int64_t st, const float* __restrict__ lnw,
@@ -80,55 +90,74 @@ __global__ __launch_bounds__(256) void summarize_kernel(
 
     float den[8], num[8];
     const uint16_t* cs = rope + (t0 + jr * 8) * 32;
+    // the tokens in two halves of four: k prep statistics (mean and variance
+    // per (token, group), every lane of the group holding its dims'
+    // deviations), then r = 1/sqrt(var + eps) of token 4h + c % 4 once per
+    // lane (lane (g, c) of the region's 32), token t's r taken from lane
+    // (g, t % 4) of the same 8 lanes, then the rest of the token's work
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float x[8], d[8], d2[8], y[8];
-      unpack_bf16x8(kr[t], x);
-      const float mu = sum8_lanes(pair8(x), lane) / 64.0f;
+    for (int h = 0; h < 2; ++h) {
+      float d[4][8], var[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        d[i] = x[i] - mu;
-        d2[i] = d[i] * d[i];
+      for (int t4 = 0; t4 < 4; ++t4) {
+        float x[8], d2[8];
+        unpack_bf16x8(kr[4 * h + t4], x);
+        const float mu = sum8_lanes(pair8(x), lane) / 64.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          d[t4][i] = x[i] - mu;
+          d2[i] = d[t4][i] * d[t4][i];
+        }
+        var[t4] = sum8_lanes(pair8(d2), lane) / 64.0f;
       }
-      const float var = sum8_lanes(pair8(d2), lane) / 64.0f;
-      const float r = 1.0f / sqrtf(var + eps);
+      const int c4 = c & 3;
+      const float vc = c4 < 2 ? (c4 == 0 ? var[0] : var[1]) : (c4 == 2 ? var[2] : var[3]);
+      const float rc = 1.0f / sqrtf(vc + eps);
+      float rt[4];
+      bcast4_of8<0>(rc, rt);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float tt = (d[i] * r) * gw[i];
-        y[i] = tt + gb[i];
-      }
-      // NEOX rotation: lanes c and c^2 (c < 4) hold the two halves of the
-      // pairs; a*c - b*s on the first half is computed as a*c + b*(-s)
-      // (negation is exact)
-      float cf[8], sf[8];
-      unpack_bf16x8(ldg16(cs + t * 32 + fi), cf);
-      unpack_bf16x8(ldg16(cs + t * 32 + 16 + fi), sf);
-      float rv[8];
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int t = 4 * h + t4;
+        const float r = rt[t4];
+        float y[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float sfs = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sf[i]) ^ sflip);
-        const float own_c = y[i] * cf[i];
-        const float oth_s = dpp<DPP_QUAD_XOR2>(y[i]) * sfs;
-        const float rot = own_c + oth_s;
-        rv[i] = rotated ? rot : y[i];
-      }
-      float kv[8];
+        for (int i = 0; i < 8; ++i) {
+          const float tt = (d[t4][i] * r) * gw[i];
+          y[i] = tt + gb[i];
+        }
+        // NEOX rotation: lanes c and c^2 (c < 4) hold the two halves of the
+        // pairs; a*c - b*s on the first half is computed as a*c + b*(-s)
+        // (negation is exact)
+        float cf[8], sf[8];
+        unpack_bf16x8(ldg16(cs + t * 32 + fi), cf);
+        unpack_bf16x8(ldg16(cs + t * 32 + 16 + fi), sf);
+        float rv[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t pk = bf16x2_hw(rv[2 * i], rv[2 * i + 1]);
-        kv[2 * i] = bf_lo(pk);
-        kv[2 * i + 1] = bf_hi(pk);
-      }
+        for (int i = 0; i < 8; ++i) {
+          const float sfs = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sf[i]) ^ sflip);
+          const float own_c = y[i] * cf[i];
+          const float oth_s = dpp<DPP_QUAD_XOR2>(y[i]) * sfs;
+          const float rot = own_c + oth_s;
+          rv[i] = rotated ? rot : y[i];
+        }
+        float kv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = exp_fixed(zf[t][i] - m[i]);
-        const float pr = e * kv[i];
-        if (t == 0) {
-          den[i] = e;
-          num[i] = pr;
-        } else {
-          den[i] = den[i] + e;
-          num[i] = num[i] + pr;
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t pk = bf16x2_hw(rv[2 * i], rv[2 * i + 1]);
+          kv[2 * i] = bf_lo(pk);
+          kv[2 * i + 1] = bf_hi(pk);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = exp_fixed(zf[t][i] - m[i]);
+          const float pr = e * kv[i];
+          if (t == 0) {
+            den[i] = e;
+            num[i] = pr;
+          } else {
+            den[i] = den[i] + e;
+            num[i] = num[i] + pr;
+          }
         }
       }
     }

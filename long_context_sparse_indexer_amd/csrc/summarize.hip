@@ -61,8 +61,16 @@ __global__ __launch_bounds__(256) void summarize_kernel(
   const bool rotated = c < 4;        // dims 0..31
   const bool first_half = c < 2;     // dims 0..15 hold the pair's first element
   const int fi = (c & 1) * 8;        // frequency index of this lane's first dim
-  const uint32_t sflip = first_half ? 0x80000000u : 0u;
   const int64_t j0 = t0 >> 3;
+  // the rope rows of the wave's two regions (16 tokens), as fp32: per token
+  // cos 0..15 | sin 0..15 | -sin 0..15. Lane (region half, token sub/4,
+  // piece sub%4) stages 8 values; a lane reads cos and its signed sin at
+  // dims fi..fi+7 (the first half's a*c - b*s is a*c + b*(-s), negation
+  // being exact).
+  __shared__ float4 rope_lds[4][2][8][12];
+  float4 (*const rw)[12] = rope_lds[threadIdx.x >> 6][(threadIdx.x >> 5) & 1];
+  const int st_t = sub >> 2, st_p = sub & 3;
+  const int rd_c = fi >> 2, rd_s = (first_half ? 8 : 4) + (fi >> 2);
 
   for (int64_t u = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5); u < total;
        u += (int64_t)gridDim.x * 8) {
@@ -77,19 +85,38 @@ __global__ __launch_bounds__(256) void summarize_kernel(
 #pragma unroll
     for (int t = 0; t < 8; ++t) kr[t] = ldg16(kp + t * st);
 
-    float zf[8][8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) unpack_bf16x8(zr[t], zf[t]);
     float m[8];
+    unpack_bf16x8(zr[0], m);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      m[i] = zf[0][i];
+    for (int t = 1; t < 8; ++t) {
+      float zt[8];
+      unpack_bf16x8(zr[t], zt);
 #pragma unroll
-      for (int t = 1; t < 8; ++t) m[i] = fmaxf(m[i], zf[t][i]);
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], zt[i]);
+    }
+    // z stays packed until each token's exponentials (unpacked again there)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      __asm__ volatile("" : "+v"(zr[t].x), "+v"(zr[t].y));
+      __asm__ volatile("" : "+v"(zr[t].z), "+v"(zr[t].w));
     }
 
     float den[8], num[8];
-    const uint16_t* cs = rope + (t0 + jr * 8) * 32;
+    {
+      const uint16_t* cs = rope + (t0 + jr * 8) * 32;
+      float f[8];
+      unpack_bf16x8(ldg16(cs + st_t * 32 + st_p * 8), f);
+      const int o = st_p < 2 ? 2 * st_p : 4 + 2 * (st_p - 2);
+      rw[st_t][o] = make_float4(f[0], f[1], f[2], f[3]);
+      rw[st_t][o + 1] = make_float4(f[4], f[5], f[6], f[7]);
+      if (st_p >= 2) {
+        rw[st_t][o + 4] = make_float4(-f[0], -f[1], -f[2], -f[3]);
+        rw[st_t][o + 5] = make_float4(-f[4], -f[5], -f[6], -f[7]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     // the tokens in two halves of four: k prep statistics (mean and variance
     // per (token, group), every lane of the group holding its dims'
     // deviations), then r = 1/sqrt(var + eps) of token 4h + c % 4 once per
@@ -126,17 +153,24 @@ __global__ __launch_bounds__(256) void summarize_kernel(
           y[i] = tt + gb[i];
         }
         // NEOX rotation: lanes c and c^2 (c < 4) hold the two halves of the
-        // pairs; a*c - b*s on the first half is computed as a*c + b*(-s)
-        // (negation is exact)
-        float cf[8], sf[8];
-        unpack_bf16x8(ldg16(cs + t * 32 + fi), cf);
-        unpack_bf16x8(ldg16(cs + t * 32 + 16 + fi), sf);
+        // pairs
+        float cf[8], sfs[8];
+        {
+          // (read here, not hoisted to the loop top: the rows of all eight
+          // tokens at once would double the live registers)
+          __asm__ volatile("" ::: "memory");
+          const float4 c0 = rw[t][rd_c], c1 = rw[t][rd_c + 1];
+          const float4 s0 = rw[t][rd_s], s1 = rw[t][rd_s + 1];
+          cf[0] = c0.x; cf[1] = c0.y; cf[2] = c0.z; cf[3] = c0.w;
+          cf[4] = c1.x; cf[5] = c1.y; cf[6] = c1.z; cf[7] = c1.w;
+          sfs[0] = s0.x; sfs[1] = s0.y; sfs[2] = s0.z; sfs[3] = s0.w;
+          sfs[4] = s1.x; sfs[5] = s1.y; sfs[6] = s1.z; sfs[7] = s1.w;
+        }
         float rv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float sfs = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, sf[i]) ^ sflip);
           const float own_c = y[i] * cf[i];
-          const float oth_s = dpp<DPP_QUAD_XOR2>(y[i]) * sfs;
+          const float oth_s = dpp<DPP_QUAD_XOR2>(y[i]) * sfs[i];
           const float rot = own_c + oth_s;
           rv[i] = rotated ? rot : y[i];
         }
@@ -147,9 +181,11 @@ __global__ __launch_bounds__(256) void summarize_kernel(
           kv[2 * i] = bf_lo(pk);
           kv[2 * i + 1] = bf_hi(pk);
         }
+        float zf[8];
+        unpack_bf16x8(zr[t], zf);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float e = exp_fixed(zf[t][i] - m[i]);
+          const float e = exp_fixed(zf[i] - m[i]);
           const float pr = e * kv[i];
           if (t == 0) {
             den[i] = e;

@@ -184,10 +184,18 @@ class Timer:
         return out
 
 
-def event_time_us(torch, fn, reps):
+def event_time_us(torch, fn, reps, warm_s=0.0):
+    """Average µs of fn over reps back-to-back calls, after one untimed call
+    (or, with warm_s, untimed calls for about that many seconds, so that a
+    long kernel is timed at the clocks a busy GPU holds)."""
     stream = torch.cuda.current_stream()
     fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < warm_s:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(reps):
@@ -271,7 +279,7 @@ def run_workload(name, args, torch, s5, W):
         pass_tokens = B * prefix
         pass_name = f"{B} x {prefix} tokens"
     log(f"{name}: summary pass over {pass_name}")
-    summ_us = event_time_us(torch, full_pass, 5)
+    summ_us = event_time_us(torch, full_pass, 10, warm_s=0.5)
     summ_bytes = pass_tokens * 1024 + (pass_tokens // 8) * 256
     res["summary_pass"] = {"span": pass_name, "us": round(summ_us, 1),
                            "GBs": round(summ_bytes / summ_us / 1e3, 1),

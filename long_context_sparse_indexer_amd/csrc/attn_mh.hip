@@ -11,10 +11,12 @@
 // and walks it in 32-token chunks (4 entries), all four waves on the same
 // chunk:
 //  - the chunk's K and V rows go straight from memory into LDS
-//    (global_load_lds, 16 B per lane, no registers), double-buffered so the
-//    next chunk loads while this one is computed. A token row's 16-byte
-//    pieces are stored in XOR-swizzled slots, so that the reads below fall
-//    in distinct LDS banks;
+//    (global_load_lds, 16 B per lane, no registers), into a ring of three
+//    buffers at head dim 128 (two chunks load while one is computed) or two
+//    at 192 (one). A token row's 16-byte pieces are stored in XOR-swizzled
+//    slots, so that the reads below fall in distinct LDS banks. Each chunk's
+//    loads are waited for by count, and the buffers are read by LDS reads
+//    that wait only for themselves, so that no wait covers a later chunk;
 //  - S = Q K^T on the 16x16x32 bf16 MFMA: A = the unit's query heads (MFMA
 //    rows; rows past QPK are zero), B = 16 key tokens, each lane's D/4 dims
 //    read from LDS as 16-byte slices; every wave computes all of S;
@@ -35,6 +37,11 @@ namespace s5 {
 namespace {
 
 constexpr int MH_ENTRIES = 513;  // own region + 512 selections
+// chunk buffers: with 3, two chunks load while one is computed (head dim 128,
+// 62 KB of LDS: two workgroups per CU); with 2, one (head dim 192, whose
+// three buffers would leave one workgroup per CU)
+template <int D>
+constexpr int mh_nb() { return D <= 128 ? 3 : 2; }
 
 template <int QPK, int D>
 struct MhCfg {
@@ -66,8 +73,52 @@ __device__ inline void mh_load_lds16(const void* src, void* lds) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// wait for this wave's loads, those into LDS included
-__device__ inline void mh_wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// wait until at most N of this wave's vector memory operations (loads into
+// LDS included) are outstanding; they complete in issue order
+template <int N>
+__device__ inline void mh_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS reads of the chunk buffers. They are written by global_load_lds, and a
+// compiler-generated read of them would be preceded by a wait for every
+// outstanding load into LDS, the next chunks' included; these reads wait
+// only for themselves (in the same statement), the chunk's own loads having
+// been waited for explicitly.
+__device__ inline uint32_t mh_lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <int N>
+__device__ inline void mh_lds_read16(uint4 (&v)[N], const uint32_t (&a)[N]) {
+  static_assert(N == 4 || N == 6, "reads per statement");
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\tds_read_b128 %1, %7\n\tds_read_b128 %2, %8\n\t"
+        "ds_read_b128 %3, %9\n\tds_read_b128 %4, %10\n\tds_read_b128 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+        : "memory");
+  }
+}
+// eight 16-bit LDS values, zero-extended
+__device__ inline void mh_lds_read2x8(uint32_t (&v)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_u16 %0, %8\n\tds_read_u16 %1, %9\n\tds_read_u16 %2, %10\n\t"
+      "ds_read_u16 %3, %11\n\tds_read_u16 %4, %12\n\tds_read_u16 %5, %13\n\t"
+      "ds_read_u16 %6, %14\n\tds_read_u16 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+      : "memory");
+}
 
 // slot of piece P of chunk token tt: K rows are read 16 B per lane by 8
 // consecutive tokens, V rows 2 B per lane by 16 dims x 4 token groups
@@ -84,7 +135,8 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
     const int64_t* __restrict__ row_pos, float scale_log2, int per_split, int nsplit,
     float* __restrict__ partial, uint16_t* __restrict__ out, float* __restrict__ lse) {
   using C = MhCfg<QPK, D>;
-  __shared__ __align__(16) uint4 kv_lds[2][2][C::CP];         // [buffer][K | V][slot]
+  constexpr int NB = mh_nb<D>();
+  __shared__ __align__(16) uint4 kv_lds[NB][2][C::CP];        // [buffer][K | V][slot]
   __shared__ __align__(16) uint16_t p_lds[4][2][16 * 32];     // per wave: P high, low [head][token]
   __shared__ uint32_t ids_lds[512];
   __shared__ int32_t ent_j[MH_ENTRIES + 3];                   // the split's entries: region id
@@ -158,6 +210,17 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
   const uint16_t* kb = kc + sb + (int64_t)g * D;
   const uint16_t* vb = vc + sb + (int64_t)g * D;
   const int64_t pc = valid ? p : 0;  // a token that is always in range
+  // A operand of S: head n of the unit (zero past QPK), dims qd*D/4 ...
+  // (loaded before the chunks, so that the waits below, which count the
+  // chunks' loads, never wait for them)
+  uint4 qa[C::KS];
+#pragma unroll
+  for (int u = 0; u < C::KS; ++u) qa[u] = make_uint4(0, 0, 0, 0);
+  if (valid && n < QPK) {
+    const uint16_t* qp = q + row * qs + (int64_t)(QPK * g + n) * D + qd * (D / 4);
+#pragma unroll
+    for (int u = 0; u < C::KS; ++u) qa[u] = ldg16(qp + 8 * u);
+  }
   // chunk c into buffer bf: thread tid fills slots r * 256 + tid of K and V
   auto stage = [&](int c, int bf) {
 #pragma unroll
@@ -174,15 +237,6 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
     }
   };
 
-  // A operand of S: head n of the unit (zero past QPK), dims qd*D/4 ...
-  uint4 qa[C::KS];
-#pragma unroll
-  for (int u = 0; u < C::KS; ++u) qa[u] = make_uint4(0, 0, 0, 0);
-  if (valid && n < QPK) {
-    const uint16_t* qp = q + row * qs + (int64_t)(QPK * g + n) * D + qd * (D / 4);
-#pragma unroll
-    for (int u = 0; u < C::KS; ++u) qa[u] = ldg16(qp + 8 * u);
-  }
 
   float m[4], l[4];
   f32x4 o[C::TPW];
@@ -196,18 +250,25 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
   uint16_t* pw_hi = p_lds[wave][0];
   uint16_t* pw_lo = p_lds[wave][1];
 
-  if (nch > 0) stage(0, 0);
+  // each thread issues 2 PPT loads per chunk; chunks c + 1 .. c + NB - 1 are
+  // in flight while chunk c is computed
+  static_assert(NB == 2 || NB == 3, "the waits below count at most one chunk in flight");
+  constexpr int LPC = 2 * C::PPT;
+#pragma unroll
+  for (int c = 0; c < NB - 1; ++c)
+    if (c < nch) stage(c, c);
 #pragma unroll 1
   for (int c = 0; c < nch; ++c) {
-    const int bf = c & 1;
-    // this thread's loads of chunk c are done; after the barrier every
-    // thread's are, and every wave has finished chunk c - 1 (whose buffer
-    // chunk c + 1 reuses)
-    mh_wait_loads();
+    const int bf = c % NB;
+    // this thread's loads of chunk c are done (with 3 buffers chunk c + 1's
+    // may still be outstanding); after the barrier every thread's are, and
+    // every wave has finished chunk c - 1, whose buffer chunk c + NB - 1 reuses
+    if (NB == 3 && c + 1 < nch) mh_wait_vm<LPC>();
+    else mh_wait_vm<0>();
     __syncthreads();
-    if (c + 1 < nch) stage(c + 1, bf ^ 1);
-    const uint4* kl = kv_lds[bf][0];
-    const uint16_t* vl = reinterpret_cast<const uint16_t*>(kv_lds[bf][1]);
+    if (c + NB - 1 < nch) stage(c + NB - 1, (c + NB - 1) % NB);
+    const uint32_t kl = mh_lds_addr(kv_lds[bf][0]);
+    const uint32_t vl = mh_lds_addr(kv_lds[bf][1]);
     // S for tokens 16 st + n of the chunk
     f32x4 acc[2];
     bool kok[2];
@@ -216,9 +277,14 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
       const int tt = 16 * st + n;
       kok[st] = (tt & 7) < (int)ent_n[4 * c + (tt >> 3)];
       acc[st] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      uint32_t ka[C::KS];
+      uint4 kv[C::KS];
 #pragma unroll
       for (int u = 0; u < C::KS; ++u)
-        acc[st] = mh_mfma(qa[u], kl[tt * C::PIECES + mh_kslot(tt, qd * C::KS + u)], acc[st]);
+        ka[u] = kl + 16u * (uint32_t)(tt * C::PIECES + mh_kslot(tt, qd * C::KS + u));
+      mh_lds_read16<C::KS>(kv, ka);
+#pragma unroll
+      for (int u = 0; u < C::KS; ++u) acc[st] = mh_mfma(qa[u], kv[u], acc[st]);
     }
     float alpha[4];
 #pragma unroll
@@ -251,14 +317,16 @@ __global__ __launch_bounds__(256) void attn_mh_kernel(
       for (int r = 0; r < 4; ++r) o[ct][r] *= alpha[r];
       // B: V[tokens 8qd .. 8qd+7][dim 16 tile + n]
       const int P = 2 * tile + (n >> 3), e8 = n & 7;
+      uint32_t va[8], vv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int tt = 8 * qd + t;
+        va[t] = vl + 2u * (uint32_t)((tt * C::PIECES + mh_vslot(tt, P)) * 8 + e8);
+      }
+      mh_lds_read2x8(vv, va);
       uint32_t bw[4];
 #pragma unroll
-      for (int t2 = 0; t2 < 4; ++t2) {
-        const int t0 = 8 * qd + 2 * t2, t1 = t0 + 1;
-        const uint32_t v0 = vl[(t0 * C::PIECES + mh_vslot(t0, P)) * 8 + e8];
-        const uint32_t v1 = vl[(t1 * C::PIECES + mh_vslot(t1, P)) * 8 + e8];
-        bw[t2] = v0 | (v1 << 16);
-      }
+      for (int t2 = 0; t2 < 4; ++t2) bw[t2] = vv[2 * t2] | (vv[2 * t2 + 1] << 16);
       const uint4 bv = make_uint4(bw[0], bw[1], bw[2], bw[3]);
       o[ct] = mh_mfma(pa_hi, bv, o[ct]);
       o[ct] = mh_mfma(pa_lo, bv, o[ct]);
